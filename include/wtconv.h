@@ -1,0 +1,130 @@
+/*
+ * wtconv.h -- C ABI of libwtconv, the MI355X (gfx950) WTConv operator.
+ *
+ * WTConv ("Fast and Memory-Efficient Wavelet Convolutions via I/O-Aware
+ * Reformulation", arXiv 2608.10805, Abstract) is a multi-level 2-D Haar
+ * wavelet convolution:
+ *
+ *   LL_0 = x;  for i = 1..L:  (S_i^0..S_i^3) = orthonormal 2x2 Haar analysis of
+ *              LL_{i-1} (zero-padded right/bottom to even size), LL_i = S_i^0
+ *   Y_i   = s_i * dwconv_k(S_i, W_i)       (4C subband-channels 4c+u, zero pad k/2)
+ *   Z_{L+1} = 0,  Z_i = inverse Haar(Y_i^0 + Z_{i+1}, Y_i^1, Y_i^2, Y_i^3),
+ *                 cropped to the size of LL_{i-1}
+ *   out   = s0 * dwconv_k(x, W0) + b0 + Z_1
+ *
+ * Subband u = 2*u_y + u_x: u_x = 1 is high-pass along W, u_y = 1 along H.
+ * dwconv is cross-correlation: (W * X)[p] = sum_d W[d + k/2] X[p + d].
+ *
+ * The library computes the operator with the three reformulations that
+ * abstract names: the Haar analysis is recomputed on chip, the synthesis
+ * cascade is evaluated as one closed-form pass indexed by output-coordinate
+ * bits, and the scales are folded into the convolution weights.  The
+ * "_unfused" entry points run the same operator level by level, one kernel
+ * per step, with every intermediate in device memory (the baseline the
+ * abstract compares against).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises on these paths; calls
+ *     are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *   - x, out, g (= d loss / d out) and dx are [B, C, H, W], NCHW contiguous,
+ *     stored as float32 (dtype WTC_FP32) or bfloat16 bits (WTC_BF16; out and
+ *     dx are rounded to nearest even).  All arithmetic is float32.
+ *   - Parameters and their gradients are float32:
+ *       w0 [C, k, k] (PyTorch depthwise [C,1,k,k] order), s0 [C], b0 [C],
+ *       wl [L, 4C, k, k] with flat index ((l*C + c)*4 + u)*k*k + ky*k + kx,
+ *       sl [L, 4C]       with flat index  (l*C + c)*4 + u.
+ *     wl and sl may be NULL when L == 0.
+ *   - Outputs are overwritten, never accumulated.
+ *   - Arguments are checked before any HIP call; a failed check returns a
+ *     negative wtc_status and touches nothing.  A failed kernel launch
+ *     returns WTC_EHIP.  No C++ exception crosses this interface.
+ *   - Calls with the same workspace must not overlap in time.
+ */
+#ifndef WTCONV_H
+#define WTCONV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WTC_OK = 0,
+    WTC_EINVAL = -1,     /* null pointer, k even or < 1, L < 0, B/C/H/W < 1, bad impl/dir */
+    WTC_ESHAPE = -2,     /* plane too large for the on-chip (LDS) plane pipeline */
+    WTC_EDTYPE = -3,     /* dtype or layout not supported */
+    WTC_EWORKSPACE = -4, /* workspace NULL or smaller than the queried size */
+    WTC_EHIP = -5        /* a HIP launch or runtime call failed */
+} wtc_status;
+
+typedef enum { WTC_FP32 = 0, WTC_BF16 = 1 } wtc_dtype;
+
+typedef struct {
+    int B, C, H, W; /* batch, channels, height, width (all >= 1)              */
+    int L;          /* wavelet levels (>= 0)                                  */
+    int k;          /* kernel size (odd, 1..7 on the fused path)              */
+    int dtype;      /* wtc_dtype: storage type of x / out / g / dx           */
+    int layout;     /* 0 = NCHW (the only layout)                             */
+} wtc_desc;
+
+/* Bytes of device workspace wtconv_forward needs (0: none). */
+size_t wtconv_forward_workspace(const wtc_desc* d);
+
+/* Forward pass: out = WTConv(x).  `workspace` may be NULL when the queried
+ * size is 0. */
+int wtconv_forward(const wtc_desc* d, const void* x,
+                   const float* w0, const float* s0, const float* b0,
+                   const float* wl, const float* sl,
+                   void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace wtconv_backward needs (per-workgroup partial
+ * sums of the weight-gradient correlations). */
+size_t wtconv_backward_workspace(const wtc_desc* d);
+
+/* Backward pass: given g = d loss / d out, writes
+ *   dx  [B,C,H,W]   (same storage dtype as x)
+ *   dw0 [C,k,k], ds0 [C], db0 [C], dwl [L,4C,k,k], dsl [L,4C]  (float32;
+ *   dwl/dsl may be NULL when L == 0).
+ * Weight gradients are with respect to the unscaled weights W0 and W_i.
+ * The reduction over batch and space is deterministic (fixed order). */
+int wtconv_backward(const wtc_desc* d, const void* x, const void* g,
+                    const float* w0, const float* s0,
+                    const float* wl, const float* sl,
+                    void* dx, float* dw0, float* ds0, float* db0,
+                    float* dwl, float* dsl,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Level-by-level baseline: one kernel per step, intermediates in device
+ * memory.  Same arguments, results and error behaviour as above. */
+size_t wtconv_forward_unfused_workspace(const wtc_desc* d);
+int wtconv_forward_unfused(const wtc_desc* d, const void* x,
+                           const float* w0, const float* s0, const float* b0,
+                           const float* wl, const float* sl,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream);
+size_t wtconv_backward_unfused_workspace(const wtc_desc* d);
+int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g,
+                            const float* w0, const float* s0,
+                            const float* wl, const float* sl,
+                            void* dx, float* dw0, float* ds0, float* db0,
+                            float* dwl, float* dsl,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Analytic model of device-memory (HBM) traffic in bytes for one call:
+ * impl 0 = fused, 1 = unfused; dir 0 = forward, 1 = backward.
+ * Returns a negative value for an invalid descriptor or impl/dir. */
+double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir);
+
+/* Algorithmic floating-point operations of one call (an FMA counts 2),
+ * dir 0 = forward, 1 = backward; negative for an invalid descriptor. */
+double wtconv_flops(const wtc_desc* d, int dir);
+
+/* Static description of a status code. */
+const char* wtconv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WTCONV_H */

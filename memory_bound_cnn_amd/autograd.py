@@ -1,0 +1,52 @@
+"""PyTorch autograd wrapper of the fused WTConv kernels.
+
+Only x is saved for the backward pass: the subbands are recomputed on chip,
+so no intermediate of the wavelet cascade is kept in device memory.
+"""
+
+import math
+
+import torch
+
+from . import binding
+
+__all__ = ["WTConvFunction", "WTConv2d", "wtconv"]
+
+
+class WTConvFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, w0, s0, b0, wl, sl, L):
+        x = x.contiguous()
+        ctx.L = L
+        ctx.save_for_backward(x, w0, s0, wl, sl)
+        return binding.wtconv_forward(x, w0, s0, b0, wl, sl, L)
+
+    @staticmethod
+    def backward(ctx, g):
+        x, w0, s0, wl, sl = ctx.saved_tensors
+        r = binding.wtconv_backward(x, g.contiguous(), w0, s0, wl, sl, ctx.L)
+        return r["dx"], r["dw0"], r["ds0"], r["db0"], r["dwl"], r["dsl"], None
+
+
+def wtconv(x, w0, s0, b0, wl, sl, L):
+    return WTConvFunction.apply(x, w0, s0, b0, wl, sl, L)
+
+
+class WTConv2d(torch.nn.Module):
+    """Depthwise WTConv layer: same-size output, C channels, L levels, k x k kernels."""
+
+    def __init__(self, channels, kernel_size=5, levels=1, device=None):
+        super().__init__()
+        if kernel_size % 2 != 1:
+            raise ValueError("kernel_size must be odd")
+        C, k, L = channels, kernel_size, levels
+        f = dict(device=device, dtype=torch.float32)
+        self.L = L
+        self.w0 = torch.nn.Parameter(torch.randn(C, k, k, **f) / k)
+        self.s0 = torch.nn.Parameter(torch.ones(C, **f))
+        self.b0 = torch.nn.Parameter(torch.zeros(C, **f))
+        self.wl = torch.nn.Parameter(torch.randn(max(L, 1), 4 * C, k, k, **f) / k)
+        self.sl = torch.nn.Parameter(torch.full((max(L, 1), 4 * C), 0.1, **f))
+
+    def forward(self, x):
+        return wtconv(x, self.w0, self.s0, self.b0, self.wl, self.sl, self.L)

@@ -1,0 +1,234 @@
+"""ctypes binding of libwtconv (include/wtconv.h): argument marshalling only.
+
+Every entry point here has the name of the C function it calls.  Tensors are
+PyTorch device tensors (PyTorch supplies device memory and the current
+stream); all computation happens in the library's HIP kernels.  A missing
+library raises immediately: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "WTCError", "load_library", "wtc_desc", "make_desc",
+    "wtconv_forward", "wtconv_backward", "wtconv_forward_unfused", "wtconv_backward_unfused",
+    "wtconv_forward_workspace", "wtconv_backward_workspace",
+    "wtconv_forward_unfused_workspace", "wtconv_backward_unfused_workspace",
+    "wtconv_io_model_bytes", "wtconv_flops", "wtconv_status_string",
+    "WTC_FP32", "WTC_BF16", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwtconv.so")
+
+WTC_OK, WTC_EINVAL, WTC_ESHAPE, WTC_EDTYPE, WTC_EWORKSPACE, WTC_EHIP = 0, -1, -2, -3, -4, -5
+WTC_FP32, WTC_BF16 = 0, 1
+
+
+class WTCError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {wtconv_status_string(status)} (status {status})")
+
+
+class wtc_desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("C", ctypes.c_int), ("H", ctypes.c_int), ("W", ctypes.c_int),
+                ("L", ctypes.c_int), ("k", ctypes.c_int), ("dtype", ctypes.c_int), ("layout", ctypes.c_int)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_SZ = ctypes.c_size_t
+_D = ctypes.POINTER(wtc_desc)
+
+
+def load_library(path=None):
+    """Load libwtconv.so (built by memory_bound_cnn_amd.build); raises if missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libwtconv.so not found at {p}; run `python -m memory_bound_cnn_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.wtconv_status_string.restype = ctypes.c_char_p
+    lib.wtconv_status_string.argtypes = [ctypes.c_int]
+    for name in ("wtconv_forward_workspace", "wtconv_backward_workspace",
+                 "wtconv_forward_unfused_workspace", "wtconv_backward_unfused_workspace"):
+        f = getattr(lib, name)
+        f.restype = _SZ
+        f.argtypes = [_D]
+    for name in ("wtconv_forward", "wtconv_forward_unfused"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    for name in ("wtconv_backward", "wtconv_backward_unfused"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.wtconv_io_model_bytes.restype = ctypes.c_double
+    lib.wtconv_io_model_bytes.argtypes = [_D, ctypes.c_int, ctypes.c_int]
+    lib.wtconv_flops.restype = ctypes.c_double
+    lib.wtconv_flops.argtypes = [_D, ctypes.c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def wtconv_status_string(status):
+    return load_library().wtconv_status_string(int(status)).decode()
+
+
+def make_desc(B, C, H, W, L, k, dtype="fp32"):
+    dt = {"fp32": WTC_FP32, "bf16": WTC_BF16, torch.float32: WTC_FP32, torch.bfloat16: WTC_BF16}[dtype]
+    return wtc_desc(int(B), int(C), int(H), int(W), int(L), int(k), dt, 0)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(t, name, dtypes, device, shape=None):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a CUDA tensor on {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _desc_of(x, L, k):
+    B, C, H, W = x.shape
+    return make_desc(B, C, H, W, L, k, x.dtype)
+
+
+def _check_params(x, w0, s0, b0, wl, sl, L):
+    B, C, H, W = x.shape
+    k = w0.shape[-1]
+    dev = x.device
+    f32 = (torch.float32,)
+    _check_tensor(x, "x", (torch.float32, torch.bfloat16), dev)
+    _check_tensor(w0, "w0", f32, dev, (C, k, k))
+    _check_tensor(s0, "s0", f32, dev, (C,))
+    _check_tensor(b0, "b0", f32, dev, (C,))
+    if L > 0:
+        if wl is None or sl is None:
+            raise ValueError("wl and sl are required when L > 0")
+        _check_tensor(wl, "wl", f32, dev)
+        _check_tensor(sl, "sl", f32, dev)
+        if wl.shape[0] < L or tuple(wl.shape[1:]) != (4 * C, k, k) or sl.shape[0] < L or sl.shape[1] != 4 * C:
+            raise ValueError("wl must be [>=L, 4C, k, k] and sl [>=L, 4C]")
+    return k
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace, workspace.numel() * workspace.element_size()
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return ws, nbytes
+
+
+def _fwd_common(fn_name, ws_name, x, w0, s0, b0, wl, sl, L, out, workspace):
+    k = _check_params(x, w0, s0, b0, wl, sl, L)
+    lib = load_library()
+    d = _desc_of(x, L, k)
+    if out is None:
+        out = torch.empty_like(x)
+    _check_tensor(out, "out", (x.dtype,), x.device, x.shape)
+    ws, wsb = _workspace(getattr(lib, ws_name)(ctypes.byref(d)), x.device, workspace)
+    st = getattr(lib, fn_name)(ctypes.byref(d), _ptr(x), _ptr(w0), _ptr(s0), _ptr(b0),
+                               _ptr(wl if L > 0 else None), _ptr(sl if L > 0 else None),
+                               _ptr(out), _ptr(ws), wsb, _stream(x.device))
+    if st != WTC_OK:
+        raise WTCError(st, fn_name)
+    return out
+
+
+def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace):
+    C = x.shape[1]
+    k = _check_params(x, w0, s0, None, wl, sl, L)
+    _check_tensor(g, "g", (x.dtype,), x.device, x.shape)
+    lib = load_library()
+    d = _desc_of(x, L, k)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if grads is None:
+        f32 = dict(dtype=torch.float32, device=x.device)
+        grads = dict(dw0=torch.empty(C, k, k, **f32), ds0=torch.empty(C, **f32), db0=torch.empty(C, **f32),
+                     dwl=torch.empty(L, 4 * C, k, k, **f32) if L > 0 else None,
+                     dsl=torch.empty(L, 4 * C, **f32) if L > 0 else None)
+    ws, wsb = _workspace(getattr(lib, ws_name)(ctypes.byref(d)), x.device, workspace)
+    st = getattr(lib, fn_name)(ctypes.byref(d), _ptr(x), _ptr(g), _ptr(w0), _ptr(s0),
+                               _ptr(wl if L > 0 else None), _ptr(sl if L > 0 else None), _ptr(dx),
+                               _ptr(grads["dw0"]), _ptr(grads["ds0"]), _ptr(grads["db0"]),
+                               _ptr(grads["dwl"]), _ptr(grads["dsl"]), _ptr(ws), wsb, _stream(x.device))
+    if st != WTC_OK:
+        raise WTCError(st, fn_name)
+    out = dict(grads)
+    out["dx"] = dx
+    return out
+
+
+def wtconv_forward(x, w0, s0, b0, wl, sl, L, out=None, workspace=None):
+    """out = WTConv(x) on the current stream (fused kernels)."""
+    return _fwd_common("wtconv_forward", "wtconv_forward_workspace", x, w0, s0, b0, wl, sl, L, out, workspace)
+
+
+def wtconv_forward_unfused(x, w0, s0, b0, wl, sl, L, out=None, workspace=None):
+    """Level-by-level baseline of :func:`wtconv_forward`."""
+    return _fwd_common("wtconv_forward_unfused", "wtconv_forward_unfused_workspace", x, w0, s0, b0, wl, sl, L,
+                       out, workspace)
+
+
+def wtconv_backward(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None):
+    """Returns dict(dx, dw0, ds0, db0, dwl, dsl) for upstream gradient g (fused kernels)."""
+    return _bwd_common("wtconv_backward", "wtconv_backward_workspace", x, g, w0, s0, wl, sl, L, dx, grads,
+                       workspace)
+
+
+def wtconv_backward_unfused(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None):
+    """Level-by-level baseline of :func:`wtconv_backward`."""
+    return _bwd_common("wtconv_backward_unfused", "wtconv_backward_unfused_workspace", x, g, w0, s0, wl, sl, L,
+                       dx, grads, workspace)
+
+
+def _ws_query(name, B, C, H, W, L, k, dtype):
+    d = make_desc(B, C, H, W, L, k, dtype)
+    return int(getattr(load_library(), name)(ctypes.byref(d)))
+
+
+def wtconv_forward_workspace(B, C, H, W, L, k, dtype="fp32"):
+    return _ws_query("wtconv_forward_workspace", B, C, H, W, L, k, dtype)
+
+
+def wtconv_backward_workspace(B, C, H, W, L, k, dtype="fp32"):
+    return _ws_query("wtconv_backward_workspace", B, C, H, W, L, k, dtype)
+
+
+def wtconv_forward_unfused_workspace(B, C, H, W, L, k, dtype="fp32"):
+    return _ws_query("wtconv_forward_unfused_workspace", B, C, H, W, L, k, dtype)
+
+
+def wtconv_backward_unfused_workspace(B, C, H, W, L, k, dtype="fp32"):
+    return _ws_query("wtconv_backward_unfused_workspace", B, C, H, W, L, k, dtype)
+
+
+def wtconv_io_model_bytes(B, C, H, W, L, k, dtype="fp32", impl=0, direction=0):
+    d = make_desc(B, C, H, W, L, k, dtype)
+    return float(load_library().wtconv_io_model_bytes(ctypes.byref(d), int(impl), int(direction)))
+
+
+def wtconv_flops(B, C, H, W, L, k, dtype="fp32", direction=0):
+    d = make_desc(B, C, H, W, L, k, dtype)
+    return float(load_library().wtconv_flops(ctypes.byref(d), int(direction)))

@@ -1,0 +1,404 @@
+// Host side of libwtconv: argument checks, launch planning, dispatch, and the
+// analytic HBM-traffic model.  See include/wtconv.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "wtc_internal.h"
+
+namespace wtc {
+namespace {
+
+constexpr size_t kLdsLimit = 160 * 1024;       // gfx950 LDS per workgroup
+constexpr size_t kMultiPlaneBudget = 64 * 1024; // small planes: leave room for >= 2 workgroups / CU
+constexpr int kTargetWorkgroups = 1024;        // backward: ~4 resident workgroups per CU
+
+int ceil_log2(int v) {
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+int check_desc(const wtc_desc* d) {
+    if (!d) return WTC_EINVAL;
+    if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->L < 0) return WTC_EINVAL;
+    if (d->k < 1 || d->k % 2 == 0) return WTC_EINVAL;
+    if (d->dtype != WTC_FP32 && d->dtype != WTC_BF16) return WTC_EDTYPE;
+    if (d->layout != 0) return WTC_EDTYPE;
+    return WTC_OK;
+}
+
+struct FusedPlan {
+    FusedArgs a;
+    int nthr, bpq, grid, nchunk;
+    size_t lds;
+};
+
+// Per-slot LDS layout for one plane (floats).  Returns the slot size.
+int slot_layout(FusedArgs& a, int k, bool bwd) {
+    const int R = k / 2;
+    const int Lm = a.Lm;
+    int off = 0;
+    // level-1 bands (never overlapped: their halo rings are zeroed once)
+    for (int i = 0; i <= kMaxLm; ++i) {
+        a.b_off[i] = a.b_S[i] = a.b_bs[i] = a.b_rows[i] = 0;
+        a.z_off[i] = a.yd_off[i] = a.xb_off[i] = 0;
+    }
+    auto band_geom = [&](int i) {
+        a.b_rows[i] = (a.Hq >> i) + 2 * R;
+        a.b_S[i] = round_up((a.Wq >> i) + 2 * R, 4);
+        // band stride = 8 (mod 32) floats: the four subbands start in different LDS banks
+        a.b_bs[i] = round_up(a.b_rows[i] * a.b_S[i], 32) + 8;
+    };
+    if (Lm >= 1) {
+        band_geom(1);
+        a.b_off[1] = off;
+        off += round_up(4 * a.b_bs[1], 4);
+    }
+    // level-0 plane
+    a.a0_rows = a.Hq + 2 * R;
+    a.a0_S = round_up(a.Wq + 2 * R, 4);
+    const int a0_size = round_up(a.a0_rows * a.a0_S, 4);
+    // level >= 2 region
+    int r2 = 0;
+    auto take = [&](int n) {
+        const int o = r2;
+        r2 += round_up(n, 4);
+        return o;
+    };
+    int rel_b[kMaxLm + 1] = {0}, rel_z[kMaxLm + 1] = {0}, rel_y[kMaxLm + 1] = {0},
+        rel_x[kMaxLm + 1] = {0};
+    int rel_xl2 = 0;
+    for (int i = 2; i <= Lm; ++i) {
+        band_geom(i);
+        rel_b[i] = take(4 * a.b_bs[i]);
+        rel_z[i] = take((a.Hq >> (i - 1)) * (a.Wq >> (i - 1)));
+        if (i >= 3) rel_y[i] = take(4 * (a.Hq >> i) * (a.Wq >> i));
+        if (bwd && i >= 3) rel_x[i] = take(4 * (a.Hq >> i) * (a.Wq >> i));
+    }
+    if (bwd && Lm >= 3) rel_xl2 = take((a.Hq >> 2) * (a.Wq >> 2));
+    a.a0_off = off;
+    int r2_base;
+    if (r2 <= a0_size) {
+        a.overlap = (r2 > 0) ? 1 : 0;
+        r2_base = off;
+        off += a0_size;
+    } else {
+        a.overlap = 0;
+        off += a0_size;
+        r2_base = off;
+        off += r2;
+    }
+    for (int i = 2; i <= Lm; ++i) {
+        a.b_off[i] = r2_base + rel_b[i];
+        a.z_off[i] = r2_base + rel_z[i];
+        if (i >= 3) a.yd_off[i] = r2_base + rel_y[i];
+        if (bwd && i >= 3) a.xb_off[i] = r2_base + rel_x[i];
+    }
+    a.xl2_off = r2_base + rel_xl2;
+    a.tail_off = off;
+    off += 4;
+    return round_up(off, 4);
+}
+
+int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
+    int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    const int k = d->k, KK = k * k;
+    if (k > kMaxK) return WTC_ESHAPE;
+    FusedArgs& a = p->a;
+    std::memset(&a, 0, sizeof(a));
+    a.B = d->B; a.C = d->C; a.H = d->H; a.W = d->W; a.L = d->L;
+    const int Lcap = ceil_log2(std::max(d->H, d->W));
+    a.Lm = std::min(d->L, Lcap);
+    if (a.Lm > kMaxLm) return WTC_ESHAPE;
+    const int T = std::max(8, 1 << a.Lm);
+    a.Hq = cdiv(d->H, T) * T;
+    a.Wq = cdiv(d->W, T) * T;
+    a.nqx = a.Wq / 8;
+    a.qpp = (a.Hq / 8) * a.nqx;
+    a.vec = (d->W % 4 == 0) ? 1 : 0;
+    const int slot = slot_layout(a, k, bwd);
+    a.slot_stride = slot;
+    const int wts_n = round_up(KK * (1 + 4 * d->L) + 2, 4);
+
+    int nthr, bpq = 1, NP = 1;
+    if (a.qpp <= 64) {
+        // several planes per workgroup when planes are small; pick the plane
+        // count (within the LDS budget) that leaves the fewest idle lanes
+        int np_fit = 64 / a.qpp;
+        while (np_fit > 1 && (size_t)(np_fit * slot + wts_n) * 4 > kMultiPlaneBudget) --np_fit;
+        double best = 2.0;
+        for (int np = np_fit; np >= std::max(1, np_fit / 2); --np) {
+            int nt = round_up(4 * a.qpp * np, 64);
+            if (bwd && a.Lm >= 3) nt = std::max(nt, round_up(4 * KK, 64));
+            const double idle = 1.0 - (double)(4 * a.qpp * np) / nt;
+            if (idle < best - 1e-9) {
+                best = idle;
+                NP = np;
+            }
+        }
+        nthr = round_up(4 * a.qpp * NP, 64);
+        if (bwd && a.Lm >= 3) nthr = std::max(nthr, round_up(4 * KK, 64));
+    } else if (a.qpp <= 128) {
+        nthr = 512;
+    } else if (a.qpp <= 256) {
+        nthr = 512;
+        bpq = 2;
+    } else {
+        return WTC_ESHAPE;
+    }
+    a.NP = NP;
+    a.dsub = std::max(1, nthr / (4 * KK));
+    if (bwd && a.Lm >= 3 && nthr < 4 * KK) return WTC_ESHAPE;
+    a.wts_off = NP * slot;
+    a.P = partial_len(k, a.Lm);
+    // reduction scratch reuses the plane slots after the last plane
+    a.red_off = 0;
+    const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * KK * a.dsub;
+    size_t lds_floats = (size_t)std::max(NP * slot + wts_n, bwd ? red_n : 0);
+    p->lds = lds_floats * 4;
+    if (p->lds > kLdsLimit) return WTC_ESHAPE;
+
+    // work split over batch
+    const int iters = cdiv(d->B, NP);
+    int nchunk;
+    if (bwd) {
+        nchunk = std::max(1, std::min(iters, (kTargetWorkgroups + d->C / 2) / d->C));
+    } else {
+        nchunk = iters;
+    }
+    const int it_per = cdiv(iters, nchunk);
+    a.bpc = it_per * NP;
+    nchunk = cdiv(d->B, a.bpc);
+    p->nchunk = nchunk;
+    p->grid = nchunk * d->C;
+    p->nthr = nthr;
+    p->bpq = bpq;
+    return WTC_OK;
+}
+
+double spec_level_area(const wtc_desc* d, int i) {
+    int h = d->H, w = d->W;
+    for (int l = 0; l < i; ++l) {
+        h = (h + 1) / 2;
+        w = (w + 1) / 2;
+    }
+    return (double)h * w;
+}
+
+}  // namespace
+}  // namespace wtc
+
+using namespace wtc;
+
+extern "C" {
+
+const char* wtconv_status_string(int s) {
+    switch (s) {
+        case WTC_OK: return "ok";
+        case WTC_EINVAL: return "invalid argument";
+        case WTC_ESHAPE: return "plane too large for the on-chip plane pipeline";
+        case WTC_EDTYPE: return "unsupported dtype or layout";
+        case WTC_EWORKSPACE: return "workspace missing or too small";
+        case WTC_EHIP: return "HIP launch or runtime error";
+        default: return "unknown status";
+    }
+}
+
+size_t wtconv_forward_workspace(const wtc_desc* d) {
+    (void)d;
+    return 0;
+}
+
+int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0,
+                   const float* b0, const float* wl, const float* sl, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
+    if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
+    FusedPlan p;
+    st = plan_fused(d, false, &p);
+    if (st != WTC_OK) return st;
+    FusedArgs& a = p.a;
+    a.src = x;
+    a.aux = nullptr;
+    a.w0 = w0; a.s0 = s0; a.b0 = b0; a.wl = wl; a.sl = sl;
+    a.dst = out;
+    a.partials = nullptr;
+    const int e = launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
+    return e == 0 ? WTC_OK : WTC_EHIP;
+}
+
+size_t wtconv_backward_workspace(const wtc_desc* d) {
+    FusedPlan p;
+    if (plan_fused(d, true, &p) != WTC_OK) return 0;
+    return (size_t)p.nchunk * d->C * p.a.P * sizeof(float);
+}
+
+int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float* w0,
+                    const float* s0, const float* wl, const float* sl, void* dx, float* dw0,
+                    float* ds0, float* db0, float* dwl, float* dsl, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
+    if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
+    FusedPlan p;
+    st = plan_fused(d, true, &p);
+    if (st != WTC_OK) return st;
+    const size_t need = (size_t)p.nchunk * d->C * p.a.P * sizeof(float);
+    if (!workspace || workspace_bytes < need) return WTC_EWORKSPACE;
+    FusedArgs& a = p.a;
+    a.src = g;
+    a.aux = x;
+    a.w0 = w0; a.s0 = s0; a.b0 = nullptr; a.wl = wl; a.sl = sl;
+    a.dst = dx;
+    a.partials = static_cast<float*>(workspace);
+    int e = launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
+    if (e != 0) return WTC_EHIP;
+    FinalizeArgs f;
+    f.partials = a.partials;
+    f.w0 = w0; f.s0 = s0; f.wl = wl; f.sl = sl;
+    f.dw0 = dw0; f.ds0 = ds0; f.db0 = db0; f.dwl = dwl; f.dsl = dsl;
+    f.C = d->C; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.nchunk = p.nchunk; f.P = a.P;
+    e = launch_finalize(f, stream);
+    return e == 0 ? WTC_OK : WTC_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// Unfused baseline
+// ---------------------------------------------------------------------------
+size_t wtconv_forward_unfused_workspace(const wtc_desc* d) {
+    UnfusedPlan p;
+    if (unfused_plan(d, 0, &p) != WTC_OK) return 0;
+    return p.total;
+}
+
+int wtconv_forward_unfused(const wtc_desc* d, const void* x, const float* w0, const float* s0,
+                           const float* b0, const float* wl, const float* sl, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
+    if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
+    UnfusedPlan p;
+    st = unfused_plan(d, 0, &p);
+    if (st != WTC_OK) return st;
+    if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return WTC_EWORKSPACE;
+    return unfused_forward(d, p, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), stream);
+}
+
+size_t wtconv_backward_unfused_workspace(const wtc_desc* d) {
+    UnfusedPlan p;
+    if (unfused_plan(d, 1, &p) != WTC_OK) return 0;
+    return p.total;
+}
+
+int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g, const float* w0,
+                            const float* s0, const float* wl, const float* sl, void* dx,
+                            float* dw0, float* ds0, float* db0, float* dwl, float* dsl,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
+    if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
+    UnfusedPlan p;
+    st = unfused_plan(d, 1, &p);
+    if (st != WTC_OK) return st;
+    if (!workspace || workspace_bytes < p.total) return WTC_EWORKSPACE;
+    return unfused_backward(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
+                            static_cast<char*>(workspace), stream);
+}
+
+// ---------------------------------------------------------------------------
+// I/O model and flop count
+// ---------------------------------------------------------------------------
+double wtconv_flops(const wtc_desc* d, int dir) {
+    if (check_desc(d) != WTC_OK || (dir != 0 && dir != 1)) return -1.0;
+    const double KK = (double)d->k * d->k;
+    const double BC = (double)d->B * d->C;
+    const double N = BC * d->H * d->W;
+    // forward: base conv (FMA) + bias/combine; per level: 4 subband convs (FMA),
+    // 8 add/sub analysis butterfly and 8 add/sub synthesis butterfly per position
+    double f = 2.0 * KK * N + 2.0 * N;
+    for (int i = 1; i <= d->L; ++i) f += BC * spec_level_area(d, i) * (2.0 * 4.0 * KK + 16.0);
+    if (dir == 0) return f;
+    // backward: dX is the same pipeline without the bias; the correlations repeat
+    // every FMA once more; x needs its own analysis cascade; sum of g
+    double b = f - N;
+    b += 2.0 * KK * N + N;
+    for (int i = 1; i <= d->L; ++i) b += BC * spec_level_area(d, i) * (2.0 * 4.0 * KK + 8.0);
+    return b;
+}
+
+double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
+    if (check_desc(d) != WTC_OK || (dir != 0 && dir != 1) || (impl != 0 && impl != 1)) return -1.0;
+    const double e = d->dtype == WTC_BF16 ? 2.0 : 4.0;
+    const double KK = (double)d->k * d->k;
+    const double BC = (double)d->B * d->C;
+    const double N = BC * d->H * d->W;
+    const double params = 4.0 * (d->C * KK * (1 + 4.0 * d->L) + d->C * (2.0 + 4.0 * d->L));
+    if (impl == 0) {
+        if (dir == 0) return 2.0 * N * e + params;
+        FusedPlan p;
+        if (plan_fused(d, true, &p) != WTC_OK) return -1.0;
+        const double partials = 4.0 * (double)p.nchunk * d->C * p.a.P;
+        // read x and g, write dx; params read; partials written then read; grads written
+        return 3.0 * N * e + params + 2.0 * partials + params;
+    }
+    UnfusedPlan p;
+    if (unfused_plan(d, dir, &p) != WTC_OK) return -1.0;
+    // level-by-level: every intermediate crosses HBM (fp32 intermediates)
+    const double f4 = 4.0;
+    double t = 0.0;
+    if (dir == 0) {
+        double prevLL = N * e;  // LL_0 = x (storage dtype)
+        for (int i = 1; i <= d->L; ++i) {
+            const double n = BC * spec_level_area(d, i);
+            t += prevLL + 4.0 * n * f4;          // analysis: read LL_{i-1}, write 4 bands
+            t += 4.0 * n * f4 * 2.0;              // subband conv: read bands, write Y_i
+            prevLL = n * f4;
+        }
+        for (int i = d->L; i >= 1; --i) {
+            const double n = BC * spec_level_area(d, i);
+            const double up = BC * spec_level_area(d, i - 1);
+            // synthesis: read Y_i (4 bands) and Z_{i+1}, write Z_i
+            t += 4.0 * n * f4 + (i < d->L ? n * f4 : 0.0) + up * (i == 1 ? f4 : f4);
+        }
+        // base conv + combine: read x, read Z_1, write out
+        t += N * e + (d->L > 0 ? N * f4 : 0.0) + N * e;
+        return t + params;
+    }
+    // backward: analysis cascade of g (read g / dZ_i, write 4 bands);
+    // recompute the bands of x (as forward); per level: dS conv (read dY, write dS),
+    // weight correlation (read dY and S), scale gradient (read dY, S -> conv);
+    // synthesis of dS back to dX; base: read g, x, write dx.
+    double prev = N * e;
+    double prevx = N * e;
+    for (int i = 1; i <= d->L; ++i) {
+        const double n = BC * spec_level_area(d, i);
+        t += prev + 4.0 * n * f4;                // analysis of dZ_i
+        t += prevx + 4.0 * n * f4;               // analysis of x (recompute S_i)
+        t += 4.0 * n * f4 * 2.0;                 // dS_i = s * rot(W) * dY_i: read dY, write dS
+        t += 4.0 * n * f4 * 2.0;                 // correlations: read dY and S
+        prev = n * f4;
+        prevx = n * f4;
+    }
+    for (int i = d->L; i >= 1; --i) {
+        const double n = BC * spec_level_area(d, i);
+        const double up = BC * spec_level_area(d, i - 1);
+        t += 4.0 * n * f4 + (i < d->L ? n * f4 : 0.0) + up * f4;
+    }
+    t += 2.0 * N * e + (d->L > 0 ? N * f4 : 0.0) + N * e;  // base: read g, x, dLL_0; write dx
+    t += N * e * 2.0;                                       // base correlations: read g, x
+    return t + 2.0 * params + 4.0 * (double)p.nblk * d->C * (d->k * d->k * (1 + 4.0 * d->L) + 2) * 2.0;
+}
+
+}  // extern "C"

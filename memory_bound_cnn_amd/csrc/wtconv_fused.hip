@@ -1,0 +1,79 @@
+// Fused WTConv: dispatch over the kernel size, and the backward finalize
+// kernel (deterministic cross-workgroup sum and chain rule through the folds).
+#include <hip/hip_runtime.h>
+
+#include "wtc_internal.h"
+
+namespace wtc {
+
+int launch_fused_k1(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_k3(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_k5(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_k7(const FusedArgs&, int, int, int, int, size_t, int, void*);
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Finalize: deterministic sum over chunks, then the chain rule through the folds
+// dW = 4^-i s C, ds = 4^-i sum_d W C (level 0: dW0 = s0 C_0, ds0 = sum W0 C_0).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f) {
+    extern __shared__ __align__(16) float tot[];
+    const int c = blockIdx.x, tid = threadIdx.x, nthr = blockDim.x;
+    const int KK = f.k * f.k;
+    for (int e = tid; e < f.P; e += nthr) {
+        float v = 0.f;
+        for (int ch = 0; ch < f.nchunk; ++ch) v += f.partials[((size_t)ch * f.C + c) * f.P + e];
+        tot[e] = v;
+    }
+    __syncthreads();
+    const float tail = tot[f.P - 1];
+    // level 0
+    for (int e = tid; e < KK; e += nthr) f.dw0[(size_t)c * KK + e] = f.s0[c] * tot[e];
+    if (tid == 0) {
+        float s = 0.f;
+        for (int e = 0; e < KK; ++e) s = fmaf(f.w0[(size_t)c * KK + e], tot[e], s);
+        f.ds0[c] = s;
+        f.db0[c] = tot[f.P - 2];
+    }
+    // levels 1..L
+    for (int e = tid; e < 4 * f.L * KK; e += nthr) {
+        const int i = e / (4 * KK), rem = e - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
+        const float cv = (i < f.Lm) ? tot[KK + e] : ((tap == KK / 2) ? tail : 0.f);
+        const size_t pi = ((size_t)i * f.C + c) * 4 + u;
+        f.dwl[pi * KK + tap] = ldexpf(f.sl[pi], -2 * (i + 1)) * cv;
+    }
+    for (int e = tid; e < 4 * f.L; e += nthr) {
+        const int i = e / 4, u = e - i * 4;
+        const size_t pi = ((size_t)i * f.C + c) * 4 + u;
+        float s = 0.f;
+        if (i < f.Lm) {
+            for (int tap = 0; tap < KK; ++tap) s = fmaf(f.wl[pi * KK + tap], tot[KK + (i * 4 + u) * KK + tap], s);
+        } else {
+            s = f.wl[pi * KK + KK / 2] * tail;
+        }
+        f.dsl[pi] = ldexpf(s, -2 * (i + 1));
+    }
+}
+
+}  // namespace
+
+int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nthr, size_t lds_bytes,
+                 int grid, void* stream) {
+    switch (k) {
+        case 1: return launch_fused_k1(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 3: return launch_fused_k3(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 5: return launch_fused_k5(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 7: return launch_fused_k7(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        default: return (int)hipErrorInvalidValue;
+    }
+}
+
+int launch_finalize(const FinalizeArgs& f, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const size_t lds = (size_t)f.P * sizeof(float);
+    hipLaunchKernelGGL(wtc_finalize_kernel, dim3(f.C), dim3(256), lds, st, f);
+    return (int)hipGetLastError();
+}
+
+}  // namespace wtc

@@ -1,0 +1,101 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/wtconv.h declares, rejects bad arguments before any HIP call,
+and reports workspace sizes, the I/O model and flop counts."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from memory_bound_cnn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "wtconv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(wtconv_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load_library()
+    names = _declared()
+    assert "wtconv_forward" in names and "wtconv_backward" in names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _desc(**kw):
+    a = dict(B=2, C=3, H=16, W=16, L=2, k=5, dtype=0, layout=0)
+    a.update(kw)
+    return binding.wtc_desc(a["B"], a["C"], a["H"], a["W"], a["L"], a["k"], a["dtype"], a["layout"])
+
+
+FAKE = ctypes.c_void_p(16)   # never dereferenced: every case below fails validation first
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=4), binding.WTC_EINVAL), (dict(k=0), binding.WTC_EINVAL), (dict(L=-1), binding.WTC_EINVAL),
+    (dict(B=0), binding.WTC_EINVAL), (dict(H=0), binding.WTC_EINVAL), (dict(dtype=7), binding.WTC_EDTYPE),
+    (dict(layout=1), binding.WTC_EDTYPE), (dict(H=512, W=512), binding.WTC_ESHAPE), (dict(k=9), binding.WTC_ESHAPE),
+])
+def test_forward_rejects(kw, status):
+    lib = binding.load_library()
+    d = _desc(**kw)
+    st = lib.wtconv_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == status
+
+
+def test_null_pointers_rejected():
+    lib = binding.load_library()
+    d = _desc()
+    assert lib.wtconv_forward(ctypes.byref(d), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == binding.WTC_EINVAL
+    assert lib.wtconv_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == binding.WTC_EINVAL
+    d0 = _desc(L=0)   # wl/sl may be NULL when L == 0 -- but here x is NULL
+    assert lib.wtconv_forward(ctypes.byref(d0), None, FAKE, FAKE, FAKE, None, None, FAKE, None, 0, None) == binding.WTC_EINVAL
+    assert lib.wtconv_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                               FAKE, FAKE, FAKE, 1 << 30, None) == binding.WTC_EINVAL
+    assert lib.wtconv_forward(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == binding.WTC_EINVAL
+
+
+def test_backward_workspace_checked():
+    lib = binding.load_library()
+    d = _desc()
+    need = lib.wtconv_backward_workspace(ctypes.byref(d))
+    assert need > 0
+    st = lib.wtconv_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, FAKE, need - 1, None)
+    assert st == binding.WTC_EWORKSPACE
+    st = lib.wtconv_backward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, None, need, None)
+    assert st == binding.WTC_EWORKSPACE
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert binding.wtconv_status_string(s)
+    assert "unknown" in binding.wtconv_status_string(42)
+
+
+def test_io_model_fused_is_minimal_traffic():
+    B, C, H, W, L, k = 32, 96, 64, 64, 3, 5
+    N = B * C * H * W
+    fwd = binding.wtconv_io_model_bytes(B, C, H, W, L, k, "fp32", 0, 0)
+    bwd = binding.wtconv_io_model_bytes(B, C, H, W, L, k, "fp32", 0, 1)
+    assert 2 * N * 4 <= fwd <= 2 * N * 4 * 1.01
+    assert 3 * N * 4 <= bwd <= 3 * N * 4 * 1.03
+    bf = binding.wtconv_io_model_bytes(B, C, H, W, L, k, "bf16", 0, 0)
+    assert 2 * N * 2 <= bf <= 2 * N * 2 * 1.02
+    assert binding.wtconv_io_model_bytes(B, C, H, W, L, 4, "fp32", 0, 0) < 0
+
+
+def test_flop_count_closed_form():
+    # forward FMAs per pixel at k=5, L=3 on a 64x64 plane: 25 + 100 (1/4 + 1/16 + 1/64)
+    B, C, H, W, L, k = 1, 1, 64, 64, 3, 5
+    N = H * W
+    f = binding.wtconv_flops(B, C, H, W, L, k, "fp32", 0)
+    fma = 25 + 100 * (1 / 4 + 1 / 16 + 1 / 64)
+    adds = 2 + 16 * (1 / 4 + 1 / 16 + 1 / 64)
+    assert abs(f - N * (2 * fma + adds)) < 1e-6 * f

@@ -1,0 +1,189 @@
+"""Parity of the fused HIP path (through the C ABI) with the float64 oracle.
+
+Element-by-element comparisons at sizes the oracle finishes in seconds (several
+8x8 blocks per plane, ragged tails, every plane-size class the launch planner
+distinguishes), and sampled comparisons at the full benchmark shapes.
+Tolerance per tensor: max|gpu - oracle| <= 1e-4 * RMS(oracle) for float32
+storage and 2e-2 * RMS(oracle) for bfloat16 storage.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from memory_bound_cnn_amd import binding
+from memory_bound_cnn_amd.inputs import WORKLOADS, workload_inputs
+from tests.gpu_helpers import (check_all, dev, host, inputs, oracle_ref, rel_err, run_fused, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(B, C, H, W, L, k, seed, dtype="fp32", impl="fused"):
+    d = inputs(B, C, H, W, L, k, seed, dtype)
+    t = to_dev(d, dtype, L)
+    out, gr = run_fused(t, L, impl)
+    ref_out, ref_gr = oracle_ref(d, L)
+    return check_all(out, gr, ref_out, ref_gr, dtype, f"{impl} B{B} C{C} {H}x{W} L{L} k{k} {dtype}")
+
+
+# Reduced-batch versions of every benchmark shape (same plane size, level count,
+# kernel and dtype, hence the same kernel variant and LDS layout).
+REDUCED = [
+    (1, 8, 32, 32, 2, 5, 0, "fp32"),       # tiny workload, full size
+    (2, 6, 64, 64, 3, 5, 10, "fp32"),      # stage-1 plane
+    (3, 8, 32, 32, 3, 5, 20, "bf16"),      # bf16 storage
+    (1, 3, 128, 128, 1, 5, 30, "fp32"),    # level sweep planes
+    (1, 3, 128, 128, 3, 5, 31, "fp32"),
+    (1, 2, 128, 128, 5, 5, 32, "fp32"),
+    (5, 8, 14, 14, 2, 5, 40, "fp32"),      # odd 14x14
+    (9, 8, 7, 7, 1, 5, 41, "fp32"),        # odd 7x7
+]
+
+
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", REDUCED)
+def test_reduced_workloads(B, C, H, W, L, k, seed, dtype):
+    _case(B, C, H, W, L, k, seed, dtype)
+
+
+EDGE = [
+    (2, 3, 16, 16, 0, 5, 50),      # L = 0: plain depthwise conv
+    (2, 3, 13, 10, 3, 3, 51),      # odd, unequal sides, k = 3
+    (1, 2, 7, 5, 3, 5, 52),        # deeper than the plane (tail levels)
+    (1, 2, 3, 3, 5, 3, 53),        # tail levels on a 1x1 grid
+    (2, 2, 1, 1, 2, 5, 54),        # 1x1 planes: every level is a tail level
+    (1, 2, 9, 17, 2, 7, 55),       # k = 7, ragged blocks
+    (2, 4, 24, 24, 2, 1, 56),      # k = 1
+    (1, 2, 40, 24, 4, 5, 57),      # several quad blocks, 4 levels
+    (3, 5, 8, 8, 3, 5, 58),        # one block per plane, three levels
+    (1, 1, 100, 36, 2, 5, 59),     # 100 quad blocks -> 512-thread plan
+]
+
+
+@pytest.mark.parametrize("B,C,H,W,L,k,seed", EDGE)
+def test_edge_cases(B, C, H, W, L, k, seed):
+    _case(B, C, H, W, L, k, seed)
+
+
+def test_bf16_odd_plane():
+    _case(3, 4, 14, 14, 2, 5, 60, "bf16")
+
+
+def test_batch_not_multiple_of_planes_per_workgroup():
+    # 7x7 planes run many planes per workgroup; B leaves a ragged last chunk
+    _case(37, 3, 7, 7, 1, 5, 61)
+
+
+def test_deterministic():
+    d = inputs(4, 6, 32, 32, 3, 5, 62)
+    t = to_dev(d)
+    a_out, a = run_fused(t, 3)
+    b_out, b = run_fused(t, 3)
+    assert torch.equal(a_out, b_out)
+    for key in a:
+        if a[key] is not None:
+            assert torch.equal(a[key], b[key]), key
+
+
+def test_adjoint_dot_on_gpu():
+    """<g, out(x) - out(0)> = <dx, x> using GPU results only."""
+    B, C, H, W, L, k = 2, 4, 32, 32, 3, 5
+    d = inputs(B, C, H, W, L, k, 63)
+    t = to_dev(d)
+    out, gr = run_fused(t, L)
+    t0 = dict(t)
+    t0["x"] = torch.zeros_like(t["x"])
+    out0 = binding.wtconv_forward(t0["x"], t["w0"], t["s0"], t["b0"], t["wl"], t["sl"], L)
+    lhs = (host(t["g"]).astype(np.float64) * (host(out) - host(out0))).sum()
+    rhs = (host(gr["dx"]).astype(np.float64) * host(t["x"])).sum()
+    assert abs(lhs - rhs) <= 1e-5 * (abs(lhs) + abs(rhs) + 1.0)
+
+
+def test_finite_differences_tiny():
+    """Every parameter gradient (and some input coordinates) on the tiny
+    workload by exact central differences of <g, out> with h = 1, using only
+    the GPU forward: the loss is affine in each single coordinate."""
+    wl_ = WORKLOADS["tiny_b1c8_32x32_L2"]
+    d = workload_inputs(wl_)
+    L = wl_.L
+    t = to_dev(d)
+    gr = binding.wtconv_backward(t["x"], t["g"], t["w0"], t["s0"], t["wl"], t["sl"], L)
+    g64 = d["g"].astype(np.float64)
+
+    def loss(tt):
+        o = binding.wtconv_forward(tt["x"], tt["w0"], tt["s0"], tt["b0"], tt["wl"], tt["sl"], L)
+        return float((host(o).astype(np.float64) * g64).sum())
+
+    names = dict(w0="dw0", s0="ds0", b0="db0", wl="dwl", sl="dsl")
+    for name, gname in names.items():
+        base = t[name]
+        flat = base.view(-1)
+        fd = np.zeros(flat.numel())
+        for i in range(flat.numel()):
+            old = float(flat[i])
+            flat[i] = old + 1.0
+            lp = loss(t)
+            flat[i] = old - 1.0
+            lm = loss(t)
+            flat[i] = old
+            fd[i] = (lp - lm) / 2.0
+        got = host(gr[gname]).ravel()
+        assert rel_err(got, fd) <= 1e-3, (name, rel_err(got, fd))
+    # dx at the four corners and at random pixels
+    xf = t["x"].view(-1)
+    H, W = wl_.H, wl_.W
+    idxs = [0, W - 1, (H - 1) * W, H * W - 1] + list(np.random.default_rng(0).integers(0, xf.numel(), 12))
+    gdx = host(gr["dx"]).ravel()
+    rms = np.sqrt(np.mean(gdx ** 2))
+    for i in idxs:
+        old = float(xf[i])
+        xf[i] = old + 1.0
+        lp = loss(t)
+        xf[i] = old - 1.0
+        lm = loss(t)
+        xf[i] = old
+        assert abs((lp - lm) / 2.0 - gdx[i]) <= 1e-3 * rms, i
+
+
+FULL = ["stage1_b32c96_64x64_L3", "bf16_b64c192_32x32_L3", "odd_b128c384_14x14_L2", "odd_b128c768_7x7_L1"]
+
+
+def _full_sampled(wl_, L):
+    """Full-size launch (the benchmark's launch configuration); out and dx checked
+    on two sampled batch entries; weight gradients checked with g masked to
+    those entries, so the oracle only needs those entries."""
+    d = workload_inputs(wl_)
+    rng = np.random.default_rng(7)
+    batch = np.sort(rng.choice(wl_.B, size=2, replace=False))
+    mask = np.zeros(wl_.B, dtype=bool)
+    mask[batch] = True
+    d = dict(d)
+    d["g"] = np.where(mask[:, None, None, None], d["g"], 0.0).astype(np.float32)
+    t = to_dev(d, wl_.dtype, L)
+    if L < (t["wl"].shape[0] if t["wl"] is not None else 0):
+        t["wl"], t["sl"] = t["wl"][:L].contiguous(), t["sl"][:L].contiguous()
+    out, gr = run_fused(t, L)
+    dd = dict(d)
+    dd["x"], dd["g"] = d["x"][batch], d["g"][batch]
+    ref_out, ref_gr = oracle_ref(dd, L)
+    o = host(out)[batch]
+    gr_h = {k: host(v) for k, v in gr.items()}
+    gr_h["dx"] = gr_h["dx"][batch]
+    tol = 1e-4 if wl_.dtype == "fp32" else 2e-2
+    errs = {"out": rel_err(o, ref_out)}
+    for k in ("dx", "dw0", "ds0", "db0", "dwl", "dsl"):
+        if ref_gr.get(k) is not None:
+            errs[k] = rel_err(gr_h[k], ref_gr[k])
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{wl_.name} L{L}: {bad} (all {errs})"
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    wl_ = WORKLOADS[name]
+    _full_sampled(wl_, wl_.L)
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4, 5])
+def test_full_size_sweep_sampled(L):
+    _full_sampled(WORKLOADS["sweep_b64c96_128x128"], L)
