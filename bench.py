@@ -1,0 +1,332 @@
+"""Benchmark of the fused WTConv forward + backward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--impl fused|unfused]
+                    [--no-cpu-baseline] [--no-summary]
+
+One step = one wtconv_forward + one wtconv_backward (every kernel of the hot
+path) over one batch of synthetic, seeded inputs already resident in HBM.
+Input buffer sets are rotated so that the working set of consecutive steps
+exceeds the 256 MB Infinity Cache.  Prints ONE JSON line.
+
+value  = achieved HBM throughput of the step in GB/s: the fused I/O model's
+         algorithmic bytes (forward: read x, write out; backward: read x and g,
+         write dx; plus parameters and partial sums) / measured step time.
+roofline = the dominant call (the backward pass) against the VALU peak it is
+         bound by, timed live with HIP events on the launch stream.
+cpu_baseline = the float64 CPU oracle on the host's cores (a baseline, not a target).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+# fp32 VALU peak without packed-FP32 instructions: 256 CUs x 4 SIMDs x 16 lanes
+# x 2 flop (FMA) x 2.4 GHz.  (Packed FP32 FMA doubles this to 157.3 TFLOP/s;
+# the library is built with packed-FP32 instructions disabled.)
+VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+VALU_PACKED_PEAK_TFLOPS = 2 * VALU_PEAK_TFLOPS
+HEADLINE = "stage1_b32c96_64x64_L3"
+MALL_BYTES = 256 * 2 ** 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=HEADLINE)
+    p.add_argument("--level", type=int, default=None, help="override L (sweep workload)")
+    p.add_argument("--impl", default="fused", choices=["fused", "unfused"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-summary", action="store_true")
+    p.add_argument("--profile-steps", type=int, default=None,
+                   help="run only this many steps, no summary / CPU baseline (for rocprofv3)")
+    p.add_argument("--copy-probe-mib", type=int, default=None,
+                   help="run a plain device copy (read N + write N bytes) 3 times, to calibrate "
+                        "rocprofv3 FETCH_SIZE / WRITE_SIZE against known traffic")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "memory_bound_cnn_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+class Runner:
+    """Device buffers for one workload and one implementation."""
+
+    def __init__(self, wl, L, impl, torch, binding, rotate=True):
+        from memory_bound_cnn_amd.inputs import workload_inputs
+        self.torch, self.b = torch, binding
+        self.wl, self.L, self.impl = wl, L, impl
+        dev = torch.device("cuda", 0)
+        d = workload_inputs(wl)
+        sd = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        e = 2 if wl.dtype == "bf16" else 4
+        N = wl.B * wl.C * wl.H * wl.W
+        set_bytes = 4 * N * e
+        R = max(1, min(8, math.ceil(4 * MALL_BYTES / set_bytes))) if rotate else 1
+        self.R = R
+        x = torch.from_numpy(d["x"]).to(dev).to(sd)
+        g = torch.from_numpy(d["g"]).to(dev).to(sd)
+        self.sets = []
+        for r in range(R):
+            xs = x if r == 0 else x.roll(r, dims=0).contiguous()
+            gs = g if r == 0 else g.roll(r, dims=0).contiguous()
+            self.sets.append(dict(x=xs, g=gs, out=torch.empty_like(x), dx=torch.empty_like(x)))
+        f = lambda a: torch.from_numpy(a).to(dev)
+        self.w0, self.s0, self.b0 = f(d["w0"]), f(d["s0"]), f(d["b0"])
+        self.wl_ = f(d["wl"][:L]).contiguous() if L > 0 else None
+        self.sl_ = f(d["sl"][:L]).contiguous() if L > 0 else None
+        C, k = wl.C, wl.k
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.grads = dict(dw0=torch.empty(C, k, k, **f32), ds0=torch.empty(C, **f32), db0=torch.empty(C, **f32),
+                          dwl=torch.empty(L, 4 * C, k, k, **f32) if L > 0 else None,
+                          dsl=torch.empty(L, 4 * C, **f32) if L > 0 else None)
+        shp = (wl.B, wl.C, wl.H, wl.W, L, k, wl.dtype)
+        if impl == "fused":
+            self.fwd, self.bwd = binding.wtconv_forward, binding.wtconv_backward
+            wsf, wsb = binding.wtconv_forward_workspace(*shp), binding.wtconv_backward_workspace(*shp)
+        else:
+            self.fwd, self.bwd = binding.wtconv_forward_unfused, binding.wtconv_backward_unfused
+            wsf = binding.wtconv_forward_unfused_workspace(*shp)
+            wsb = binding.wtconv_backward_unfused_workspace(*shp)
+        self.ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device=dev)
+        self.ws_b = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        self.N, self.e = N, e
+
+    def step(self, i, ev=None):
+        s = self.sets[i % self.R]
+        if ev is not None:
+            ev[0].record()
+        self.fwd(s["x"], self.w0, self.s0, self.b0, self.wl_, self.sl_, self.L, out=s["out"], workspace=self.ws_f)
+        if ev is not None:
+            ev[1].record()
+        self.bwd(s["x"], s["g"], self.w0, self.s0, self.wl_, self.sl_, self.L, dx=s["dx"], grads=self.grads,
+                 workspace=self.ws_b)
+        if ev is not None:
+            ev[2].record()
+
+    def time(self, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            self.step(i, evs[i])
+        stop.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        return total_ms / steps, fwd_ms, bwd_ms
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host cores
+# ---------------------------------------------------------------------------
+def _oracle_task(args):
+    os.environ["OMP_NUM_THREADS"] = "1"
+    x, g, w0, s0, b0, wl_, sl_, L = args
+    import oracle
+    t0 = time.perf_counter()
+    oracle.forward(x, w0, s0, b0, wl_, sl_, L)
+    oracle.backward(x, g, w0, s0, b0, wl_, sl_, L)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
+    """Time the float64 oracle (forward + backward) on a bounded sample of the
+    workload: whole batch entries, one per task, in a pool of host processes."""
+    from memory_bound_cnn_amd.inputs import workload_inputs
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    cores = max(1, min(16, ncpu))
+    d = workload_inputs(wl)
+    wl_ = d["wl"][:L] if L > 0 else None
+    sl_ = d["sl"][:L] if L > 0 else None
+    task = lambda b: (d["x"][b:b + 1], d["g"][b:b + 1], d["w0"], d["s0"], d["b0"], wl_, sl_, L)
+    t1 = _oracle_task(task(0))                      # one entry, one core: sizes the sample
+    n_entries = int(min(wl.B, max(cores, budget_s * cores / max(t1, 1e-3))))
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_task, [task(0)] * cores)   # warm the workers (imports)
+        t0 = time.perf_counter()
+        pool.map(_oracle_task, [task(b) for b in range(n_entries)], chunksize=1)
+        wall = time.perf_counter() - t0
+    value = n_entries * bytes_per_batch_entry / wall / 1e9
+    return dict(value=value, unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{n_entries} of {wl.B} batch entries of {wl.name} (L={L}): float64 NumPy oracle, "
+                       f"forward + backward, one batch entry per task on a pool of {cores} processes "
+                       f"(1 thread each); wall {wall:.2f} s; one entry on one core {t1:.3f} s",
+                wall_s=round(wall, 3), entries=n_entries)
+
+
+# ---------------------------------------------------------------------------
+def traffic_from_profiles(wl, L):
+    """HBM bytes per backward launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except ValueError:
+        return None
+    key = f"{wl.name}_L{L}"
+    r = rec.get("workloads", {}).get(key)
+    if not r or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return r
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU: the operator has no multi-GPU path "
+                                   "(batch sharding needs only an all-reduce of the tiny weight gradients); "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+    from memory_bound_cnn_amd import binding
+    from memory_bound_cnn_amd.inputs import WORKLOADS
+    binding.load_library()
+    wl = WORKLOADS[a.workload]
+    L = wl.L if a.level is None else a.level
+    shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
+    io_f = binding.wtconv_io_model_bytes(*shp, impl=0, direction=0)
+    io_b = binding.wtconv_io_model_bytes(*shp, impl=0, direction=1)
+
+    # The CPU baseline runs first, before this process touches the GPU.
+    cpu = None
+    if not a.no_cpu_baseline and a.profile_steps is None and a.copy_probe_mib is None:
+        cpu = cpu_baseline(wl, L, (io_f + io_b) / wl.B)
+        cpu["value"] = round(cpu["value"], 4)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+
+    if a.copy_probe_mib is not None:
+        n = a.copy_probe_mib * 2 ** 20 // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 3}))
+        return
+
+    if a.profile_steps is not None:
+        r = Runner(wl, L, a.impl, torch, binding)
+        r.time(a.profile_steps, 2)
+        print(json.dumps({"profile_run": wl.name, "L": L, "impl": a.impl, "steps": a.profile_steps}))
+        return
+
+    r = Runner(wl, L, a.impl, torch, binding)
+    ms, fwd_ms, bwd_ms = r.time(a.steps, a.warmup)
+    fl_f = binding.wtconv_flops(*shp, direction=0)
+    fl_b = binding.wtconv_flops(*shp, direction=1)
+    gbps = (io_f + io_b) / (ms * 1e-3) / 1e9
+    tflops_b = fl_b / (bwd_ms * 1e-3) / 1e12
+    tflops_f = fl_f / (fwd_ms * 1e-3) / 1e12
+    line = {
+        "metric": "WTConv fwd+bwd ms/iter and achieved HBM GB/s (% of MI355X peak) per level L",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if wl.dtype == "fp32" else "bf16-storage/f32-compute",
+        "data": "synthetic (seeded N(0,1) inputs and gradients, N(0,1/k^2) weights, U[0.05,0.5] scales)",
+        "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W, "L": L, "k": wl.k,
+                   "storage": wl.dtype, "impl": a.impl},
+        "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "fwd_ms": round(fwd_ms, 5),
+        "bwd_ms": round(bwd_ms, 5),
+        "io_model_bytes": {"fwd": io_f, "bwd": io_b},
+        "flops": {"fwd": fl_f, "bwd": fl_b},
+        "buffer_sets_rotated": r.R,
+    }
+    tr = traffic_from_profiles(wl, L)
+    line["roofline"] = {
+        "bound": "alu",
+        "kernel": "wtconv_backward (fused backward kernel + finalize), the dominant call",
+        "achieved": round(tflops_b, 3),
+        "peak": round(VALU_PEAK_TFLOPS, 1),
+        "unit": "TFLOP/s",
+        "frac": round(tflops_b / VALU_PEAK_TFLOPS, 4),
+        "traffic": tr["bwd_bytes"] if tr else None,
+        "peak_packed_fp32": round(VALU_PACKED_PEAK_TFLOPS, 1),
+        "algorithmic_flops_per_launch": fl_b,
+        "launch_ms": round(bwd_ms, 5),
+        "hbm_gbps_of_kernel": round(io_b / (bwd_ms * 1e-3) / 1e9, 1),
+        "forward": {"achieved": round(tflops_f, 3), "frac": round(tflops_f / VALU_PEAK_TFLOPS, 4),
+                    "hbm_gbps": round(io_f / (fwd_ms * 1e-3) / 1e9, 1),
+                    "traffic": tr["fwd_bytes"] if tr else None},
+    }
+    if tr:
+        line["measured_bytes_over_model"] = {"fwd": tr["fwd_bytes"] / io_f, "bwd": tr["bwd_bytes"] / io_b}
+
+    if not a.no_summary:
+        summary = []
+        for name, w in WORKLOADS.items():
+            levels = w.sweep if w.sweep else (w.L,)
+            for Lw in levels:
+                ww = w.at_level(Lw)
+                sh = (ww.B, ww.C, ww.H, ww.W, Lw, ww.k, ww.dtype)
+                row = {"workload": name, "L": Lw}
+                for impl in ("fused", "unfused"):
+                    try:
+                        rr = Runner(ww, Lw, impl, torch, binding)
+                        steps = max(10, min(100, int(2e5 / max(1, ww.B * ww.C * ww.H * ww.W / 1e3))))
+                        m, mf, mb = rr.time(steps, 5)
+                        del rr
+                        torch.cuda.empty_cache()
+                    except Exception as ex:  # noqa: BLE001 - report and continue
+                        row[impl] = {"error": str(ex)[:200]}
+                        continue
+                    model = binding.wtconv_io_model_bytes(*sh, impl=0, direction=0) + \
+                        binding.wtconv_io_model_bytes(*sh, impl=0, direction=1)
+                    fl = binding.wtconv_flops(*sh, direction=0) + binding.wtconv_flops(*sh, direction=1)
+                    row[impl] = {"ms": round(m, 5), "fwd_ms": round(mf, 5), "bwd_ms": round(mb, 5),
+                                 "gbps_fused_model": round(model / (m * 1e-3) / 1e9, 1),
+                                 "pct_hbm_peak": round(100 * model / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                                 "pct_valu_peak": round(100 * fl / (m * 1e-3) / 1e12 / VALU_PEAK_TFLOPS, 2)}
+                if "ms" in row.get("fused", {}) and "ms" in row.get("unfused", {}):
+                    row["speedup_vs_unfused"] = round(row["unfused"]["ms"] / row["fused"]["ms"], 3)
+                    row["unfused_model_bytes"] = binding.wtconv_io_model_bytes(*sh, impl=1, direction=0) + \
+                        binding.wtconv_io_model_bytes(*sh, impl=1, direction=1)
+                summary.append(row)
+        line["per_workload"] = summary
+
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
+        line["gpu_over_cpu"] = round(gbps / cpu["value"], 1)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

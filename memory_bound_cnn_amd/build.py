@@ -25,7 +25,9 @@ COMMON = [
 ]
 
 SOURCES = ["wtconv_fused.hip", "wtconv_fused_k1.hip", "wtconv_fused_k3.hip", "wtconv_fused_k5.hip",
-           "wtconv_fused_k7.hip", "wtconv_unfused.hip", "wtconv_api.cpp"]
+           "wtconv_fused_k7.hip", "wtconv_fused_s_p64.hip", "wtconv_fused_s_p32.hip",
+           "wtconv_fused_s_p128a.hip", "wtconv_fused_s_p128b.hip", "wtconv_fused_s_small.hip",
+           "wtconv_unfused.hip", "wtconv_api.cpp"]
 
 
 def _compile(src):
@@ -39,7 +41,7 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(OBJDIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         results = list(ex.map(_compile, SOURCES))
     objs = [o for o, _ in results]
     if verbose:

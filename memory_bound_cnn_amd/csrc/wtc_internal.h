@@ -12,9 +12,83 @@ namespace wtc {
 constexpr int kMaxLm = 7;   // levels evaluated on a grid larger than 1x1 (planes <= 128)
 constexpr int kMaxK = 7;
 
+// LDS layout of one plane slot (all offsets and sizes in floats).
+// Order: [level-1 .. level-early bands][level-0 plane | later arrays][tail].
+// Arrays first written after the level-0 phase (deeper bands, deep conv
+// results, x bands) may overlap the level-0 plane ("overlap").
+struct Layout {
+    int early_lv;      // levels analysed in registers during the level-0 phase (<= 3)
+    int overlap;       // later arrays overlap the level-0 plane (rings re-zeroed per plane)
+    int slot;          // floats per plane slot
+    int a0_off, a0_S, a0_rows;                 // level-0 plane with halo k/2
+    int b_off[kMaxLm + 1], b_S[kMaxLm + 1];    // level-i raw bands with halo k/2
+    int b_bs[kMaxLm + 1], b_rows[kMaxLm + 1];  // band stride, rows (incl. halo)
+    int yd_off[kMaxLm + 1];                    // Y'_i (i >= 3), [4][Hq_i][Wq_i]
+    int xb_off[kMaxLm + 1];                    // backward: bands of x (i >= 3), [4][Hq_i][Wq_i]
+    int tail_off;                              // tail term rho * kappa
+};
+
+constexpr int lay_round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// The one definition of the slot layout, evaluated on the host for the
+// runtime-geometry kernel and at compile time for the fixed-geometry ones.
+constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd) {
+    Layout L{};
+    const int R = k / 2;
+    L.early_lv = Lm < early_req ? Lm : early_req;
+    int off = 0;
+    for (int i = 1; i <= Lm; ++i) {
+        L.b_rows[i] = (Hq >> i) + 2 * R;
+        L.b_S[i] = lay_round_up((Wq >> i) + 2 * R, 4);
+        // band stride = 8 (mod 32) floats: the four subbands start in different LDS banks
+        L.b_bs[i] = lay_round_up(L.b_rows[i] * L.b_S[i], 32) + 8;
+    }
+    for (int i = 1; i <= L.early_lv; ++i) {
+        L.b_off[i] = off;
+        off += lay_round_up(4 * L.b_bs[i], 4);
+    }
+    L.a0_rows = Hq + 2 * R;
+    L.a0_S = lay_round_up(Wq + 2 * R, 4);
+    const int a0_size = lay_round_up(L.a0_rows * L.a0_S, 4);
+    int r2 = 0;
+    int rel_b[kMaxLm + 1] = {}, rel_y[kMaxLm + 1] = {}, rel_x[kMaxLm + 1] = {};
+    for (int i = L.early_lv + 1; i <= Lm; ++i) {
+        rel_b[i] = r2;
+        r2 += lay_round_up(4 * L.b_bs[i], 4);
+    }
+    for (int i = 3; i <= Lm; ++i) {
+        rel_y[i] = r2;
+        r2 += lay_round_up(4 * (Hq >> i) * (Wq >> i), 4);
+        if (bwd) {
+            rel_x[i] = r2;
+            r2 += lay_round_up(4 * (Hq >> i) * (Wq >> i), 4);
+        }
+    }
+    L.a0_off = off;
+    int r2_base = off;
+    if (r2 <= a0_size) {
+        L.overlap = r2 > 0 ? 1 : 0;
+        off += a0_size;
+    } else {
+        L.overlap = 0;
+        off += a0_size;
+        r2_base = off;
+        off += r2;
+    }
+    for (int i = L.early_lv + 1; i <= Lm; ++i) L.b_off[i] = r2_base + rel_b[i];
+    for (int i = 3; i <= Lm; ++i) {
+        L.yd_off[i] = r2_base + rel_y[i];
+        if (bwd) L.xb_off[i] = r2_base + rel_x[i];
+    }
+    L.tail_off = off;
+    off += 4;
+    L.slot = lay_round_up(off, 4);
+    return L;
+}
+
 // Arguments of the fused plane-pipeline kernel.  All offsets are in floats.
-// One workgroup owns one channel c and a chunk of batch entries; it walks the
-// chunk NP planes at a time, each plane held in an LDS "slot".
+// A workgroup walks a contiguous range of planes in channel-major order, NP
+// planes at a time, each plane held in an LDS "slot".
 struct FusedArgs {
     const void* src;   // forward: x;  backward: g  (the tensor that is convolved)
     const void* aux;   // backward: x (correlation partner); forward: unused
@@ -24,36 +98,27 @@ struct FusedArgs {
     const float* wl;
     const float* sl;
     void* dst;         // forward: out;  backward: dx
-    float* partials;   // backward: [nchunk][C][P] per-workgroup correlation sums
+    float* partials;   // backward: [grid][2][P] per-(workgroup, channel segment) sums
 
     int B, C, H, W;
     int L;             // levels requested
     int Lm;            // levels on grids larger than 1x1; levels Lm+1..L are 1x1 ("tail")
     int Hq, Wq;        // zero-extended plane: multiples of max(8, 2^Lm)
-    int bpc;           // batch entries per workgroup
+    int ppw;           // planes per workgroup (channel-major range, <= B)
     int NP;            // plane slots per workgroup iteration
     int qpp, nqx;      // 8x8 pixel blocks ("quad blocks") per plane, per plane row
     int vec;           // W % 4 == 0: 4-pixel vector global accesses
-    int overlap;       // level>=2 arrays overlap the level-0 array (rings re-zeroed)
-    int slot_stride;
-
-    int a0_off, a0_S, a0_rows;                 // level-0 plane with halo k/2
-    int b_off[kMaxLm + 1], b_S[kMaxLm + 1];    // level-i raw bands with halo k/2
-    int b_bs[kMaxLm + 1], b_rows[kMaxLm + 1];  // band stride, rows (incl. halo)
-    int z_off[kMaxLm + 1];                     // Z_i (i >= 2) on the level i-1 grid
-    int yd_off[kMaxLm + 1];                    // Y'_i (i >= 3), [4][Hq_i][Wq_i]
-    int xl2_off;                               // backward: LL_2 of x, [Hq_2][Wq_2]
-    int xb_off[kMaxLm + 1];                    // backward: bands of x (i >= 3), [4][Hq_i][Wq_i]
-    int tail_off;                              // per slot: tail term rho * kappa
-    int wts_off;                               // folded weights (per workgroup)
-    int red_off;                               // reduction scratch (backward)
-    int dsub;                                  // position subsets of the deep-level correlation
-    int P;                                     // partial record length (floats)
+    int pf_on;         // prefetch the next planes into registers
+    Layout lay;
+    int wts_off;       // folded weights (per workgroup)
+    int red_off;       // reduction scratch (backward)
+    int dsub;          // position subsets of the deep-level correlation
+    int P;             // partial record length (floats)
 };
 
-// Partial record of one (chunk, channel): [C_0 (k*k)] [levels 1..Lm: 4 bands x k*k]
+// Partial record of one (workgroup, channel segment): [C_0 (k*k)] [levels 1..Lm: 4 bands x k*k]
 // [sum g] [tail correlation]; all correlations in natural tap order.
-inline int partial_len(int k, int Lm) { return k * k * (1 + 4 * Lm) + 2; }
+constexpr int partial_len(int k, int Lm) { return k * k * (1 + 4 * Lm) + 2; }
 
 struct FinalizeArgs {
     const float* partials;
@@ -66,7 +131,7 @@ struct FinalizeArgs {
     float* db0;
     float* dwl;
     float* dsl;
-    int C, L, Lm, k, nchunk, P;
+    int C, B, L, Lm, k, ppw, P;
 };
 
 // Launchers (defined in the .hip files); return a hipError_t as int.

@@ -12,7 +12,7 @@ namespace {
 
 constexpr size_t kLdsLimit = 160 * 1024;       // gfx950 LDS per workgroup
 constexpr size_t kMultiPlaneBudget = 64 * 1024; // small planes: leave room for >= 2 workgroups / CU
-constexpr int kTargetWorkgroups = 1024;        // backward: ~4 resident workgroups per CU
+constexpr int kComputeUnits = 256;             // MI355X
 
 int ceil_log2(int v) {
     int l = 0;
@@ -37,73 +37,6 @@ struct FusedPlan {
     size_t lds;
 };
 
-// Per-slot LDS layout for one plane (floats).  Returns the slot size.
-int slot_layout(FusedArgs& a, int k, bool bwd) {
-    const int R = k / 2;
-    const int Lm = a.Lm;
-    int off = 0;
-    // level-1 bands (never overlapped: their halo rings are zeroed once)
-    for (int i = 0; i <= kMaxLm; ++i) {
-        a.b_off[i] = a.b_S[i] = a.b_bs[i] = a.b_rows[i] = 0;
-        a.z_off[i] = a.yd_off[i] = a.xb_off[i] = 0;
-    }
-    auto band_geom = [&](int i) {
-        a.b_rows[i] = (a.Hq >> i) + 2 * R;
-        a.b_S[i] = round_up((a.Wq >> i) + 2 * R, 4);
-        // band stride = 8 (mod 32) floats: the four subbands start in different LDS banks
-        a.b_bs[i] = round_up(a.b_rows[i] * a.b_S[i], 32) + 8;
-    };
-    if (Lm >= 1) {
-        band_geom(1);
-        a.b_off[1] = off;
-        off += round_up(4 * a.b_bs[1], 4);
-    }
-    // level-0 plane
-    a.a0_rows = a.Hq + 2 * R;
-    a.a0_S = round_up(a.Wq + 2 * R, 4);
-    const int a0_size = round_up(a.a0_rows * a.a0_S, 4);
-    // level >= 2 region
-    int r2 = 0;
-    auto take = [&](int n) {
-        const int o = r2;
-        r2 += round_up(n, 4);
-        return o;
-    };
-    int rel_b[kMaxLm + 1] = {0}, rel_z[kMaxLm + 1] = {0}, rel_y[kMaxLm + 1] = {0},
-        rel_x[kMaxLm + 1] = {0};
-    int rel_xl2 = 0;
-    for (int i = 2; i <= Lm; ++i) {
-        band_geom(i);
-        rel_b[i] = take(4 * a.b_bs[i]);
-        rel_z[i] = take((a.Hq >> (i - 1)) * (a.Wq >> (i - 1)));
-        if (i >= 3) rel_y[i] = take(4 * (a.Hq >> i) * (a.Wq >> i));
-        if (bwd && i >= 3) rel_x[i] = take(4 * (a.Hq >> i) * (a.Wq >> i));
-    }
-    if (bwd && Lm >= 3) rel_xl2 = take((a.Hq >> 2) * (a.Wq >> 2));
-    a.a0_off = off;
-    int r2_base;
-    if (r2 <= a0_size) {
-        a.overlap = (r2 > 0) ? 1 : 0;
-        r2_base = off;
-        off += a0_size;
-    } else {
-        a.overlap = 0;
-        off += a0_size;
-        r2_base = off;
-        off += r2;
-    }
-    for (int i = 2; i <= Lm; ++i) {
-        a.b_off[i] = r2_base + rel_b[i];
-        a.z_off[i] = r2_base + rel_z[i];
-        if (i >= 3) a.yd_off[i] = r2_base + rel_y[i];
-        if (bwd && i >= 3) a.xb_off[i] = r2_base + rel_x[i];
-    }
-    a.xl2_off = r2_base + rel_xl2;
-    a.tail_off = off;
-    off += 4;
-    return round_up(off, 4);
-}
-
 int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     int st = check_desc(d);
     if (st != WTC_OK) return st;
@@ -121,9 +54,12 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.nqx = a.Wq / 8;
     a.qpp = (a.Hq / 8) * a.nqx;
     a.vec = (d->W % 4 == 0) ? 1 : 0;
-    const int slot = slot_layout(a, k, bwd);
-    a.slot_stride = slot;
-    const int wts_n = round_up(KK * (1 + 4 * d->L) + 2, 4);
+    // levels 2 and 3 are analysed in registers when their bands fit beside the
+    // level-0 plane; otherwise (large planes) in flat loops after it
+    const int wts_n = round_up(KK * (1 + 4 * d->L) + 4, 4);
+    a.lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd);
+    if ((size_t)(a.lay.slot + wts_n) * 4 > kLdsLimit) a.lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd);
+    const int slot = a.lay.slot;
 
     int nthr, bpq = 1, NP = 1;
     if (a.qpp <= 64) {
@@ -152,6 +88,13 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         return WTC_ESHAPE;
     }
     a.NP = NP;
+    {
+        // prefetch when every thread's share of a plane group fits 16 floats
+        const int per = a.vec ? d->H * (d->W / 4) : d->H * d->W;
+        const int units = cdiv(NP * per, nthr);
+        a.pf_on = (units * (a.vec ? 4 : 1) <= 16) ? 1 : 0;
+        if (NP * per >= 65536) return WTC_ESHAPE;   // fast in-kernel index division range
+    }
     a.dsub = std::max(1, nthr / (4 * KK));
     if (bwd && a.Lm >= 3 && nthr < 4 * KK) return WTC_ESHAPE;
     a.wts_off = NP * slot;
@@ -163,19 +106,23 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     p->lds = lds_floats * 4;
     if (p->lds > kLdsLimit) return WTC_ESHAPE;
 
-    // work split over batch
-    const int iters = cdiv(d->B, NP);
-    int nchunk;
-    if (bwd) {
-        nchunk = std::max(1, std::min(iters, (kTargetWorkgroups + d->C / 2) / d->C));
-    } else {
-        nchunk = iters;
-    }
-    const int it_per = cdiv(iters, nchunk);
-    a.bpc = it_per * NP;
-    nchunk = cdiv(d->B, a.bpc);
-    p->nchunk = nchunk;
-    p->grid = nchunk * d->C;
+    // Work split over the batch: one resident "wave" of workgroups over the
+    // whole chip, each walking a chunk of planes of one channel.  Resident
+    // workgroups per CU: LDS-limited, and register-limited to about 4 (forward)
+    // or 2 (backward) waves per SIMD.
+    const int waves_per_wg = nthr / 64;
+    const int lds_wgs = (int)std::max<size_t>(1, kLdsLimit / std::max<size_t>(p->lds, 1));
+    const int reg_wgs = std::max(1, (4 * (bwd ? 2 : 4)) / waves_per_wg);
+    const int wgs_per_cu = std::max(1, std::min(lds_wgs, reg_wgs));
+    const long qtot = (long)d->B * d->C;
+    const long slots = (long)kComputeUnits * wgs_per_cu;
+    long ppw = (qtot + slots - 1) / slots;
+    ppw = (ppw + NP - 1) / NP * NP;            // whole plane groups where channels allow
+    ppw = std::min<long>(ppw, d->B);           // at most two channel segments per workgroup
+    a.ppw = (int)std::max<long>(1, ppw);
+    const int grid = (int)((qtot + a.ppw - 1) / a.ppw);
+    p->nchunk = grid;
+    p->grid = grid;
     p->nthr = nthr;
     p->bpq = bpq;
     return WTC_OK;
@@ -239,7 +186,7 @@ int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const floa
 size_t wtconv_backward_workspace(const wtc_desc* d) {
     FusedPlan p;
     if (plan_fused(d, true, &p) != WTC_OK) return 0;
-    return (size_t)p.nchunk * d->C * p.a.P * sizeof(float);
+    return (size_t)p.grid * 2 * p.a.P * sizeof(float);
 }
 
 int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -253,7 +200,7 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     FusedPlan p;
     st = plan_fused(d, true, &p);
     if (st != WTC_OK) return st;
-    const size_t need = (size_t)p.nchunk * d->C * p.a.P * sizeof(float);
+    const size_t need = (size_t)p.grid * 2 * p.a.P * sizeof(float);
     if (!workspace || workspace_bytes < need) return WTC_EWORKSPACE;
     FusedArgs& a = p.a;
     a.src = g;
@@ -267,7 +214,7 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     f.partials = a.partials;
     f.w0 = w0; f.s0 = s0; f.wl = wl; f.sl = sl;
     f.dw0 = dw0; f.ds0 = ds0; f.db0 = db0; f.dwl = dwl; f.dsl = dsl;
-    f.C = d->C; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.nchunk = p.nchunk; f.P = a.P;
+    f.C = d->C; f.B = d->B; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.ppw = a.ppw; f.P = a.P;
     e = launch_finalize(f, stream);
     return e == 0 ? WTC_OK : WTC_EHIP;
 }
@@ -349,7 +296,7 @@ double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
         if (dir == 0) return 2.0 * N * e + params;
         FusedPlan p;
         if (plan_fused(d, true, &p) != WTC_OK) return -1.0;
-        const double partials = 4.0 * (double)p.nchunk * d->C * p.a.P;
+        const double partials = 4.0 * (double)p.grid * 2 * p.a.P;
         // read x and g, write dx; params read; partials written then read; grads written
         return 3.0 * N * e + params + 2.0 * partials + params;
     }

@@ -6,10 +6,15 @@
 
 namespace wtc {
 
-int launch_fused_k1(const FusedArgs&, int, int, int, int, size_t, int, void*);
-int launch_fused_k3(const FusedArgs&, int, int, int, int, size_t, int, void*);
-int launch_fused_k5(const FusedArgs&, int, int, int, int, size_t, int, void*);
-int launch_fused_k7(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_rt_k1(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_rt_k3(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_rt_k5(const FusedArgs&, int, int, int, int, size_t, int, void*);
+int launch_fused_rt_k7(const FusedArgs&, int, int, int, int, size_t, int, void*);
+bool launch_fused_static_p64(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
+bool launch_fused_static_p32(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
+bool launch_fused_static_p128a(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
+bool launch_fused_static_p128b(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
+bool launch_fused_static_small(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
 
 namespace {
 
@@ -21,9 +26,17 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
     extern __shared__ __align__(16) float tot[];
     const int c = blockIdx.x, tid = threadIdx.x, nthr = blockDim.x;
     const int KK = f.k * f.k;
+    // records of channel c: workgroups whose plane range meets [c*B, (c+1)*B);
+    // segment 0 if the range starts in channel c, else segment 1.  Summed in a
+    // fixed order (deterministic).
+    const int w_lo = (int)(((long)c * f.B) / f.ppw);
+    const int w_hi = (int)(((long)(c + 1) * f.B - 1) / f.ppw);
     for (int e = tid; e < f.P; e += nthr) {
         float v = 0.f;
-        for (int ch = 0; ch < f.nchunk; ++ch) v += f.partials[((size_t)ch * f.C + c) * f.P + e];
+        for (int w = w_lo; w <= w_hi; ++w) {
+            const int seg = ((long)w * f.ppw) / f.B == c ? 0 : 1;
+            v += f.partials[((size_t)w * 2 + seg) * f.P + e];
+        }
         tot[e] = v;
     }
     __syncthreads();
@@ -60,11 +73,21 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
 
 int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nthr, size_t lds_bytes,
                  int grid, void* stream) {
+    if (k == 5) {
+        // fixed-geometry kernels for the plane classes compiled in; else runtime geometry
+        int err = 0;
+        if (launch_fused_static_p64(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
+            launch_fused_static_p32(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
+            launch_fused_static_p128a(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
+            launch_fused_static_p128b(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
+            launch_fused_static_small(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err))
+            return err;
+    }
     switch (k) {
-        case 1: return launch_fused_k1(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
-        case 3: return launch_fused_k3(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
-        case 5: return launch_fused_k5(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
-        case 7: return launch_fused_k7(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 1: return launch_fused_rt_k1(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 3: return launch_fused_rt_k3(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 5: return launch_fused_rt_k5(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
+        case 7: return launch_fused_rt_k7(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream);
         default: return (int)hipErrorInvalidValue;
     }
 }

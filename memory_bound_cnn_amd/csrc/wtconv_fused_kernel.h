@@ -7,8 +7,10 @@
 //   (1) the Haar analysis butterfly is recomputed on chip (LDS / registers)
 //       instead of storing subbands in HBM;
 //   (2) the multi-level synthesis is one pass whose signs are indexed by the
-//       output-coordinate bits (evaluated deepest level first, one LDS pass per
-//       level, the last one fused with the output store);
+//       output-coordinate bits: each lane sums, for its own 4x4 output block,
+//       one subband quadruple per level (with signs from the bits of the
+//       block's coordinates) and one 2x2 butterfly per level-1 position, fused
+//       with the output store;
 //   (3) the per-channel scales -- and the 2^-i Haar normalisations of analysis
 //       and synthesis -- are folded into the convolution weights,
 //       W'_i = 4^-i * s_i * W_i and W'_0 = s0 * W0, so every butterfly is a raw
@@ -16,7 +18,8 @@
 // HBM traffic is one read of the convolved tensor, one write of the result
 // and, in the backward pass, one read of x.
 //
-// Work decomposition (one workgroup = one channel, a chunk of the batch):
+// Work decomposition (one workgroup = a contiguous range of planes in
+// channel-major order, at most two channel segments):
 //   * each plane is staged in LDS with a zero halo of k/2 and zero-extended to
 //     Hq x Wq (multiples of max(8, 2^Lm)); zero extension is exactly the
 //     "pad to even before each analysis, crop after each synthesis" rule;
@@ -24,9 +27,14 @@
 //     4x4 sub-block; at levels 1 and 2 lane t convolves subband t over the
 //     whole quad block (4x4 resp. 2x2 positions), so one lane needs one set
 //     of k*k weights and one set of correlation accumulators per level;
-//   * levels >= 3 (grids of at most one position per quad) are flat loops;
-//     their weight-gradient correlations are output-stationary (one thread
-//     per subband x tap x position subset) so they need one register each.
+//   * the analysis of levels 1..3 happens in registers while the base conv
+//     runs (a lane's 4x4 block is one level-2 position, a quad's 8x8 block one
+//     level-3 position); deeper levels (large planes only) are flat loops;
+//   * levels >= 3 (at most one position per quad) are convolved in flat
+//     loops; their weight-gradient correlations are output-stationary (one
+//     thread per subband x tap x position subset), one register each;
+//   * the next planes are prefetched into registers while the current one is
+//     computed.
 // The backward pass is the same pipeline applied to g with 180-degree-rotated
 // weights (the adjoint: the orthonormal Haar matrix is symmetric, so analysis
 // and synthesis are each other's transpose), plus the correlations
@@ -114,29 +122,38 @@ __device__ __forceinline__ void lds_row(const float* p, float (&row)[WW]) {
     }
 }
 
-// Zero every element of a rows x S array outside the rectangle [r0,r1) x [c0,c1).
-__device__ void zero_ring(float* base, int rows, int S, int r0, int r1, int c0, int c1, int tid,
+// Zero every element of a rows x S array outside the interior [r0, r0+h) x
+// [c0, c0+w) (c0 + w <= S).  The ring is a prefix, a suffix and one gap of
+// S - w elements between consecutive interior rows: no divisions needed.
+__device__ void zero_ring(float* base, int rows, int S, int r0, int h, int c0, int w, int tid,
                           int nthr) {
-    const int top = r0 * S;
-    const int bot = (rows - r1) * S;
-    const int side = c0 + (S - c1);
-    const int mid = (r1 - r0) * side;
-    const int n = top + bot + mid;
-    for (int e = tid; e < n; e += nthr) {
-        int idx;
-        if (e < top) {
-            idx = e;
-        } else if (e < top + bot) {
-            idx = r1 * S + (e - top);
-        } else {
-            const int m = e - top - bot;
-            const int row = r0 + m / side;
-            const int col = m % side;
-            idx = row * S + (col < c0 ? col : c1 + (col - c0));
-        }
-        base[idx] = 0.f;
+    const int pre = r0 * S + c0;
+    const int suf0 = (r0 + h - 1) * S + c0 + w;
+    const int suf = rows * S - suf0;
+    for (int e = tid; e < pre; e += nthr) base[e] = 0.f;
+    for (int e = tid; e < suf; e += nthr) base[suf0 + e] = 0.f;
+    const int gap = S - w;
+    for (int y = tid; y < h - 1; y += nthr) {
+        float* g = base + (r0 + y) * S + c0 + w;
+        for (int j = 0; j < gap; ++j) g[j] = 0.f;
     }
 }
+
+// Integer division of 0 <= e < 2^16 by a loop-invariant 1 <= d <= 4096 with a
+// biased float reciprocal (exact in that range: checked exhaustively on the
+// host, including a reciprocal one ulp off).  Three full-rate VALU ops instead
+// of the ~15-op integer division sequence.
+struct FastDiv {
+    int d;
+    float r;
+};
+__device__ __forceinline__ FastDiv make_div(int d) {
+    FastDiv f;
+    f.d = d;
+    f.r = (1.0f / (float)d) * 1.0000076f;  // 1 + 2^-17
+    return f;
+}
+__device__ __forceinline__ int fdiv(int e, const FastDiv& f) { return (int)((float)e * f.r); }
 
 // ---------------------------------------------------------------------------
 // Register-blocked stencil: OH x OW outputs from an (OH+K-1) x (OW+K-1) LDS
@@ -229,61 +246,196 @@ __device__ __forceinline__ float wave_sum(float v, int width_mask_from) {
 }
 
 // ---------------------------------------------------------------------------
+// Plane geometry.  RtGeom reads it from the kernel arguments (any plane size);
+// CtGeom fixes it at compile time, so LDS strides and offsets become
+// immediates and the per-level loops unroll.  Both describe the same layout
+// (make_layout), so one kernel body serves both.
+// ---------------------------------------------------------------------------
+struct RtGeom {
+    const FusedArgs& a;
+    __device__ RtGeom(const FusedArgs& args) : a(args) {}
+    __device__ int Lm() const { return a.Lm; }
+    __device__ int early() const { return a.lay.early_lv; }
+    __device__ int Hq() const { return a.Hq; }
+    __device__ int Wq() const { return a.Wq; }
+    __device__ int NP() const { return a.NP; }
+    __device__ int qpp() const { return a.qpp; }
+    __device__ int nqx() const { return a.nqx; }
+    __device__ int nthr() const { return blockDim.x; }
+    __device__ bool ovl() const { return a.lay.overlap != 0; }
+    __device__ int slot() const { return a.lay.slot; }
+    __device__ int a0_off() const { return a.lay.a0_off; }
+    __device__ int a0_S() const { return a.lay.a0_S; }
+    __device__ int a0_rows() const { return a.lay.a0_rows; }
+    __device__ int b_off(int i) const { return a.lay.b_off[i]; }
+    __device__ int b_S(int i) const { return a.lay.b_S[i]; }
+    __device__ int b_bs(int i) const { return a.lay.b_bs[i]; }
+    __device__ int b_rows(int i) const { return a.lay.b_rows[i]; }
+    __device__ int yd_off(int i) const { return a.lay.yd_off[i]; }
+    __device__ int xb_off(int i) const { return a.lay.xb_off[i]; }
+    __device__ int tail_off() const { return a.lay.tail_off; }
+    __device__ int wts_off() const { return a.wts_off; }
+    __device__ int red_off() const { return a.red_off; }
+    __device__ int dsub() const { return a.dsub; }
+    __device__ int P() const { return a.P; }
+};
+
+template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL>
+struct CtGeom {
+    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL);
+    const FusedArgs& a;
+    __device__ CtGeom(const FusedArgs& args) : a(args) {}
+    __device__ static constexpr int Lm() { return LM; }
+    __device__ static constexpr int early() { return lay.early_lv; }
+    __device__ static constexpr int Hq() { return HQ; }
+    __device__ static constexpr int Wq() { return WQ; }
+    __device__ static constexpr int NP() { return NPV; }
+    __device__ static constexpr int qpp() { return (HQ / 8) * (WQ / 8); }
+    __device__ static constexpr int nqx() { return WQ / 8; }
+    __device__ static constexpr int nthr() { return NTHR; }
+    __device__ static constexpr bool ovl() { return lay.overlap != 0; }
+    __device__ static constexpr int slot() { return lay.slot; }
+    __device__ static constexpr int a0_off() { return lay.a0_off; }
+    __device__ static constexpr int a0_S() { return lay.a0_S; }
+    __device__ static constexpr int a0_rows() { return lay.a0_rows; }
+    __device__ static constexpr int b_off(int i) { return lay.b_off[i]; }
+    __device__ static constexpr int b_S(int i) { return lay.b_S[i]; }
+    __device__ static constexpr int b_bs(int i) { return lay.b_bs[i]; }
+    __device__ static constexpr int b_rows(int i) { return lay.b_rows[i]; }
+    __device__ static constexpr int yd_off(int i) { return lay.yd_off[i]; }
+    __device__ static constexpr int xb_off(int i) { return lay.xb_off[i]; }
+    __device__ static constexpr int tail_off() { return lay.tail_off; }
+    __device__ static constexpr int wts_off() { return NPV * lay.slot; }
+    __device__ static constexpr int red_off() { return 0; }
+    __device__ static constexpr int dsub() { return NTHR / (4 * K * K) > 0 ? NTHR / (4 * K * K) : 1; }
+    __device__ static constexpr int P() { return partial_len(K, LM); }
+};
+
+// Workgroup barrier for LDS communication only.  __syncthreads() also fences
+// device memory, i.e. it waits for every outstanding global load and store of
+// the wave -- which would drain the next planes' prefetch and the previous
+// plane's stores at every phase boundary.  All inter-wave communication in
+// these kernels goes through LDS, so waiting for the LDS counter suffices; the
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt untouched
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // The fused kernel
 // ---------------------------------------------------------------------------
-template <int K, typename ST, bool BWD, int BPQ, bool VEC>
-__global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
+// Sign of subband u at the position with low bits (py, px): (-1)^(u_y py + u_x px).
+__device__ __forceinline__ float band_sign(int u, int py, int px) {
+    return (((u >> 1) & py) ^ (u & px & 1)) ? -1.f : 1.f;
+}
+
+// Raw +-1 butterfly of a 2x2 block a=(0,0), b=(0,1), c=(1,0), d=(1,1):
+// r[u] = sum over the block of (-1)^(u_y py + u_x px) * pixel.
+__device__ __forceinline__ void haar4(float a, float b, float c, float d, float (&r)[4]) {
+    const float s01 = a + b, d01 = a - b, s23 = c + d, d23 = c - d;
+    r[0] = s01 + s23;
+    r[1] = d01 + d23;
+    r[2] = s01 - s23;
+    r[3] = d01 - d23;
+}
+
+template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD || BPQ > 1) ? 2 : 4))) wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
+    constexpr int PFF = 16;                     // prefetch capacity, floats per thread
+    constexpr int PFU = VEC ? PFF / 4 : PFF;    // prefetch units (4-pixel groups or pixels)
+    constexpr int UW = VEC ? 4 : 1;
     extern __shared__ __align__(16) float lds[];
 
-    const int tid = threadIdx.x, nthr = blockDim.x, nquads = nthr >> 2;
-    const int c = blockIdx.x % a.C, chunk = blockIdx.x / a.C;
-    const int b_begin = chunk * a.bpc;
-    const int b_end = min(a.B, b_begin + a.bpc);
-    const int t = tid & 3, Q = tid >> 2;
-    const int sy = t >> 1, sx = t & 1;
-    const float sgx = (t & 1) ? -1.f : 1.f;   // sign of the W-direction high-pass for band t
-    const float sgy = (t & 2) ? -1.f : 1.f;   // sign of the H-direction high-pass for band t
-    const int Lm = a.Lm;
+    const G g(a);
+    const int tid0 = threadIdx.x;
+    const int nthr = g.nthr(), nquads = nthr >> 2;
+    // This workgroup's planes: [q0, q1) in channel-major order (q = c*B + b),
+    // at most two channel segments.
+    const long qtot = (long)a.C * a.B;
+    const long q0 = (long)blockIdx.x * a.ppw;
+    const long q1 = min(q0 + (long)a.ppw, qtot);
+    const int c_first = (int)(q0 / a.B);
+    const int Lm = g.Lm();
+    const bool tail = a.L > Lm;
     const size_t plane_sz = (size_t)a.H * a.W;
+    const FastDiv dqpp = make_div(g.qpp()), dnqx = make_div(g.nqx());
 
-    int slot, qpb[BPQ];
-    if constexpr (BPQ == 1) {
-        slot = Q / a.qpp;
-        qpb[0] = Q - slot * a.qpp;
-    } else {
-        slot = 0;
-#pragma unroll
-        for (int s = 0; s < BPQ; ++s) qpb[s] = Q + s * nquads;
-    }
+    // Per-thread roles.  Recomputed at the top of every plane iteration from an
+    // opaque copy of the thread index, so that the compiler does not hoist every
+    // per-thread address out of the plane loop and keep them all live.
+    int tid, t, sy, sx, slot, qpb[BPQ], qyv[BPQ], qxv[BPQ];
+    float sgx, sgy;   // signs of the W- and H-direction high-pass of band t
     bool qok[BPQ];
+    auto roles = [&](int tid_in) {
+        tid = tid_in;
+        t = tid & 3;
+        const int Q = tid >> 2;
+        sy = t >> 1;
+        sx = t & 1;
+        sgx = (t & 1) ? -1.f : 1.f;
+        sgy = (t & 2) ? -1.f : 1.f;
+        if constexpr (BPQ == 1) {
+            slot = fdiv(Q, dqpp);
+            qpb[0] = Q - slot * g.qpp();
+        } else {
+            slot = 0;
 #pragma unroll
-    for (int s = 0; s < BPQ; ++s) qok[s] = (slot < a.NP) && (qpb[s] < a.qpp);
+            for (int s = 0; s < BPQ; ++s) qpb[s] = Q + s * nquads;
+        }
+#pragma unroll
+        for (int s = 0; s < BPQ; ++s) {
+            qok[s] = (slot < g.NP()) && (qpb[s] < g.qpp());
+            qyv[s] = fdiv(qpb[s], dnqx);
+            qxv[s] = qpb[s] - qyv[s] * g.nqx();
+        }
+    };
+    roles(tid0);
 
-    // ---- fold scales (and Haar normalisations) into the level weights ----
-    // The base weights stay unfolded in scalar registers; s0 is applied once
-    // per output pixel, fused with the synthesis add: out = s0 * (W0 * x) + Z.
-    float* wts = lds + a.wts_off;
-    const int wlev = 0;                        // level i (1-based) band u at wlev + ((i-1)*4+u)*KK
+    for (int seg = 0; seg < 2; ++seg) {
+    const int c = c_first + seg;
+    const long qs = max(q0, (long)c * a.B), qe = min(q1, (long)(c + 1) * a.B);
+    if (qs >= qe) break;
+    const int b_begin = (int)(qs - (long)c * a.B);
+    const int b_end = (int)(qe - (long)c * a.B);
+    lds_barrier();  // the previous segment is done with the weights and the slots
+    // ---- zero the halo rings: per segment (the backward reduction reuses the
+    // slots), and per plane where regions overlap ----
+    for (int s2 = 0; s2 < g.NP(); ++s2) {
+        float* S = lds + s2 * g.slot();
+        zero_ring(S + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
+        for (int i = 1; i <= Lm; ++i)
+            for (int u = 0; u < 4; ++u)
+                zero_ring(S + g.b_off(i) + u * g.b_bs(i), g.b_rows(i), g.b_S(i), R, g.Hq() >> i, R,
+                          g.Wq() >> i, tid, nthr);
+    }
+    // ---- fold scales and Haar normalisations into the level weights ----
+    // W'_i = 4^-i s_i W_i (LDS, per workgroup).  The base weights stay unfolded;
+    // s0 is applied once per output pixel, fused with the synthesis add.
+    // Every parameter is read from device memory here, once per workgroup: no
+    // vector-memory load may sit behind the next planes' prefetch in the plane
+    // loop (vector-memory completions are counted in order).
+    float* wts = lds + g.wts_off();
+    float* wbase = wts + 4 * a.L * KK;          // unfolded base weights W0[c]
     for (int e = tid; e < 4 * a.L * KK; e += nthr) {
         const int i = e / (4 * KK), rem = e - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
         const float sc = ldexpf(a.sl[((size_t)i * a.C + c) * 4 + u], -2 * (i + 1));
-        wts[wlev + e] = sc * a.wl[(((size_t)i * a.C + c) * 4 + u) * KK + tap];
+        wts[e] = sc * a.wl[(((size_t)i * a.C + c) * 4 + u) * KK + tap];
+    }
+    for (int e = tid; e < KK; e += nthr) wbase[e] = a.w0[(size_t)c * KK + e];
+    if (tid == 0) {
+        wbase[KK] = BWD ? 0.f : a.b0[c];
+        wbase[KK + 1] = a.s0[c];
     }
 
-    // ---- zero the halo rings that nothing else writes ----
-    for (int s2 = 0; s2 < a.NP; ++s2) {
-        float* S = lds + s2 * a.slot_stride;
-        zero_ring(S + a.a0_off, a.a0_rows, a.a0_S, R, R + a.H, R, R + a.W, tid, nthr);
-        if (Lm >= 1)
-            for (int u = 0; u < 4; ++u)
-                zero_ring(S + a.b_off[1] + u * a.b_bs[1], a.b_rows[1], a.b_S[1], R,
-                          R + (a.Hq >> 1), R, R + (a.Wq >> 1), tid, nthr);
-    }
-    __syncthreads();
+    lds_barrier();
+    // tail levels (1x1 grids): kappa = sum of their folded centre taps
     float kappa = 0.f;
     for (int i = Lm; i < a.L; ++i)
-        for (int u = 0; u < 4; ++u) kappa += wts[wlev + (i * 4 + u) * KK + (KK >> 1)];
+        for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KK + (KK >> 1)];
 
     // ---- persistent backward accumulators ----
     float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm];
@@ -292,79 +444,121 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
     for (int i = 0; i < kMaxLm; ++i) cdeep[i] = 0.f;
     float sumg = 0.f, tailc = 0.f;
-    // deep-level correlation role: subband du, tap (dty, dtx), position subset dsb
+    // deep-level correlation role: subband du, tap dtap, position subset dsb
     const int drole = tid;
-    const bool dactive = BWD && drole < 4 * KK * a.dsub;
+    const bool dactive = BWD && drole < 4 * KK * g.dsub();
     const int du = drole & 3, dtap = (drole >> 2) % KK, dsb = (drole >> 2) / KK;
     const int ddy = dtap / K - R, ddx = dtap % K - R;
 
     const ST* srcp = reinterpret_cast<const ST*>(a.src);
     const ST* auxp = reinterpret_cast<const ST*>(a.aux);
     ST* dstp = reinterpret_cast<ST*>(a.dst);
-    constexpr bool vec = VEC;
 
-    for (int bb = b_begin; bb < b_end; bb += a.NP) {
-        const int b = bb + slot;
-        const bool pok = (slot < a.NP) && (b < b_end);
-        float* S = lds + (slot < a.NP ? slot : 0) * a.slot_stride;
-        const size_t poff = ((size_t)b * a.C + c) * plane_sz;
-
-        __syncthreads();  // the previous plane is fully consumed
-
-        // ---------------- phase 1: stage the planes in LDS ----------------
-        {
-            const int per = vec ? a.H * (a.W >> 2) : a.H * a.W;
-            const int wv = vec ? (a.W >> 2) : a.W;
-            for (int e = tid; e < a.NP * per; e += nthr) {
-                const int s2 = e / per, m = e - s2 * per;
-                const int b2 = bb + s2;
-                if (b2 >= b_end) continue;
-                const int y = m / wv, xq = m - y * wv;
-                const ST* pl = srcp + ((size_t)b2 * a.C + c) * plane_sz;
-                float* dstl = lds + s2 * a.slot_stride + a.a0_off + (y + R) * a.a0_S + R;
-                if constexpr (VEC) {
-                    float v[4];
-                    load4(pl + (size_t)y * a.W + 4 * xq, v);
+    // ---- plane staging: units of UW pixels, unit e -> (slot, row, column) ----
+    const int wv = VEC ? (a.W >> 2) : a.W;
+    const int per = a.H * wv;
+    const FastDiv dper = make_div(per), dwv = make_div(wv);
+    const bool pf_on = a.pf_on != 0;
+    float pf[PFU][UW];
+    // issue the global loads of the NP planes starting at batch index bbn
+    auto pf_issue = [&](int bbn) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dstl[4 * xq + i] = v[i];
-                } else {
-                    dstl[xq] = to_f32(pl[(size_t)y * a.W + xq]);
+        for (int k = 0; k < PFU; ++k) {
+            const int e = tid + k * nthr;
+            if (e < g.NP() * per) {
+                const int s2 = fdiv(e, dper), m = e - s2 * per;
+                const int y = fdiv(m, dwv), xq = m - y * wv;
+                if (bbn + s2 < b_end) {
+                    const ST* pl = srcp + ((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)y * a.W + xq * UW;
+                    if constexpr (VEC) {
+                        load4(pl, pf[k]);
+                    } else {
+                        pf[k][0] = to_f32(pl[0]);
+                    }
                 }
             }
-            if (a.overlap)
-                for (int s2 = 0; s2 < a.NP; ++s2)
-                    zero_ring(lds + s2 * a.slot_stride + a.a0_off, a.a0_rows, a.a0_S, R, R + a.H,
-                              R, R + a.W, tid, nthr);
         }
-        __syncthreads();
+    };
+    auto pf_commit = [&](int bbn) {
+#pragma unroll
+        for (int k = 0; k < PFU; ++k) {
+            const int e = tid + k * nthr;
+            if (e < g.NP() * per) {
+                const int s2 = fdiv(e, dper), m = e - s2 * per;
+                const int y = fdiv(m, dwv), xq = m - y * wv;
+                if (bbn + s2 < b_end) {
+                    float* d = lds + s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW;
+#pragma unroll
+                    for (int i = 0; i < UW; ++i) d[i] = pf[k][i];
+                }
+            }
+        }
+    };
+    if (pf_on) pf_issue(b_begin);
 
-        // ---------------- phase 2: base conv, level-1 analysis ----------------
+    for (int bb = b_begin; bb < b_end; bb += g.NP()) {
+        roles(opaque(tid0));
+        const int b = bb + slot;
+        const bool pok = (slot < g.NP()) && (b < b_end);
+        float* S = lds + (slot < g.NP() ? slot : 0) * g.slot();
+        const size_t poff = ((size_t)b * a.C + c) * plane_sz;
+
+        lds_barrier();  // the previous plane is fully consumed
+
+        // ---------------- phase 1: stage the planes in LDS ----------------
+        if (pf_on) {
+            pf_commit(bb);
+        } else {
+            for (int e = tid; e < g.NP() * per; e += nthr) {
+                const int s2 = fdiv(e, dper), m = e - s2 * per;
+                if (bb + s2 >= b_end) continue;
+                const int y = fdiv(m, dwv), xq = m - y * wv;
+                const ST* pl = srcp + ((size_t)(bb + s2) * a.C + c) * plane_sz + (size_t)y * a.W + xq * UW;
+                float* d = lds + s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW;
+                if constexpr (VEC) {
+                    float v[4];
+                    load4(pl, v);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) d[i] = v[i];
+                } else {
+                    d[0] = to_f32(pl[0]);
+                }
+            }
+        }
+        if (g.ovl())
+            for (int s2 = 0; s2 < g.NP(); ++s2)
+                zero_ring(lds + s2 * g.slot() + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
+        lds_barrier();
+        // the next planes' loads fly while this plane is computed
+        if (pf_on && bb + g.NP() < b_end) pf_issue(bb + g.NP());
+
+        // ---------------- phase 2: base conv; analysis of levels 1..3 ----------------
         float acc[BPQ][4][4];
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
             if (!(pok && qok[s])) continue;
-            const int qy = qpb[s] / a.nqx, qx = qpb[s] - (qpb[s] / a.nqx) * a.nqx;
+            const int qy = qyv[s], qx = qxv[s];
             const int py0 = 8 * qy + 4 * sy, px0 = 8 * qx + 4 * sx;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[s][i][j] = 0.f;
             float w[KK];
-            load_w<K, BWD>(a.w0 + (size_t)c * KK, w);
+            load_w<K, BWD>(wbase, w);
             float xo[4][4];
             if constexpr (BWD) {
                 const ST* xp = auxp + poff + opaque(py0 * a.W + px0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ld_row4<VEC>(xp + i * a.W, py0 + i < a.H, px0, a.W, xo[i]);
             }
-            const float* win = S + a.a0_off + py0 * a.a0_S + px0;
-            stencil<K, 4, 4, 4, BWD>(win, a.a0_S, w, acc[s], xo, corr0);
-            // the block itself (window centre) -> level-1 raw bands, sum of g
+            const float* win = S + g.a0_off() + py0 * g.a0_S() + px0;
+            stencil<K, 4, 4, 4, BWD>(win, g.a0_S(), w, acc[s], xo, corr0);
+            // the block itself (window centre): raw analysis cascade in registers
             float ctr[4][4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float rowv[4];
-                lds_row<4, (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1)>(win + (i + R) * a.a0_S + R, rowv);
+                lds_row<4, (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1)>(win + (i + R) * g.a0_S() + R, rowv);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) ctr[i][j] = rowv[j];
             }
@@ -375,55 +569,71 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
                     for (int j = 0; j < 4; ++j) sumg += ctr[i][j];
             }
             if (Lm >= 1) {
-                float* B1 = S + a.b_off[1];
-                const int S1 = a.b_S[1], bs1 = a.b_bs[1];
+                float ll1[2][2];
+                float* B1 = S + g.b_off(1);
+                const int S1 = g.b_S(1), bs1 = g.b_bs(1);
 #pragma unroll
                 for (int jy = 0; jy < 2; ++jy)
 #pragma unroll
                     for (int jx = 0; jx < 2; ++jx) {
-                        const float p0 = ctr[2 * jy][2 * jx], p1 = ctr[2 * jy][2 * jx + 1];
-                        const float p2 = ctr[2 * jy + 1][2 * jx], p3 = ctr[2 * jy + 1][2 * jx + 1];
-                        const float s01 = p0 + p1, d01 = p0 - p1, s23 = p2 + p3, d23 = p2 - p3;
+                        float r[4];
+                        haar4(ctr[2 * jy][2 * jx], ctr[2 * jy][2 * jx + 1], ctr[2 * jy + 1][2 * jx],
+                              ctr[2 * jy + 1][2 * jx + 1], r);
                         const int off = (py0 / 2 + jy + R) * S1 + (px0 / 2 + jx + R);
-                        B1[off] = s01 + s23;
-                        B1[bs1 + off] = d01 + d23;
-                        B1[2 * bs1 + off] = s01 - s23;
-                        B1[3 * bs1 + off] = d01 - d23;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) B1[u * bs1 + off] = r[u];
+                        ll1[jy][jx] = r[0];
                     }
-            } else if (a.L > 0 && py0 == 0 && px0 == 0) {
-                // every level is a 1x1 grid: tail term enters at pixel (0, 0)
-                S[a.tail_off] = ctr[0][0] * kappa;
+                if (g.early() >= 2) {
+                    // this lane's 4x4 block is one level-2 position
+                    float r2[4];
+                    haar4(ll1[0][0], ll1[0][1], ll1[1][0], ll1[1][1], r2);
+                    float* B2 = S + g.b_off(2);
+                    const int off2 = (2 * qy + sy + R) * g.b_S(2) + 2 * qx + sx + R;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) B2[u * g.b_bs(2) + off2] = r2[u];
+                    if (g.early() >= 3) {
+                        // the quad's 8x8 block is one level-3 position: lane t
+                        // gathers the quad's four level-2 LL values, writes band t
+                        const int qb = (tid & 63) & ~3;
+                        const float l0 = __shfl(r2[0], qb + 0, 64), l1 = __shfl(r2[0], qb + 1, 64);
+                        const float l2 = __shfl(r2[0], qb + 2, 64), l3 = __shfl(r2[0], qb + 3, 64);
+                        const float b3 = fmaf(sgy, fmaf(sgx, l3, l2), fmaf(sgx, l1, l0));
+                        S[g.b_off(3) + t * g.b_bs(3) + (qy + R) * g.b_S(3) + qx + R] = b3;
+                    }
+                }
+            } else if (tail && py0 == 0 && px0 == 0) {
+                // every level is a 1x1 grid: the tail term enters at pixel (0, 0)
+                S[g.tail_off()] = ctr[0][0] * kappa;
                 if constexpr (BWD) tailc = fmaf(ctr[0][0], xo[0][0], tailc);
             }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---------------- phase 3: analysis of levels 2..Lm ----------------
-        for (int i = 2; i <= Lm; ++i) {
-            const int hi = a.Hq >> i, wi = a.Wq >> i, Si = a.b_S[i], rows = a.b_rows[i];
-            const int per = rows * Si;
-            for (int e = tid; e < a.NP * per; e += nthr) {
-                const int s2 = e / per, m = e - s2 * per;
+        // ---------------- phase 3: analysis of levels early_lv+1..Lm ----------------
+        for (int i = g.early() + 1; i <= Lm; ++i) {
+            const int hi = g.Hq() >> i, wi = g.Wq() >> i, Si = g.b_S(i), bs = g.b_bs(i);
+            const int pi = hi * wi;
+            const FastDiv dpi = make_div(pi), dwi = make_div(wi);
+            const int Sp = g.b_S(i - 1);
+            for (int e = tid; e < g.NP() * pi; e += nthr) {
+                const int s2 = fdiv(e, dpi), m = e - s2 * pi;
                 if (bb + s2 >= b_end) continue;
-                float* Sl = lds + s2 * a.slot_stride;
-                const int ry = m / Si, rx = m - ry * Si;
-                const int jy = ry - R, jx = rx - R;
-                float v0 = 0.f, v1 = 0.f, v2 = 0.f, v3 = 0.f;
-                if (jy >= 0 && jy < hi && jx >= 0 && jx < wi) {
-                    const float* LL = Sl + a.b_off[i - 1];
-                    const int Sp = a.b_S[i - 1];
-                    const int o = (2 * jy + R) * Sp + 2 * jx + R;
-                    const float p0 = LL[o], p1 = LL[o + 1], p2 = LL[o + Sp], p3 = LL[o + Sp + 1];
-                    const float s01 = p0 + p1, d01 = p0 - p1, s23 = p2 + p3, d23 = p2 - p3;
-                    v0 = s01 + s23; v1 = d01 + d23; v2 = s01 - s23; v3 = d01 - d23;
-                }
-                float* Bi = Sl + a.b_off[i];
-                Bi[m] = v0;
-                Bi[a.b_bs[i] + m] = v1;
-                Bi[2 * a.b_bs[i] + m] = v2;
-                Bi[3 * a.b_bs[i] + m] = v3;
+                float* Sl = lds + s2 * g.slot();
+                const int jy = fdiv(m, dwi), jx = m - jy * wi;
+                const float* LL = Sl + g.b_off(i - 1) + (2 * jy + R) * Sp + 2 * jx + R;
+                float r[4];
+                haar4(LL[0], LL[1], LL[Sp], LL[Sp + 1], r);
+                float* Bi = Sl + g.b_off(i) + (jy + R) * Si + jx + R;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) Bi[u * bs] = r[u];
             }
-            __syncthreads();
+            if (g.ovl())  // this level lives where the level-0 plane was staged
+                for (int s2 = 0; s2 < g.NP(); ++s2)
+                    for (int u = 0; u < 4; ++u)
+                        zero_ring(lds + s2 * g.slot() + g.b_off(i) + u * bs, g.b_rows(i), Si, R, hi,
+                                  R, wi, tid, nthr);
+            lds_barrier();
         }
 
         // ---------------- phase 4a: levels 1 and 2, subband per lane ----------------
@@ -431,10 +641,12 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
             if (!(pok && qok[s]) || Lm < 1) continue;
-            const int qy = qpb[s] / a.nqx, qx = qpb[s] - (qpb[s] / a.nqx) * a.nqx;
-            float rx1[4][4], ll1[4][4];
+            const int qy = qyv[s], qx = qxv[s];
+            float rx1[4][4], rx2[2][2];
+            float ll2[2][2];
             if constexpr (BWD) {
-                // x over the quad's 8x8 block -> band t and LL at level 1
+                // x over the quad's 8x8 block -> band t (and LL) at levels 1, 2, 3
+                float ll1[4][4];
                 const ST* xp = auxp + poff + opaque(8 * qy * a.W + 8 * qx);
 #pragma unroll
                 for (int jy = 0; jy < 4; ++jy) {
@@ -457,9 +669,6 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
                     for (int jx = 0; jx < 4; ++jx) asm volatile("" : "+v"(ll1[jy][jx]), "+v"(rx1[jy][jx]));
                     asm volatile("" ::: "memory");
                 }
-            }
-            float ll2[2][2], rx2[2][2];
-            if constexpr (BWD) {
 #pragma unroll
                 for (int jy = 0; jy < 2; ++jy)
 #pragma unroll
@@ -469,111 +678,113 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
                         ll2[jy][jx] = (p0 + p1) + (p2 + p3);
                         rx2[jy][jx] = fmaf(sgy, fmaf(sgx, p3, p2), fmaf(sgx, p1, p0));
                     }
-            }
-            {
-                float w[KK];
-                load_w<K, BWD>(wts + wlev + t * KK, w);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) y1[s][i][j] = 0.f;
-                const float* win = S + a.b_off[1] + t * a.b_bs[1] + (4 * qy) * a.b_S[1] + 4 * qx;
-                stencil<K, 4, 4, 4, BWD>(win, a.b_S[1], w, y1[s], rx1, corr1);
-            }
-            if (Lm >= 2) {
-                float w[KK];
-                load_w<K, BWD>(wts + wlev + (4 + t) * KK, w);
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) y2[s][i][j] = 0.f;
-                const float* win = S + a.b_off[2] + t * a.b_bs[2] + (2 * qy) * a.b_S[2] + 2 * qx;
-                stencil<K, 2, 2, 2, BWD>(win, a.b_S[2], w, y2[s], rx2, corr2);
-                if constexpr (BWD) {
-                    if (Lm >= 3 && t == 0) {
-                        float* xl2 = S + a.xl2_off;
-                        const int w2 = a.Wq >> 2;
-#pragma unroll
-                        for (int jy = 0; jy < 2; ++jy)
-#pragma unroll
-                            for (int jx = 0; jx < 2; ++jx) xl2[(2 * qy + jy) * w2 + 2 * qx + jx] = ll2[jy][jx];
-                    }
+                if (Lm >= 3) {
+                    const float rx3 = fmaf(sgy, fmaf(sgx, ll2[1][1], ll2[1][0]), fmaf(sgx, ll2[0][1], ll2[0][0]));
+                    const int h3 = g.Hq() >> 3, w3 = g.Wq() >> 3;
+                    S[g.xb_off(3) + t * h3 * w3 + qy * w3 + qx] = rx3;
                 }
-            }
-            // tail term: rho = raw LL of the convolved tensor at level Lm, position (0,0)
-            if (a.L > Lm && qpb[s] == 0 && t == 0) {
-                const float rho = S[a.b_off[Lm] + R * a.b_S[Lm] + R];
-                S[a.tail_off] = rho * kappa;
-                if constexpr (BWD) {
+                if (tail && qpb[s] == 0 && t == 0) {
+                    // tail correlation: raw LL of g and of x at level Lm, position (0, 0)
+                    const float rho = S[g.b_off(Lm) + R * g.b_S(Lm) + R];
                     if (Lm == 1) tailc = fmaf(rho, ll1[0][0], tailc);
                     if (Lm == 2) tailc = fmaf(rho, ll2[0][0], tailc);
                 }
             }
+            {
+                float w[KK];
+                load_w<K, BWD>(wts + t * KK, w);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) y1[s][i][j] = 0.f;
+                const float* win = S + g.b_off(1) + t * g.b_bs(1) + (4 * qy) * g.b_S(1) + 4 * qx;
+                stencil<K, 4, 4, 4, BWD>(win, g.b_S(1), w, y1[s], rx1, corr1);
+            }
+            if (Lm >= 2) {
+                float w[KK];
+                load_w<K, BWD>(wts + (4 + t) * KK, w);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) y2[s][i][j] = 0.f;
+                const float* win = S + g.b_off(2) + t * g.b_bs(2) + (2 * qy) * g.b_S(2) + 2 * qx;
+                stencil<K, 2, 2, 2, BWD>(win, g.b_S(2), w, y2[s], rx2, corr2);
+            }
+            // tail term: rho = raw LL of the convolved tensor at level Lm, position (0,0)
+            if (tail && qpb[s] == 0 && t == 0) S[g.tail_off()] = S[g.b_off(Lm) + R * g.b_S(Lm) + R] * kappa;
         }
 
-        // ---------------- phase 4b: x bands of levels >= 3 (backward) ----------------
+        // ---------------- phase 4b: x bands of levels >= 4 (backward) ----------------
         if constexpr (BWD) {
             if (Lm >= 3) {
-                __syncthreads();
-                for (int i = 3; i <= Lm; ++i) {
-                    const int hi = a.Hq >> i, wi = a.Wq >> i, wp = a.Wq >> (i - 1);
-                    const int per = hi * wi;
-                    for (int e = tid; e < a.NP * per; e += nthr) {
-                        const int s2 = e / per, m = e - s2 * per;
+                lds_barrier();  // band 0 of level 3 (x) written in phase 4a
+                for (int i = 4; i <= Lm; ++i) {
+                    const int hi = g.Hq() >> i, wi = g.Wq() >> i, wp = g.Wq() >> (i - 1);
+                    const int pi = hi * wi;
+                    const FastDiv dpi = make_div(pi), dwi = make_div(wi);
+                    for (int e = tid; e < g.NP() * pi; e += nthr) {
+                        const int s2 = fdiv(e, dpi), m = e - s2 * pi;
                         if (bb + s2 >= b_end) continue;
-                        float* Sl = lds + s2 * a.slot_stride;
-                        const float* LL = (i == 3) ? (Sl + a.xl2_off) : (Sl + a.xb_off[i - 1]);
-                        const int jy = m / wi, jx = m - jy * wi;
+                        float* Sl = lds + s2 * g.slot();
+                        const float* LL = Sl + g.xb_off(i - 1);
+                        const int jy = fdiv(m, dwi), jx = m - jy * wi;
                         const int o = 2 * jy * wp + 2 * jx;
-                        const float p0 = LL[o], p1 = LL[o + 1], p2 = LL[o + wp], p3 = LL[o + wp + 1];
-                        const float s01 = p0 + p1, d01 = p0 - p1, s23 = p2 + p3, d23 = p2 - p3;
-                        float* XB = Sl + a.xb_off[i];
-                        XB[m] = s01 + s23;
-                        XB[per + m] = d01 + d23;
-                        XB[2 * per + m] = s01 - s23;
-                        XB[3 * per + m] = d01 - d23;
+                        float r[4];
+                        haar4(LL[o], LL[o + 1], LL[o + wp], LL[o + wp + 1], r);
+                        float* XB = Sl + g.xb_off(i);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) XB[u * pi + m] = r[u];
                     }
-                    __syncthreads();
+                    lds_barrier();
                 }
-                if (a.L > Lm && pok && qok[0] && qpb[0] == 0 && t == 0) {
-                    const float rho = S[a.b_off[Lm] + R * a.b_S[Lm] + R];
-                    tailc = fmaf(rho, S[a.xb_off[Lm]], tailc);
+                if (tail && pok && qok[0] && qpb[0] == 0 && t == 0) {
+                    const float rho = S[g.b_off(Lm) + R * g.b_S(Lm) + R];
+                    tailc = fmaf(rho, S[g.xb_off(Lm)], tailc);
                 }
             }
         }
 
         // ---------------- phase 4c: levels >= 3, flat ----------------
         for (int i = 3; i <= Lm; ++i) {
-            const int hi = a.Hq >> i, wi = a.Wq >> i, Si = a.b_S[i], bs = a.b_bs[i];
-            const int per = 4 * hi * wi;
-            for (int e = tid; e < a.NP * per; e += nthr) {
-                const int s2 = e / per, m = e - s2 * per;
+            const int hi = g.Hq() >> i, wi = g.Wq() >> i, Si = g.b_S(i), bs = g.b_bs(i);
+            const int pi4 = 4 * hi * wi;
+            const FastDiv dpi = make_div(pi4), dwi = make_div(wi);
+            for (int e = tid; e < g.NP() * pi4; e += nthr) {
+                const int s2 = fdiv(e, dpi), m = e - s2 * pi4;
                 if (bb + s2 >= b_end) continue;
-                float* Sl = lds + s2 * a.slot_stride;
+                float* Sl = lds + s2 * g.slot();
                 const int u = m & 3, j = m >> 2;
-                const int jy = j / wi, jx = j - jy * wi;
+                const int jy = fdiv(j, dwi), jx = j - jy * wi;
                 float w[KK];
-                load_w<K, BWD>(wts + wlev + ((i - 1) * 4 + u) * KK, w);
-                const float* win = Sl + a.b_off[i] + u * bs + jy * Si + jx;
+                load_w<K, BWD>(wts + ((i - 1) * 4 + u) * KK, w);
+                const float* win = Sl + g.b_off(i) + u * bs + jy * Si + jx;
                 float accv = 0.f;
 #pragma unroll
                 for (int ky = 0; ky < K; ++ky)
 #pragma unroll
                     for (int kx = 0; kx < K; ++kx) accv = fmaf(w[ky * K + kx], win[ky * Si + kx], accv);
-                Sl[a.yd_off[i] + u * hi * wi + j] = accv;
+                Sl[g.yd_off(i) + u * hi * wi + j] = accv;
             }
             if constexpr (BWD) {
                 // output-stationary correlation: C_i^du[d] over this role's positions
                 if (dactive) {
                     float cv = 0.f;
-                    for (int s2 = 0; s2 < a.NP; ++s2) {
+                    for (int s2 = 0; s2 < g.NP(); ++s2) {
                         if (bb + s2 >= b_end) break;
-                        const float* Sl = lds + s2 * a.slot_stride;
-                        const float* XB = Sl + a.xb_off[i] + du * hi * wi;
-                        const float* G = Sl + a.b_off[i] + du * bs;
-                        for (int m = dsb; m < hi * wi; m += a.dsub) {
-                            const int my = m / wi, mx = m - my * wi;
-                            cv = fmaf(XB[m], G[(my - ddy + R) * Si + (mx - ddx + R)], cv);
+                        const float* Sl = lds + s2 * g.slot();
+                        const float* XB = Sl + g.xb_off(i) + du * hi * wi;
+                        const float* Gb = Sl + g.b_off(i) + du * bs;
+                        // positions m = dsb, dsb + dsub, ... walked as (row, col) without division
+                        int my = fdiv(dsb, dwi), mx = dsb - my * wi;
+                        const int stepy = fdiv(g.dsub(), dwi), stepx = g.dsub() - stepy * wi;
+                        for (int m = dsb; m < hi * wi; m += g.dsub()) {
+                            cv = fmaf(XB[m], Gb[(my - ddy + R) * Si + (mx - ddx + R)], cv);
+                            mx += stepx;
+                            my += stepy;
+                            if (mx >= wi) {
+                                mx -= wi;
+                                ++my;
+                            }
                         }
                     }
 #pragma unroll
@@ -582,97 +793,91 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---------------- phase 4d: levels 1, 2 results in place ----------------
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
             if (!(pok && qok[s]) || Lm < 1) continue;
-            const int qy = qpb[s] / a.nqx, qx = qpb[s] - (qpb[s] / a.nqx) * a.nqx;
-            float* B1 = S + a.b_off[1] + t * a.b_bs[1];
+            const int qy = qyv[s], qx = qxv[s];
+            float* B1 = S + g.b_off(1) + t * g.b_bs(1);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) B1[(4 * qy + i + R) * a.b_S[1] + 4 * qx + j + R] = y1[s][i][j];
+                for (int j = 0; j < 4; ++j) B1[(4 * qy + i + R) * g.b_S(1) + 4 * qx + j + R] = y1[s][i][j];
             if (Lm >= 2) {
-                float* B2 = S + a.b_off[2] + t * a.b_bs[2];
+                float* B2 = S + g.b_off(2) + t * g.b_bs(2);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) B2[(2 * qy + i + R) * a.b_S[2] + 2 * qx + j + R] = y2[s][i][j];
+                    for (int j = 0; j < 2; ++j) B2[(2 * qy + i + R) * g.b_S(2) + 2 * qx + j + R] = y2[s][i][j];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
-        // ---------------- phase 5: synthesis of levels Lm..2 ----------------
-        for (int i = Lm; i >= 2; --i) {
-            const int hi = a.Hq >> i, wi = a.Wq >> i;
-            const int per = hi * wi, wz = a.Wq >> (i - 1);
-            for (int e = tid; e < a.NP * per; e += nthr) {
-                const int s2 = e / per, j = e - s2 * per;
-                if (bb + s2 >= b_end) continue;
-                float* Sl = lds + s2 * a.slot_stride;
-                const int jy = j / wi, jx = j - jy * wi;
-                float T0, T1, T2, T3;
-                if (i == 2) {
-                    const float* B2 = Sl + a.b_off[2];
-                    const int o = (jy + R) * a.b_S[2] + jx + R, bs = a.b_bs[2];
-                    T0 = B2[o]; T1 = B2[bs + o]; T2 = B2[2 * bs + o]; T3 = B2[3 * bs + o];
-                } else {
-                    const float* Y = Sl + a.yd_off[i];
-                    T0 = Y[j]; T1 = Y[per + j]; T2 = Y[2 * per + j]; T3 = Y[3 * per + j];
-                }
-                if (i < Lm) T0 += Sl[a.z_off[i + 1] + j];
-                if (i == Lm && j == 0 && a.L > Lm) T0 += Sl[a.tail_off];
-                const float s01 = T0 + T1, d01 = T0 - T1, s23 = T2 + T3, d23 = T2 - T3;
-                float* Z = Sl + a.z_off[i] + (2 * jy) * wz + 2 * jx;
-                Z[0] = s01 + s23;
-                Z[1] = d01 + d23;
-                Z[wz] = s01 - s23;
-                Z[wz + 1] = d01 - d23;
-            }
-            __syncthreads();
-        }
-
-        // ---------------- phase 6: level-1 synthesis fused with the store ----------------
+        // ---------------- phase 6: closed-form synthesis fused with the store ----------------
+        // Every level >= 2 contributes to this lane's 4x4 block through a single
+        // position per level (the block is 2^i-aligned for i <= 2 and the quad's
+        // block for i = 3 ...), with signs given by the bits of the block's
+        // level-(i-1) coordinate; level 1 adds one 2x2 butterfly per position.
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
             if (!(pok && qok[s])) continue;
-            const int qy = qpb[s] / a.nqx, qx = qpb[s] - (qpb[s] / a.nqx) * a.nqx;
+            const int qy = qyv[s], qx = qxv[s];
             const int py0 = 8 * qy + 4 * sy, px0 = 8 * qx + 4 * sx;
-            const float bias = BWD ? 0.f : a.b0[c];
+            const float bias = wbase[KK];
             float z[4][4];
             if (Lm >= 1) {
-                const float* B1 = S + a.b_off[1];
-                const int S1 = a.b_S[1], bs1 = a.b_bs[1], w1 = a.Wq >> 1;
+                // levels Lm..3: v = Z_3 at this lane's level-2 position
+                float v = 0.f;
+                for (int i = Lm; i >= 3; --i) {
+                    const int wi = g.Wq() >> i, pi = (g.Hq() >> i) * wi;
+                    const int jy = py0 >> i, jx = px0 >> i;
+                    const int by = (py0 >> (i - 1)) & 1, bx = (px0 >> (i - 1)) & 1;
+                    const float* Y = S + g.yd_off(i) + jy * wi + jx;
+                    float T0 = Y[0] + v;
+                    if (i == Lm && tail && jy == 0 && jx == 0) T0 += S[g.tail_off()];
+                    const float sxb = bx ? -1.f : 1.f, syb = by ? -1.f : 1.f;
+                    v = T0 + sxb * Y[pi] + syb * Y[2 * pi] + (sxb * syb) * Y[3 * pi];
+                }
+                float z2[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+                if (Lm >= 2) {
+                    const float* B2 = S + g.b_off(2) + (py0 / 4 + R) * g.b_S(2) + px0 / 4 + R;
+                    const int bs2 = g.b_bs(2);
+                    float T0 = B2[0] + v;
+                    if (Lm == 2 && tail && py0 == 0 && px0 == 0) T0 += S[g.tail_off()];
+                    float r[4];
+                    haar4(T0, B2[bs2], B2[2 * bs2], B2[3 * bs2], r);
+                    z2[0][0] = r[0]; z2[0][1] = r[1]; z2[1][0] = r[2]; z2[1][1] = r[3];
+                }
+                const float* B1 = S + g.b_off(1);
+                const int S1 = g.b_S(1), bs1 = g.b_bs(1);
 #pragma unroll
                 for (int dy = 0; dy < 2; ++dy)
 #pragma unroll
                     for (int dx = 0; dx < 2; ++dx) {
                         const int jy = py0 / 2 + dy, jx = px0 / 2 + dx;
                         const int o = (jy + R) * S1 + jx + R;
-                        float T0 = B1[o] + bias;
-                        const float T1 = B1[bs1 + o], T2 = B1[2 * bs1 + o], T3 = B1[3 * bs1 + o];
-                        if (Lm >= 2) T0 += S[a.z_off[2] + jy * w1 + jx];
-                        if (Lm == 1 && a.L > 1 && jy == 0 && jx == 0) T0 += S[a.tail_off];
-                        const float s01 = T0 + T1, d01 = T0 - T1, s23 = T2 + T3, d23 = T2 - T3;
-                        z[2 * dy][2 * dx] = s01 + s23;
-                        z[2 * dy][2 * dx + 1] = d01 + d23;
-                        z[2 * dy + 1][2 * dx] = s01 - s23;
-                        z[2 * dy + 1][2 * dx + 1] = d01 - d23;
+                        float T0 = B1[o] + bias + z2[dy][dx];
+                        if (Lm == 1 && tail && jy == 0 && jx == 0) T0 += S[g.tail_off()];
+                        float r[4];
+                        haar4(T0, B1[bs1 + o], B1[2 * bs1 + o], B1[3 * bs1 + o], r);
+                        z[2 * dy][2 * dx] = r[0];
+                        z[2 * dy][2 * dx + 1] = r[1];
+                        z[2 * dy + 1][2 * dx] = r[2];
+                        z[2 * dy + 1][2 * dx + 1] = r[3];
                     }
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) z[i][j] = bias;
-                if (a.L > 0 && py0 == 0 && px0 == 0) z[0][0] += S[a.tail_off];
+                if (tail && py0 == 0 && px0 == 0) z[0][0] += S[g.tail_off()];
             }
-            const float s0c = a.s0[c];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[s][i][j] = fmaf(s0c, acc[s][i][j], z[i][j]);
+                for (int j = 0; j < 4; ++j) acc[s][i][j] = fmaf(wbase[KK + 1], acc[s][i][j], z[i][j]);
             ST* op = dstp + poff + opaque(py0 * a.W + px0);
             if constexpr (VEC) {
 #pragma unroll
@@ -687,11 +892,10 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
             }
         }
     }
-
     if constexpr (BWD) {
         // ---------------- reduction of the correlation accumulators ----------------
-        __syncthreads();
-        float* red = lds + a.red_off;
+        lds_barrier();
+        float* red = lds + g.red_off();
         const int nw = nthr >> 6, wave = tid >> 6, lane = tid & 63;
         // per-wave record: [C_0 (KK)][C_1 u=0..3 (KK each)][C_2 u=0..3][sumg][tail]
         const int WR = KK * 9 + 2;
@@ -716,10 +920,10 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
         }
         float* dred = red + nw * WR;   // deep: [q][role]
         if (dactive)
-            for (int q = 0; q + 3 <= Lm; ++q) dred[q * 4 * KK * a.dsub + drole] = cdeep[q];
-        __syncthreads();
-        float* rec = a.partials + ((size_t)chunk * a.C + c) * a.P;
-        for (int e = tid; e < a.P; e += nthr) {
+            for (int q = 0; q + 3 <= Lm; ++q) dred[q * 4 * KK * g.dsub() + drole] = cdeep[q];
+        lds_barrier();
+        float* rec = a.partials + ((size_t)blockIdx.x * 2 + seg) * g.P();
+        for (int e = tid; e < g.P(); e += nthr) {
             float v = 0.f;
             if (e < KK) {
                 for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + e];
@@ -731,10 +935,10 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
                     for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + base + rem];
                 } else {
                     const int u = rem / KK, tap = rem - u * KK;
-                    for (int sb = 0; sb < a.dsub; ++sb)
-                        v += dred[(lvl - 3) * 4 * KK * a.dsub + (sb * KK + tap) * 4 + u];
+                    for (int sb = 0; sb < g.dsub(); ++sb)
+                        v += dred[(lvl - 3) * 4 * KK * g.dsub() + (sb * KK + tap) * 4 + u];
                 }
-            } else if (e == a.P - 2) {
+            } else if (e == g.P() - 2) {
                 for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + 9 * KK];
             } else {
                 for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + 9 * KK + 1];
@@ -742,11 +946,12 @@ __global__ void __launch_bounds__(512) wtc_fused_kernel(const FusedArgs a) {
             rec[e] = v;
         }
     }
+    }  // channel segments
 }
 
-template <int K, typename ST, bool BWD, int BPQ, bool VEC>
+template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 hipError_t launch_t(const FusedArgs& a, int nthr, size_t lds, int grid, hipStream_t st) {
-    auto kern = wtc_fused_kernel<K, ST, BWD, BPQ, VEC>;
+    auto kern = wtc_fused_kernel<K, ST, BWD, BPQ, VEC, G>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -756,27 +961,45 @@ hipError_t launch_t(const FusedArgs& a, int nthr, size_t lds, int grid, hipStrea
     return hipGetLastError();
 }
 
-template <int K, typename ST, bool BWD>
-hipError_t launch_b(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st) {
-    if (a.vec) {
-        if (bpq == 1) return launch_t<K, ST, BWD, 1, true>(a, nthr, lds, grid, st);
-        return launch_t<K, ST, BWD, 2, true>(a, nthr, lds, grid, st);
-    }
-    if (bpq == 1) return launch_t<K, ST, BWD, 1, false>(a, nthr, lds, grid, st);
-    return launch_t<K, ST, BWD, 2, false>(a, nthr, lds, grid, st);
-}
-
-template <int K, typename ST>
-hipError_t launch_d(const FusedArgs& a, int bwd, int bpq, int nthr, size_t lds, int grid, hipStream_t st) {
-    return bwd ? launch_b<K, ST, true>(a, bpq, nthr, lds, grid, st)
-               : launch_b<K, ST, false>(a, bpq, nthr, lds, grid, st);
-}
-
+// Runtime-geometry kernel for any plane the LDS pipeline holds.
 template <int K>
-hipError_t launch_k(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
-                    hipStream_t st) {
-    return dtype == WTC_BF16 ? launch_d<K, bf16_t>(a, bwd, bpq, nthr, lds, grid, st)
-                             : launch_d<K, float>(a, bwd, bpq, nthr, lds, grid, st);
+hipError_t launch_rt(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
+                     hipStream_t st) {
+#define WTC_RT(ST_, BWD_)                                                                    \
+    do {                                                                                     \
+        if (a.vec) {                                                                         \
+            if (bpq == 1) return launch_t<K, ST_, BWD_, 1, true, RtGeom>(a, nthr, lds, grid, st); \
+            return launch_t<K, ST_, BWD_, 2, true, RtGeom>(a, nthr, lds, grid, st);          \
+        }                                                                                    \
+        if (bpq == 1) return launch_t<K, ST_, BWD_, 1, false, RtGeom>(a, nthr, lds, grid, st); \
+        return launch_t<K, ST_, BWD_, 2, false, RtGeom>(a, nthr, lds, grid, st);             \
+    } while (0)
+    if (dtype == WTC_BF16) {
+        if (bwd) WTC_RT(bf16_t, true);
+        WTC_RT(bf16_t, false);
+    }
+    if (bwd) WTC_RT(float, true);
+    WTC_RT(float, false);
+#undef WTC_RT
+}
+
+}  // namespace fused_detail
+}  // namespace wtc
+
+namespace wtc {
+namespace fused_detail {
+
+// Launch the fixed-geometry instantiation if the plan matches it exactly.
+template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
+          int NTHR>
+bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
+                hipError_t* err) {
+    if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
+        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC)
+        return false;
+    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD>>(a, nthr, lds,
+                                                                                    grid, st);
+    return true;
 }
 
 }  // namespace fused_detail
