@@ -96,8 +96,12 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g,
                     float* dwl, float* dsl,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Level-by-level baseline: one kernel per step, intermediates in device
- * memory.  Same arguments, results and error behaviour as above. */
+/* Level-by-level baseline: one kernel per step, every intermediate (bands,
+ * convolved bands, partial syntheses) a float32 tensor in the workspace.
+ * Same arguments and results as above.  It accepts any plane size but
+ * returns WTC_ESHAPE for k > 7, L > 30, or tensors of 2^31 elements or more
+ * (32-bit indexing).  Its weight-gradient reduction is also deterministic.
+ * The forward workspace is 0 bytes when L == 0. */
 size_t wtconv_forward_unfused_workspace(const wtc_desc* d);
 int wtconv_forward_unfused(const wtc_desc* d, const void* x,
                            const float* w0, const float* s0, const float* b0,

@@ -142,20 +142,21 @@ int launch_finalize(const FinalizeArgs& f, void* stream);
 // ---------------------------------------------------------------------------
 // Unfused (level-by-level) baseline
 // ---------------------------------------------------------------------------
+constexpr int kMaxUnfusedL = 30;   // levels the baseline accepts (grids stay 1x1 beyond log2 size)
+
 struct UnfusedPlan {
-    // workspace offsets in bytes
-    size_t ll_off[kMaxLm + 2];   // forward: raw LL/band tensors per level [B,4C,h_i,w_i] (fp32)
-    size_t y_off[kMaxLm + 2];    // Y_i (scaled conv outputs) [B,4C,h_i,w_i]
-    size_t z_off[kMaxLm + 2];    // Z_i [B,C,h_{i-1},w_{i-1}]
-    size_t dt_off[kMaxLm + 2];   // backward: analysis of dZ per level
-    size_t ds_off[kMaxLm + 2];   // backward: dS per level
-    size_t part_off;             // weight-gradient partial sums
-    size_t base_off;             // forward: base conv output
+    // workspace offsets in bytes, per level 1..L (float32 tensors)
+    size_t s_off[kMaxUnfusedL + 1];    // S_i   [B, C, 4, h_i, w_i]  bands of x
+    size_t y_off[kMaxUnfusedL + 1];    // Y_i (forward) / dS_i (backward), same shape
+    size_t z_off[kMaxUnfusedL + 1];    // Z_i (forward) / dLL_{i-1} (backward) [B, C, h_{i-1}, w_{i-1}]
+    size_t dt_off[kMaxUnfusedL + 1];   // backward: analysis of g, same shape as S_i
+    size_t part_off;                   // backward: correlation partial sums
     size_t total;
-    int h[kMaxLm + 2], w[kMaxLm + 2];
-    int nblk;                    // reduction partial blocks per channel
+    int h[kMaxUnfusedL + 1], w[kMaxUnfusedL + 1];
 };
 
+// workgroups per channel of the baseline's weight-gradient correlation
+int unfused_corr_blocks(int nb, int nch);
 int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p);
 int unfused_forward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const float* w0,
                     const float* s0, const float* b0, const float* wl, const float* sl, void* out,

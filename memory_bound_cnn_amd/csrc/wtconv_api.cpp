@@ -302,50 +302,31 @@ double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
     }
     UnfusedPlan p;
     if (unfused_plan(d, dir, &p) != WTC_OK) return -1.0;
-    // level-by-level: every intermediate crosses HBM (fp32 intermediates)
+    // Level-by-level baseline: the bytes its kernels move, each tensor read or
+    // written once per kernel that touches it (stencil halos hit in cache).
+    // Intermediates are float32; x, g, out and dx use the storage dtype.
     const double f4 = 4.0;
+    const int kk1 = d->k * d->k + 1;
+    auto band = [&](int i) { return BC * spec_level_area(d, i) * f4; };   // one band of level i
     double t = 0.0;
-    if (dir == 0) {
-        double prevLL = N * e;  // LL_0 = x (storage dtype)
-        for (int i = 1; i <= d->L; ++i) {
-            const double n = BC * spec_level_area(d, i);
-            t += prevLL + 4.0 * n * f4;          // analysis: read LL_{i-1}, write 4 bands
-            t += 4.0 * n * f4 * 2.0;              // subband conv: read bands, write Y_i
-            prevLL = n * f4;
-        }
-        for (int i = d->L; i >= 1; --i) {
-            const double n = BC * spec_level_area(d, i);
-            const double up = BC * spec_level_area(d, i - 1);
-            // synthesis: read Y_i (4 bands) and Z_{i+1}, write Z_i
-            t += 4.0 * n * f4 + (i < d->L ? n * f4 : 0.0) + up * (i == 1 ? f4 : f4);
-        }
-        // base conv + combine: read x, read Z_1, write out
-        t += N * e + (d->L > 0 ? N * f4 : 0.0) + N * e;
-        return t + params;
-    }
-    // backward: analysis cascade of g (read g / dZ_i, write 4 bands);
-    // recompute the bands of x (as forward); per level: dS conv (read dY, write dS),
-    // weight correlation (read dY and S), scale gradient (read dY, S -> conv);
-    // synthesis of dS back to dX; base: read g, x, write dx.
-    double prev = N * e;
-    double prevx = N * e;
+    // analysis cascade (forward: of x; backward: of g and of x): read LL_{i-1}, write 4 bands
+    const double casc_n = dir == 0 ? 1.0 : 2.0;
+    for (int i = 1; i <= d->L; ++i) t += casc_n * ((i == 1 ? N * e : band(i - 1)) + 4.0 * band(i));
+    // subband conv per level: read 4 bands, write 4 bands
+    for (int i = 1; i <= d->L; ++i) t += 8.0 * band(i);
+    // synthesis per level: read 4 bands (+ the deeper partial result), write the finer grid
+    for (int i = 1; i <= d->L; ++i) t += 4.0 * band(i) + (i < d->L ? band(i) : 0.0) + band(i - 1);
+    // base: read the convolved tensor and Z_1 (dLL_0), write out (dx)
+    t += 2.0 * N * e + (d->L > 0 ? band(0) : 0.0);
+    if (dir == 0) return t + params;
+    // correlations: per level read dT_i and S_i (8 bands), base read g and x;
+    // partials written and read back; parameters read twice, gradients written
     for (int i = 1; i <= d->L; ++i) {
-        const double n = BC * spec_level_area(d, i);
-        t += prev + 4.0 * n * f4;                // analysis of dZ_i
-        t += prevx + 4.0 * n * f4;               // analysis of x (recompute S_i)
-        t += 4.0 * n * f4 * 2.0;                 // dS_i = s * rot(W) * dY_i: read dY, write dS
-        t += 4.0 * n * f4 * 2.0;                 // correlations: read dY and S
-        prev = n * f4;
-        prevx = n * f4;
+        t += 8.0 * band(i);
+        t += 2.0 * f4 * unfused_corr_blocks(d->B, 4 * d->C) * 4.0 * d->C * kk1;
     }
-    for (int i = d->L; i >= 1; --i) {
-        const double n = BC * spec_level_area(d, i);
-        const double up = BC * spec_level_area(d, i - 1);
-        t += 4.0 * n * f4 + (i < d->L ? n * f4 : 0.0) + up * f4;
-    }
-    t += 2.0 * N * e + (d->L > 0 ? N * f4 : 0.0) + N * e;  // base: read g, x, dLL_0; write dx
-    t += N * e * 2.0;                                       // base correlations: read g, x
-    return t + 2.0 * params + 4.0 * (double)p.nblk * d->C * (d->k * d->k * (1 + 4.0 * d->L) + 2) * 2.0;
+    t += 2.0 * N * e + 2.0 * f4 * unfused_corr_blocks(d->B, d->C) * (double)d->C * kk1;
+    return t + 3.0 * params;
 }
 
 }  // extern "C"

@@ -1,17 +1,558 @@
-// Level-by-level WTConv baseline (placeholder until the baseline kernels land).
+// Level-by-level WTConv baseline for gfx950: one kernel per step of the
+// cascade, with every intermediate (subbands, convolution outputs, partial
+// syntheses) stored in device memory in float32.  This is the execution
+// structure that "Fast and Memory-Efficient Wavelet Convolutions via
+// I/O-Aware Reformulation" (abstract) describes for the original WTConv: the
+// same operator, its intermediates travelling through HBM between steps.
+//
+// Forward:  analysis L times -> scaled subband conv per level -> synthesis L
+//           times (deepest first) -> base conv + bias + Z_1.
+// Backward: analysis cascade of g (adjoint of the synthesis), analysis cascade
+//           of x, per level the rotated subband conv and the weight-gradient
+//           correlation, synthesis of the subband gradients (adjoint of the
+//           analysis), base rotated conv + correlation; a small kernel per
+//           level applies the chain rule through the scales.
+//
+// The stencil kernels stage tiles in LDS and unroll for the kernel size, and
+// the elementwise ones stream, so the baseline is limited by the HBM round
+// trips of its intermediates rather than by its own arithmetic.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "wtc_internal.h"
 
 namespace wtc {
-int unfused_plan(const wtc_desc*, int, UnfusedPlan*) { return WTC_EINVAL; }
-int unfused_forward(const wtc_desc*, const UnfusedPlan&, const void*, const float*, const float*,
-                    const float*, const float*, const float*, void*, char*, void*) {
-    return WTC_EINVAL;
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCorrTarget = 2048;   // correlation workgroups per launch (before the batch cap)
+
+__device__ __forceinline__ float ldv(const float* p, uint32_t i) { return p[i]; }
+__device__ __forceinline__ float ldv(const uint16_t* p, uint32_t i) {
+    return __uint_as_float(((uint32_t)p[i]) << 16);
 }
-int unfused_backward(const wtc_desc*, const UnfusedPlan&, const void*, const void*, const float*,
-                     const float*, const float*, const float*, void*, float*, float*, float*,
-                     float*, float*, char*, void*) {
-    return WTC_EINVAL;
+__device__ __forceinline__ void stv(float* p, uint32_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stv(uint16_t* p, uint32_t i, float v) {
+    // round to nearest even (finite values)
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    p[i] = (uint16_t)(u >> 16);
 }
+
+uint32_t blocks_for(uint64_t n) {
+    const uint64_t b = (n + kThreads - 1) / kThreads;
+    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(b, 1u << 20));
+}
+
+// One level of the orthonormal 2x2 Haar analysis.  Input plane p is
+// in[p * in_ps + y * w_in + x] (h_in x w_in, zero beyond: the pad to even);
+// output out[(p * 4 + u) * h_o * w_o + j], u = 2 u_y + u_x.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) k_analysis(const T* __restrict__ in, uint32_t in_ps, uint32_t n,
+                                                       int h_in, int w_in, float* __restrict__ out, int h_o,
+                                                       int w_o) {
+    for (uint32_t e = blockIdx.x * kThreads + threadIdx.x; e < n; e += gridDim.x * kThreads) {
+        const uint32_t jx = e % (uint32_t)w_o;
+        const uint32_t t = e / (uint32_t)w_o;
+        const uint32_t jy = t % (uint32_t)h_o;
+        const uint32_t p = t / (uint32_t)h_o;
+        const uint32_t base = p * in_ps;
+        const int y = 2 * (int)jy, x = 2 * (int)jx;
+        const bool rx = x + 1 < w_in, ry = y + 1 < h_in;
+        const float a = ldv(in, base + y * w_in + x);
+        const float b = rx ? ldv(in, base + y * w_in + x + 1) : 0.f;
+        const float c = ry ? ldv(in, base + (y + 1) * w_in + x) : 0.f;
+        const float d = (rx && ry) ? ldv(in, base + (y + 1) * w_in + x + 1) : 0.f;
+        const uint32_t bs = (uint32_t)h_o * w_o;
+        const uint32_t o = p * 4 * bs + jy * w_o + jx;
+        out[o] = 0.5f * ((a + b) + (c + d));
+        out[o + bs] = 0.5f * ((a - b) + (c - d));
+        out[o + 2 * bs] = 0.5f * ((a + b) - (c + d));
+        out[o + 3 * bs] = 0.5f * ((a - b) - (c - d));
+    }
+}
+
+// Tiling of one level's planes for the LDS-staged stencil kernels.  A
+// workgroup stages NPB planes (consecutive planes for the convolutions, the
+// same channel across the batch for the correlation) and one TH x TW tile of
+// each, with a halo of R = k/2, in LDS; each thread then produces 4 vertically
+// adjacent outputs of one column per work item.
+struct Tile {
+    int h, w;       // plane
+    int TH, TW;     // output tile
+    int ntx, nty;   // tiles per plane along x and y
+    int NPB;        // planes per workgroup
+    int NRG;        // 4-row groups per tile (rows staged: 4 NRG + 2 halo)
+};
+
+constexpr int kTileOut = 2048;                  // outputs per workgroup (target)
+constexpr size_t kTileLdsBytes = 48 * 1024;     // LDS per workgroup (cap)
+
+size_t tile_lds_floats(const Tile& t, int k, bool corr) {
+    const int R = k / 2;
+    const size_t halo_tile = (size_t)(4 * t.NRG + 2 * R) * (t.TW + 2 * R);
+    if (corr) return (size_t)t.NPB * (4 * t.NRG * t.TW + halo_tile);
+    return (size_t)t.NPB * (k * k + 2 + halo_tile);
+}
+
+Tile make_tile(int h, int w, int k, bool corr) {
+    Tile t;
+    t.h = h;
+    t.w = w;
+    t.TW = std::min(w, 64);
+    t.TH = std::min(h, 32);
+    t.ntx = (w + t.TW - 1) / t.TW;
+    t.nty = (h + t.TH - 1) / t.TH;
+    t.NRG = (t.TH + 3) / 4;
+    t.NPB = std::max(1, std::min(256, kTileOut / (t.TH * t.TW)));
+    while (t.NPB > 1 && tile_lds_floats(t, k, corr) * sizeof(float) > kTileLdsBytes) --t.NPB;
+    return t;
+}
+
+// Incremental walk over a [n2][n1][n0] index space in flat steps of `step`
+// (avoids a division per element).
+struct Walk3 {
+    int i0, i1, i2, d0, d1, d2, n0, n1;
+    __device__ Walk3(int start, int step, int n0_, int n1_) : n0(n0_), n1(n1_) {
+        i0 = start % n0;
+        const int r = start / n0;
+        i1 = r % n1;
+        i2 = r / n1;
+        d0 = step % n0;
+        const int q = step / n0;
+        d1 = q % n1;
+        d2 = q / n1;
+    }
+    __device__ void next() {
+        i0 += d0;
+        i1 += d1;
+        i2 += d2;
+        if (i0 >= n0) { i0 -= n0; ++i1; }
+        if (i1 >= n1) { i1 -= n1; ++i2; }
+    }
+};
+
+// Stage planes p0 + j * pstride (j < np_valid; zero for j >= np_valid) of the
+// h x w tensor `src`, rows ty0 - halo .. ty0 + 4 NRG + halo - 1 and columns
+// tx0 - halo .. tx0 + TW + halo - 1, zero outside the plane, into
+// lds[j][row][col] (row stride TW + 2 halo).
+template <typename T>
+__device__ void stage(float* lds, const T* __restrict__ src, int p0, int pstride, int np_valid, const Tile& t,
+                      int ty0, int tx0, int halo) {
+    const int RH = 4 * t.NRG + 2 * halo, SW = t.TW + 2 * halo;
+    const int total = t.NPB * RH * SW;
+    const uint32_t hw = (uint32_t)t.h * t.w;
+    Walk3 it(threadIdx.x, kThreads, SW, RH);
+    for (int f = threadIdx.x; f < total; f += kThreads, it.next()) {
+        const int y = ty0 + it.i1 - halo, x = tx0 + it.i0 - halo;
+        float v = 0.f;
+        if (it.i2 < np_valid && y >= 0 && y < t.h && x >= 0 && x < t.w)
+            v = ldv(src, (uint32_t)(p0 + it.i2 * pstride) * hw + (uint32_t)(y * t.w + x));
+        lds[f] = v;
+    }
+}
+
+// Depthwise K x K cross-correlation (weights rotated by 180 degrees if ROT) of
+// P planes, channel ch = p % nch, zero padding K/2:
+//   out[p] = scale[ch] * (W[ch] * in[p]) + bias[ch] + Z[p]   (bias, Z optional)
+// 1-D grid: workgroup = (plane group, tile).
+template <int K, bool ROT, typename TI, typename TO>
+__global__ void __launch_bounds__(kThreads) k_tconv(const TI* __restrict__ in, int P, int nch, Tile t,
+                                                    const float* __restrict__ wt, const float* __restrict__ scale,
+                                                    const float* __restrict__ bias, const float* __restrict__ Z,
+                                                    TO* __restrict__ out) {
+    extern __shared__ float lds[];
+    constexpr int R = K / 2, KK = K * K, NR = 4 + 2 * R;
+    const int ntile = t.ntx * t.nty;
+    const int g = blockIdx.x / ntile, tile = blockIdx.x - g * ntile;
+    const int ty0 = (tile / t.ntx) * t.TH, tx0 = (tile % t.ntx) * t.TW;
+    const int p0 = g * t.NPB;
+    const int npv = min(t.NPB, P - p0);
+    float* wl = lds;                        // [NPB][KK + 2]: weights, scale, bias
+    float* xs = lds + t.NPB * (KK + 2);     // [NPB][4 NRG + 2R][TW + 2R]
+    for (int f = threadIdx.x; f < npv * (KK + 2); f += kThreads) {
+        const int j = f / (KK + 2), d = f - j * (KK + 2);
+        const int ch = (p0 + j) % nch;
+        float v;
+        if (d < KK) v = wt[ch * KK + (ROT ? KK - 1 - d : d)];
+        else if (d == KK) v = scale[ch];
+        else v = bias ? bias[ch] : 0.f;
+        wl[f] = v;
+    }
+    stage(xs, in, p0, 1, npv, t, ty0, tx0, R);
+    __syncthreads();
+    const int SW = t.TW + 2 * R, RH = 4 * t.NRG + 2 * R;
+    const int total = t.NPB * t.NRG * t.TW;
+    const uint32_t hw = (uint32_t)t.h * t.w;
+    Walk3 it(threadIdx.x, kThreads, t.TW, t.NRG);
+    for (int f = threadIdx.x; f < total; f += kThreads, it.next()) {
+        const int j = it.i2, rg = it.i1, c = it.i0;
+        if (j >= npv) continue;
+        const float* wp = wl + j * (KK + 2);
+        const float* xb = xs + (j * RH + rg * 4) * SW + c;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int xr = 0; xr < NR; ++xr) {
+            float xv[K];
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx) xv[kx] = xb[xr * SW + kx];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int ky = xr - q;
+                if (ky < 0 || ky >= K) continue;
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) acc[q] = fmaf(wp[ky * K + kx], xv[kx], acc[q]);
+            }
+        }
+        const float sc = wp[KK], bi = wp[KK + 1];
+        const uint32_t pbase = (uint32_t)(p0 + j) * hw;
+        const int x = tx0 + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = rg * 4 + q, y = ty0 + r;
+            if (r < t.TH && y < t.h && x < t.w) {
+                const uint32_t o = pbase + (uint32_t)(y * t.w + x);
+                float v = fmaf(sc, acc[q], bi);
+                if (Z) v += Z[o];
+                stv(out, o, v);
+            }
+        }
+    }
+}
+
+// Inverse Haar of one level cropped to h_up x w_up: T^0 = Y^0 + Zd (Zd, on the
+// h x w grid, is optional).  The 2x2 orthonormal matrix is its own inverse;
+// one thread writes the 2x2 output block of one coarse position.
+__global__ void __launch_bounds__(kThreads) k_synthesis(const float* __restrict__ Y, const float* __restrict__ Zd,
+                                                        uint32_t n, int h, int w, float* __restrict__ Z, int h_up,
+                                                        int w_up) {
+    for (uint32_t e = blockIdx.x * kThreads + threadIdx.x; e < n; e += gridDim.x * kThreads) {
+        const uint32_t jx = e % (uint32_t)w;
+        const uint32_t t = e / (uint32_t)w;
+        const uint32_t jy = t % (uint32_t)h;
+        const uint32_t p = t / (uint32_t)h;
+        const uint32_t bs = (uint32_t)h * w;
+        const uint32_t j = jy * w + jx;
+        const float* yp = Y + p * 4 * bs + j;
+        float t0 = yp[0];
+        if (Zd) t0 += Zd[p * bs + j];
+        const float t1 = yp[bs], t2 = yp[2 * bs], t3 = yp[3 * bs];
+        const float a = t0 + t1, b = t0 - t1, c = t2 + t3, d = t2 - t3;
+        const int X0 = 2 * (int)jx, Y0 = 2 * (int)jy;
+        float* zp = Z + p * (uint32_t)(h_up * w_up) + (uint32_t)(Y0 * w_up + X0);
+        const bool rx = X0 + 1 < w_up, ry = Y0 + 1 < h_up;
+        zp[0] = 0.5f * (a + c);
+        if (rx) zp[1] = 0.5f * (b + d);
+        if (ry) {
+            zp[w_up] = 0.5f * (a - c);
+            if (rx) zp[w_up + 1] = 0.5f * (b - d);
+        }
+    }
+}
+
+// Weight-gradient correlation of channel ch = blockIdx.x over the batch slice
+// of workgroup blockIdx.y (planes (b * nch + ch), b in the slice):
+//   part[(blk * nch + ch) * (K*K + 1) + d] = sum_j A[j] X[j + d]   (X zero outside)
+//   part[(blk * nch + ch) * (K*K + 1) + K*K] = sum_j A[j]
+template <int K, typename TA, typename TX>
+__global__ void __launch_bounds__(kThreads) k_tcorr(const TA* __restrict__ A, const TX* __restrict__ X, int nb,
+                                                    int nch, Tile t, int nblk, float* __restrict__ part) {
+    extern __shared__ float lds[];
+    constexpr int R = K / 2, KK = K * K, NR = 4 + 2 * R, NW = kThreads / 64;
+    __shared__ float red[NW][KK + 1];
+    const int ch = blockIdx.x, blk = blockIdx.y;
+    const int b0 = (int)((long)nb * blk / nblk), b1 = (int)((long)nb * (blk + 1) / nblk);
+    const int ARH = 4 * t.NRG, SW = t.TW + 2 * R, RH = 4 * t.NRG + 2 * R;
+    float* as = lds;                            // [NPB][4 NRG][TW]
+    float* xs = lds + t.NPB * ARH * t.TW;       // [NPB][4 NRG + 2R][TW + 2R]
+    float acc[KK + 1];
+#pragma unroll
+    for (int d = 0; d <= KK; ++d) acc[d] = 0.f;
+    const int total = t.NPB * t.NRG * t.TW;
+    for (int bg = b0; bg < b1; bg += t.NPB) {
+        const int npv = min(t.NPB, b1 - bg);
+        for (int tile = 0; tile < t.ntx * t.nty; ++tile) {
+            const int ty0 = (tile / t.ntx) * t.TH, tx0 = (tile % t.ntx) * t.TW;
+            __syncthreads();   // the previous tile's reads are done
+            stage(as, A, bg * nch + ch, nch, npv, t, ty0, tx0, 0);
+            stage(xs, X, bg * nch + ch, nch, npv, t, ty0, tx0, R);
+            __syncthreads();
+            Walk3 it(threadIdx.x, kThreads, t.TW, t.NRG);
+            for (int f = threadIdx.x; f < total; f += kThreads, it.next()) {
+                const int j = it.i2, rg = it.i1, c = it.i0;
+                if (j >= npv) continue;
+                const float* ab = as + (j * ARH + rg * 4) * t.TW + c;
+                const float* xb = xs + (j * RH + rg * 4) * SW + c;
+                float av[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) av[q] = ab[q * t.TW];   // zero outside the plane and tile rows
+                acc[KK] += (av[0] + av[1]) + (av[2] + av[3]);
+#pragma unroll
+                for (int xr = 0; xr < NR; ++xr) {
+                    float xv[K];
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) xv[kx] = xb[xr * SW + kx];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int ky = xr - q;
+                        if (ky < 0 || ky >= K) continue;
+#pragma unroll
+                        for (int kx = 0; kx < K; ++kx) acc[ky * K + kx] = fmaf(av[q], xv[kx], acc[ky * K + kx]);
+                    }
+                }
+            }
+        }
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 0; d <= KK; ++d) {
+        float v = acc[d];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) red[wv][d] = v;
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d <= KK; d += kThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) s += red[q][d];
+        part[((uint32_t)blk * nch + ch) * (KK + 1) + d] = s;
+    }
+}
+
+// dW = s * C, ds = sum_d W * C, and (base level) db = sum g, from the partials.
+__global__ void k_corr_finalize(const float* __restrict__ part, int nch, int nblk, int k,
+                                const float* __restrict__ wt, const float* __restrict__ scale,
+                                float* __restrict__ dw, float* __restrict__ ds, float* __restrict__ db) {
+    const int ch = blockIdx.x * blockDim.x + threadIdx.x;
+    if (ch >= nch) return;
+    const int kk = k * k;
+    float dsv = 0.f;
+    for (int d = 0; d < kk; ++d) {
+        float cv = 0.f;
+        for (int b = 0; b < nblk; ++b) cv += part[((size_t)b * nch + ch) * (kk + 1) + d];
+        dw[(size_t)ch * kk + d] = scale[ch] * cv;
+        dsv = fmaf(wt[(size_t)ch * kk + d], cv, dsv);
+    }
+    ds[ch] = dsv;
+    if (db) {
+        float s = 0.f;
+        for (int b = 0; b < nblk; ++b) s += part[((size_t)b * nch + ch) * (kk + 1) + kk];
+        db[ch] = s;
+    }
+}
+
+template <typename T>
+void launch_analysis(const T* in, uint32_t in_ps, int P, int h_in, int w_in, float* out, int h_o, int w_o,
+                     hipStream_t st) {
+    const uint32_t n = (uint32_t)P * h_o * w_o;
+    hipLaunchKernelGGL(k_analysis<T>, dim3(blocks_for(n)), dim3(kThreads), 0, st, in, in_ps, n, h_in, w_in, out,
+                       h_o, w_o);
+}
+
+void launch_synthesis(const float* Y, const float* Zd, int P, int h, int w, float* Z, int h_up, int w_up,
+                      hipStream_t st) {
+    const uint32_t n = (uint32_t)P * h * w;
+    hipLaunchKernelGGL(k_synthesis, dim3(blocks_for(n)), dim3(kThreads), 0, st, Y, Zd, n, h, w, Z, h_up, w_up);
+}
+
+// out = scale * conv(in) + bias + Z over P planes of h x w, channel p % nch
+template <int K, typename TI, typename TO>
+void launch_conv(bool rot, const TI* in, int P, int nch, int h, int w, const float* wt, const float* scale,
+                 const float* bias, const float* Z, TO* out, hipStream_t st) {
+    const Tile t = make_tile(h, w, K, false);
+    const uint32_t grid = (uint32_t)((P + t.NPB - 1) / t.NPB) * (uint32_t)(t.ntx * t.nty);
+    const size_t lds = tile_lds_floats(t, K, false) * sizeof(float);
+    if (rot)
+        hipLaunchKernelGGL((k_tconv<K, true, TI, TO>), dim3(grid), dim3(kThreads), lds, st, in, P, nch, t, wt, scale,
+                           bias, Z, out);
+    else
+        hipLaunchKernelGGL((k_tconv<K, false, TI, TO>), dim3(grid), dim3(kThreads), lds, st, in, P, nch, t, wt,
+                           scale, bias, Z, out);
+}
+
+}  // namespace
+
+int unfused_corr_blocks(int nb, int nch) {
+    return std::max(1, std::min(nb, (kCorrTarget + nch - 1) / nch));
+}
+
+namespace {
+
+// correlation + finalize of one level (nch channels, nb planes per channel)
+template <int K, typename TA, typename TX>
+void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const float* wt, const float* scale,
+                 float* dw, float* ds, float* db, float* part, hipStream_t st) {
+    const int nblk = unfused_corr_blocks(nb, nch);
+    const Tile t = make_tile(h, w, K, true);
+    const size_t lds = tile_lds_floats(t, K, true) * sizeof(float);
+    hipLaunchKernelGGL((k_tcorr<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, nblk,
+                       part);
+    hipLaunchKernelGGL(k_corr_finalize, dim3((nch + 63) / 64), dim3(64), 0, st, part, nch, nblk, K, wt, scale, dw,
+                       ds, db);
+}
+
+template <int K, typename T>
+int fwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const float* w0, const float* s0,
+          const float* b0, const float* wl, const float* sl, T* out, char* ws, hipStream_t st) {
+    const int B = d->B, C = d->C, L = d->L;
+    const int P = B * C;
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    for (int i = 1; i <= L; ++i) {
+        if (i == 1)
+            launch_analysis<T>(x, (uint32_t)(p.h[0] * p.w[0]), P, p.h[0], p.w[0], F(p.s_off[1]), p.h[1], p.w[1], st);
+        else
+            launch_analysis<float>(F(p.s_off[i - 1]), (uint32_t)(4 * p.h[i - 1] * p.w[i - 1]), P, p.h[i - 1],
+                                   p.w[i - 1], F(p.s_off[i]), p.h[i], p.w[i], st);
+    }
+    for (int i = 1; i <= L; ++i)
+        launch_conv<K, float, float>(false, F(p.s_off[i]), 4 * P, 4 * C, p.h[i], p.w[i],
+                                     wl + (size_t)(i - 1) * 4 * C * K * K, sl + (size_t)(i - 1) * 4 * C, nullptr,
+                                     nullptr, F(p.y_off[i]), st);
+    for (int i = L; i >= 1; --i)
+        launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : nullptr, P, p.h[i], p.w[i], F(p.z_off[i]),
+                         p.h[i - 1], p.w[i - 1], st);
+    launch_conv<K, T, T>(false, x, P, C, d->H, d->W, w0, s0, b0, L > 0 ? F(p.z_off[1]) : nullptr, out, st);
+    return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
+}
+
+template <int K, typename T>
+int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const float* w0, const float* s0,
+          const float* wl, const float* sl, T* dx, float* dw0, float* ds0, float* db0, float* dwl, float* dsl,
+          char* ws, hipStream_t st) {
+    const int B = d->B, C = d->C, L = d->L;
+    const int P = B * C;
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    float* part = F(p.part_off);
+    // analysis cascades of g (the adjoint of the synthesis) and of x
+    for (int i = 1; i <= L; ++i) {
+        if (i == 1) {
+            const uint32_t ps = (uint32_t)(p.h[0] * p.w[0]);
+            launch_analysis<T>(g, ps, P, p.h[0], p.w[0], F(p.dt_off[1]), p.h[1], p.w[1], st);
+            launch_analysis<T>(x, ps, P, p.h[0], p.w[0], F(p.s_off[1]), p.h[1], p.w[1], st);
+        } else {
+            const uint32_t ps = (uint32_t)(4 * p.h[i - 1] * p.w[i - 1]);
+            launch_analysis<float>(F(p.dt_off[i - 1]), ps, P, p.h[i - 1], p.w[i - 1], F(p.dt_off[i]), p.h[i],
+                                   p.w[i], st);
+            launch_analysis<float>(F(p.s_off[i - 1]), ps, P, p.h[i - 1], p.w[i - 1], F(p.s_off[i]), p.h[i], p.w[i],
+                                   st);
+        }
+    }
+    // per level: dS = s * (rot W * dY);  dW, ds from corr(dY, S)
+    for (int i = 1; i <= L; ++i) {
+        const float* wli = wl + (size_t)(i - 1) * 4 * C * K * K;
+        const float* sli = sl + (size_t)(i - 1) * 4 * C;
+        launch_conv<K, float, float>(true, F(p.dt_off[i]), 4 * P, 4 * C, p.h[i], p.w[i], wli, sli, nullptr, nullptr,
+                                     F(p.y_off[i]), st);
+        launch_corr<K, float, float>(F(p.dt_off[i]), F(p.s_off[i]), B, 4 * C, p.h[i], p.w[i], wli, sli,
+                                     dwl + (size_t)(i - 1) * 4 * C * K * K, dsl + (size_t)(i - 1) * 4 * C, nullptr,
+                                     part, st);
+    }
+    // adjoint of the analysis: synthesis of dS, deepest first
+    for (int i = L; i >= 1; --i)
+        launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : nullptr, P, p.h[i], p.w[i], F(p.z_off[i]),
+                         p.h[i - 1], p.w[i - 1], st);
+    // base: dx = s0 * (rot W0 * g) + dLL_0;  dW0, ds0, db0 from corr(g, x)
+    launch_conv<K, T, T>(true, g, P, C, d->H, d->W, w0, s0, nullptr, L > 0 ? F(p.z_off[1]) : nullptr, dx, st);
+    launch_corr<K, T, T>(g, x, B, C, d->H, d->W, w0, s0, dw0, ds0, db0, part, st);
+    return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
+}
+
+size_t align256_host(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+// Workspace (float32 tensors, 256-byte aligned).  Per level i:
+//   S_i  [B, C, 4, h_i, w_i]       bands of x
+//   Y_i  same shape                forward: scaled conv output;  backward: dS_i
+//   Z_i  [B, C, h_{i-1}, w_{i-1}]  forward: partial synthesis;  backward: dLL_{i-1}
+//   dT_i same shape as S_i         backward only: analysis of g
+// then the correlation partials (backward).
+int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p) {
+    if (d->k > kMaxK) return WTC_ESHAPE;
+    if (d->L > kMaxUnfusedL) return WTC_ESHAPE;
+    const uint64_t BC = (uint64_t)d->B * d->C;
+    // 32-bit element indexing of every tensor (the level-1 bands are the largest)
+    const uint64_t h1 = (d->H + 1) / 2, w1 = (d->W + 1) / 2;
+    if (BC * d->H * d->W >= (1ull << 31) || BC * 4 * h1 * w1 >= (1ull << 31)) return WTC_ESHAPE;
+    p->h[0] = d->H;
+    p->w[0] = d->W;
+    size_t off = 0;
+    for (int i = 1; i <= d->L; ++i) {
+        p->h[i] = (p->h[i - 1] + 1) / 2;
+        p->w[i] = (p->w[i - 1] + 1) / 2;
+        const size_t n4 = BC * 4 * p->h[i] * p->w[i] * sizeof(float);
+        const size_t nz = BC * p->h[i - 1] * p->w[i - 1] * sizeof(float);
+        p->s_off[i] = off;
+        off += align256_host(n4);
+        p->y_off[i] = off;
+        off += align256_host(n4);
+        p->z_off[i] = off;
+        off += align256_host(nz);
+        if (bwd) {
+            p->dt_off[i] = off;
+            off += align256_host(n4);
+        }
+    }
+    p->part_off = off;
+    if (bwd) {
+        const int kk1 = d->k * d->k + 1;
+        size_t np = (size_t)unfused_corr_blocks(d->B, d->C) * d->C * kk1;
+        if (d->L > 0) np = std::max(np, (size_t)unfused_corr_blocks(d->B, 4 * d->C) * 4 * d->C * kk1);
+        off += align256_host(np * sizeof(float));
+    }
+    p->total = off;
+    return WTC_OK;
+}
+
+namespace {
+
+template <int K>
+int fwd_k(const wtc_desc* d, const UnfusedPlan& p, const void* x, const float* w0, const float* s0,
+          const float* b0, const float* wl, const float* sl, void* out, char* ws, hipStream_t st) {
+    if (d->dtype == WTC_BF16)
+        return fwd_t<K, uint16_t>(d, p, static_cast<const uint16_t*>(x), w0, s0, b0, wl, sl,
+                                  static_cast<uint16_t*>(out), ws, st);
+    return fwd_t<K, float>(d, p, static_cast<const float*>(x), w0, s0, b0, wl, sl, static_cast<float*>(out), ws, st);
+}
+
+template <int K>
+int bwd_k(const wtc_desc* d, const UnfusedPlan& p, const void* x, const void* g, const float* w0,
+          const float* s0, const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0,
+          float* dwl, float* dsl, char* ws, hipStream_t st) {
+    if (d->dtype == WTC_BF16)
+        return bwd_t<K, uint16_t>(d, p, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(g), w0, s0, wl,
+                                  sl, static_cast<uint16_t*>(dx), dw0, ds0, db0, dwl, dsl, ws, st);
+    return bwd_t<K, float>(d, p, static_cast<const float*>(x), static_cast<const float*>(g), w0, s0, wl, sl,
+                           static_cast<float*>(dx), dw0, ds0, db0, dwl, dsl, ws, st);
+}
+
+}  // namespace
+
+int unfused_forward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const float* w0, const float* s0,
+                    const float* b0, const float* wl, const float* sl, void* out, char* ws, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    switch (d->k) {
+        case 1: return fwd_k<1>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
+        case 3: return fwd_k<3>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
+        case 5: return fwd_k<5>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
+        case 7: return fwd_k<7>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
+        default: return WTC_ESHAPE;
+    }
+}
+
+int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const void* g, const float* w0,
+                     const float* s0, const float* wl, const float* sl, void* dx, float* dw0, float* ds0,
+                     float* db0, float* dwl, float* dsl, char* ws, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    switch (d->k) {
+        case 1: return bwd_k<1>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
+        case 3: return bwd_k<3>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
+        case 5: return bwd_k<5>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
+        case 7: return bwd_k<7>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
+        default: return WTC_ESHAPE;
+    }
+}
+
 }  // namespace wtc

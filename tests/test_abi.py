@@ -99,3 +99,56 @@ def test_flop_count_closed_form():
     fma = 25 + 100 * (1 / 4 + 1 / 16 + 1 / 64)
     adds = 2 + 16 * (1 / 4 + 1 / 16 + 1 / 64)
     assert abs(f - N * (2 * fma + adds)) < 1e-6 * f
+
+
+def test_unfused_workspace_and_limits():
+    lib = binding.load_library()
+    B, C, H, W, L, k = 2, 3, 16, 10, 3, 5
+    # forward: S_i, Y_i (4 bands each) and Z_i (the finer grid) per level, float32, 256-byte aligned
+    sizes = [(16, 10), (8, 5), (4, 3), (2, 2)]
+    want = 0
+    for i in range(1, L + 1):
+        n4 = B * C * 4 * sizes[i][0] * sizes[i][1] * 4
+        nz = B * C * sizes[i - 1][0] * sizes[i - 1][1] * 4
+        want += 2 * (-(-n4 // 256) * 256) + (-(-nz // 256) * 256)
+    assert binding.wtconv_forward_unfused_workspace(B, C, H, W, L, k) == want
+    assert binding.wtconv_forward_unfused_workspace(B, C, H, W, 0, k) == 0
+    assert binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k) > want
+    # any plane size is accepted (no LDS limit) ...
+    assert binding.wtconv_forward_unfused_workspace(1, 1, 512, 512, 2, 5) > 0
+    # ... but not more than 30 levels, k > 7, or tensors beyond 32-bit indexing
+    d = _desc(L=31)
+    assert lib.wtconv_forward_unfused(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      1 << 40, None) == binding.WTC_ESHAPE
+    d = _desc(k=9)
+    assert lib.wtconv_forward_unfused(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      1 << 40, None) == binding.WTC_ESHAPE
+    d = _desc(B=4096, C=1024, H=32, W=32)
+    assert lib.wtconv_forward_unfused(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      1 << 40, None) == binding.WTC_ESHAPE
+    d = _desc()
+    need = lib.wtconv_forward_unfused_workspace(ctypes.byref(d))
+    assert lib.wtconv_forward_unfused(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      need - 1, None) == binding.WTC_EWORKSPACE
+
+
+def test_io_model_unfused_counts_intermediates():
+    # forward at L = 1 on a 64x64 fp32 plane, per plane (N = 4096 pixels, bands 4 x 1024):
+    # analysis reads N, writes N; conv reads N, writes N; synthesis reads N, writes N;
+    # base reads x and Z_1, writes out: 9 N floats
+    B, C, H, W, k = 1, 1, 64, 64, 5
+    N = H * W
+    params = 4 * (C * k * k * (1 + 4) + C * (2 + 4))
+    f1 = binding.wtconv_io_model_bytes(B, C, H, W, 1, k, "fp32", 1, 0)
+    assert abs(f1 - (9 * N * 4 + params)) < 1e-6 * f1
+    # each level adds traffic, and the unfused path always moves more than the fused one
+    prev = f1
+    for L in range(2, 6):
+        f = binding.wtconv_io_model_bytes(B, C, H, W, L, k, "fp32", 1, 0)
+        assert f > prev
+        prev = f
+    for L in range(0, 6):
+        for dr in (0, 1):
+            fu = binding.wtconv_io_model_bytes(32, 96, 64, 64, L, k, "fp32", 1, dr)
+            fz = binding.wtconv_io_model_bytes(32, 96, 64, 64, L, k, "fp32", 0, dr)
+            assert fu >= fz * (0.99 if L == 0 else 1.5), (L, dr)

@@ -1,0 +1,53 @@
+"""Parity of the level-by-level HIP baseline (the "_unfused" entry points)
+with the float64 oracle, and agreement with the fused path at a full
+benchmark shape.  Same tolerances as the fused path: max|err| <= 1e-4 * RMS
+(float32 storage), 2e-2 * RMS (bfloat16 storage)."""
+
+import pytest
+import torch
+
+from memory_bound_cnn_amd.inputs import WORKLOADS, workload_inputs
+from tests.gpu_helpers import check_all, host, inputs, oracle_ref, rel_err, run_fused, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    (1, 8, 32, 32, 2, 5, 100, "fp32"),
+    (2, 6, 64, 64, 3, 5, 101, "fp32"),
+    (3, 8, 32, 32, 3, 5, 102, "bf16"),
+    (1, 2, 128, 128, 5, 5, 103, "fp32"),
+    (5, 8, 14, 14, 2, 5, 104, "fp32"),
+    (9, 8, 7, 7, 1, 5, 105, "fp32"),
+    (2, 3, 16, 16, 0, 5, 106, "fp32"),     # L = 0
+    (2, 3, 13, 10, 3, 3, 107, "fp32"),     # odd sides, k = 3
+    (1, 2, 3, 3, 5, 3, 108, "fp32"),       # levels past the 1x1 grid
+    (1, 2, 9, 17, 2, 7, 109, "fp32"),      # k = 7
+    (2, 4, 24, 24, 2, 1, 110, "fp32"),     # k = 1
+    (1, 1, 200, 72, 2, 5, 111, "fp32"),    # larger than the fused path's LDS plane limit in one side
+]
+
+
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", CASES)
+def test_unfused_matches_oracle(B, C, H, W, L, k, seed, dtype):
+    d = inputs(B, C, H, W, L, k, seed, dtype)
+    t = to_dev(d, dtype, L)
+    out, gr = run_fused(t, L, "unfused")
+    ref_out, ref_gr = oracle_ref(d, L)
+    check_all(out, gr, ref_out, ref_gr, dtype, f"unfused B{B} C{C} {H}x{W} L{L} k{k} {dtype}")
+
+
+@pytest.mark.parametrize("name", ["stage1_b32c96_64x64_L3", "bf16_b64c192_32x32_L3"])
+def test_unfused_agrees_with_fused_full_size(name):
+    wl_ = WORKLOADS[name]
+    d = workload_inputs(wl_)
+    t = to_dev(d, wl_.dtype, wl_.L)
+    fo, fg = run_fused(t, wl_.L, "fused")
+    uo, ug = run_fused(t, wl_.L, "unfused")
+    tol = 2e-4 if wl_.dtype == "fp32" else 4e-2   # both sides within the oracle tolerance
+    errs = {"out": rel_err(host(uo), host(fo))}
+    for key in fg:
+        if fg[key] is not None:
+            errs[key] = rel_err(host(ug[key]), host(fg[key]))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{name}: {bad} (all {errs})"
+    torch.cuda.synchronize()
