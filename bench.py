@@ -36,6 +36,7 @@ VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 VALU_PACKED_PEAK_TFLOPS = 2 * VALU_PEAK_TFLOPS
 HEADLINE = "stage1_b32c96_64x64_L3"
 MALL_BYTES = 256 * 2 ** 20
+COPY_PROBE_MIB = 1024
 
 
 def parse():
@@ -53,6 +54,14 @@ def parse():
     p.add_argument("--copy-probe-mib", type=int, default=None,
                    help="run a plain device copy (read N + write N bytes) 3 times, to calibrate "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known traffic")
+    p.add_argument("--stats-summary", nargs=2, metavar=("PROFILE_DIR", "OUT_TXT"), default=None,
+                   help="format the kernel_stats.csv of a rocprofv3 --kernel-trace --stats --output-format csv "
+                        "run as a text summary (no GPU needed)")
+    p.add_argument("--pmc-summary", nargs=5, default=None,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT_TXT"),
+                   help="turn FETCH_SIZE / WRITE_SIZE counter runs of --profile-steps and of --copy-probe-mib "
+                        "into calibrated HBM bytes per launch: writes OUT_TXT and profiles/pmc_traffic.json")
+    p.add_argument("--cmd", default="", help="command line recorded in a summary")
     return p.parse_args()
 
 
@@ -182,6 +191,127 @@ def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
 
 
 # ---------------------------------------------------------------------------
+# rocprofv3 summaries (CSV output) -> committed text summaries
+# ---------------------------------------------------------------------------
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for fn in sorted(files):
+            if fn.endswith(suffix):
+                return os.path.join(root, fn)
+    raise SystemExit(f"no *{suffix} under {d}")
+
+
+def _rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(names)
+
+
+def kernel_role(name):
+    """'fwd' / 'bwd' for the fused kernels, None for anything else."""
+    import re
+    if "wtc_finalize_kernel" in name:
+        return "bwd"
+    m = re.search(r"wtc_fused_kernel<\s*\d+\s*,[^,]+,\s*(true|false)", name)
+    if m:
+        return "bwd" if m.group(1) == "true" else "fwd"
+    return None
+
+
+def _short(name, n=96):
+    name = name.replace("(anonymous namespace)::", "")
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def stats_summary(prof_dir, out_txt, cmd):
+    rows = _rows(_find_csv(prof_dir, "kernel_stats.csv"))
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {cmd}", "",
+             f"{'kernel':96s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_us':>10s} {'pct':>6s}"]
+    for r in rows:
+        calls = int(_col(r, "Calls"))
+        lines.append(f"{_short(_col(r, 'Name', 'KernelName')):96s} {calls:6d} "
+                     f"{float(_col(r, 'AverageNs')) / 1e3:9.2f} {float(_col(r, 'MinNs')) / 1e3:9.2f} "
+                     f"{float(_col(r, 'MaxNs')) / 1e3:9.2f} {float(_col(r, 'TotalDurationNs')) / 1e3:10.1f} "
+                     f"{float(_col(r, 'Percentage')):6.2f}")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _pmc_avg(d, counter):
+    """Average counter value (KiB) per dispatch, per kernel name."""
+    acc = {}
+    for r in _rows(_find_csv(d, "counter_collection.csv")):
+        if _col(r, "Counter_Name", "counter_name") != counter:
+            continue
+        k = _col(r, "Kernel_Name", "kernel_name")
+        acc.setdefault(k, []).append(float(_col(r, "Counter_Value", "value")))
+    return {k: sum(v) / len(v) for k, v in acc.items()}
+
+
+def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_txt, cmd, wl_name, L):
+    from memory_bound_cnn_amd.inputs import WORKLOADS
+    fetch, write = _pmc_avg(fetch_dir, "FETCH_SIZE"), _pmc_avg(write_dir, "WRITE_SIZE")
+    cf, cw = _pmc_avg(cfetch_dir, "FETCH_SIZE"), _pmc_avg(cwrite_dir, "WRITE_SIZE")
+    # the copy probe's kernel is the one elementwise kernel moving the most bytes
+    ck = max(cf, key=lambda k: cf[k])
+    copy_bytes = float(COPY_PROBE_MIB * 2 ** 20)
+    f_fac = copy_bytes / (cf[ck] * 1024.0)
+    w_fac = copy_bytes / (cw[ck] * 1024.0)
+    wl = WORKLOADS[wl_name]
+    shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
+    tot = {"fwd": 0.0, "bwd": 0.0}
+    per_kernel = {}
+    for k in sorted(set(fetch) | set(write)):
+        role = kernel_role(k)
+        if role is None:
+            continue
+        rb = fetch.get(k, 0.0) * 1024.0 * f_fac
+        wb = write.get(k, 0.0) * 1024.0 * w_fac
+        tot[role] += rb + wb
+        per_kernel[_short(k)] = {"role": role, "read_bytes": rb, "write_bytes": wb,
+                                 "fetch_kib_raw": fetch.get(k), "write_kib_raw": write.get(k)}
+    from memory_bound_cnn_amd import binding
+    model = {"fwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=0),
+             "bwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=1)}
+    rec = {"source_hash": kernel_source_hash(), "command": cmd,
+           "calibration": {"copy_kernel": _short(ck), "copy_bytes_each_way": copy_bytes,
+                           "fetch_factor": f_fac, "write_factor": w_fac},
+           "workloads": {f"{wl_name}_L{L}": {"fwd_bytes": tot["fwd"], "bwd_bytes": tot["bwd"],
+                                             "model_fwd_bytes": model["fwd"], "model_bwd_bytes": model["bwd"],
+                                             "kernels": per_kernel}}}
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    old = {}
+    if os.path.exists(path):
+        try:
+            old = json.load(open(path))
+        except ValueError:
+            old = {}
+    if old.get("source_hash") == rec["source_hash"]:
+        old["workloads"].update(rec["workloads"])
+        rec["workloads"] = old["workloads"]
+    json.dump(rec, open(path, "w"), indent=1)
+    lines = ["# rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, calibrated against a plain copy",
+             f"# command: {cmd}", "",
+             f"copy probe: {_short(ck)} moving {copy_bytes:.0f} B each way; FETCH_SIZE reads "
+             f"{cf[ck]:.1f} KiB -> factor {f_fac:.4f}; WRITE_SIZE reads {cw[ck]:.1f} KiB -> factor {w_fac:.4f}",
+             f"workload {wl_name} L={L}", ""]
+    for k, v in per_kernel.items():
+        lines.append(f"{k:96s} {v['role']}: FETCH {v['fetch_kib_raw']} KiB, WRITE {v['write_kib_raw']} KiB "
+                     f"-> read {v['read_bytes'] / 1e6:.2f} MB, write {v['write_bytes'] / 1e6:.2f} MB")
+    for r in ("fwd", "bwd"):
+        lines.append(f"{r}: measured {tot[r] / 1e6:.2f} MB per call vs I/O model {model[r] / 1e6:.2f} MB "
+                     f"(ratio {tot[r] / model[r]:.3f})")
+    open(out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_from_profiles(wl, L):
     """HBM bytes per backward launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel sources."""
@@ -211,6 +341,12 @@ def main():
     binding.load_library()
     wl = WORKLOADS[a.workload]
     L = wl.L if a.level is None else a.level
+    if a.stats_summary:
+        stats_summary(a.stats_summary[0], a.stats_summary[1], a.cmd)
+        return
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary, a.cmd, wl.name, L)
+        return
     shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
     io_f = binding.wtconv_io_model_bytes(*shp, impl=0, direction=0)
     io_b = binding.wtconv_io_model_bytes(*shp, impl=0, direction=1)
@@ -226,6 +362,8 @@ def main():
         raise SystemExit("bench.py needs a GPU")
 
     if a.copy_probe_mib is not None:
+        if a.copy_probe_mib != COPY_PROBE_MIB:
+            raise SystemExit(f"--copy-probe-mib must be {COPY_PROBE_MIB} (the size the calibration assumes)")
         n = a.copy_probe_mib * 2 ** 20 // 4
         src = torch.randn(n, device="cuda")
         dst = torch.empty_like(src)

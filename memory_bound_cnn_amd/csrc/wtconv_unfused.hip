@@ -322,25 +322,30 @@ __global__ void __launch_bounds__(kThreads) k_tcorr(const TA* __restrict__ A, co
 }
 
 // dW = s * C, ds = sum_d W * C, and (base level) db = sum g, from the partials.
-__global__ void k_corr_finalize(const float* __restrict__ part, int nch, int nblk, int k,
-                                const float* __restrict__ wt, const float* __restrict__ scale,
-                                float* __restrict__ dw, float* __restrict__ ds, float* __restrict__ db) {
-    const int ch = blockIdx.x * blockDim.x + threadIdx.x;
-    if (ch >= nch) return;
+// One workgroup of 64 lanes per channel, lane d < K*K+1 sums slot d over the
+// partial blocks in a fixed order.
+__global__ void __launch_bounds__(64) k_corr_finalize(const float* __restrict__ part, int nch, int nblk, int k,
+                                                      const float* __restrict__ wt, const float* __restrict__ scale,
+                                                      float* __restrict__ dw, float* __restrict__ ds,
+                                                      float* __restrict__ db) {
+    const int ch = blockIdx.x, d = threadIdx.x;
     const int kk = k * k;
-    float dsv = 0.f;
-    for (int d = 0; d < kk; ++d) {
-        float cv = 0.f;
-        for (int b = 0; b < nblk; ++b) cv += part[((size_t)b * nch + ch) * (kk + 1) + d];
+    float cv = 0.f;
+    if (d <= kk) {
+        const float* pp = part + (size_t)ch * (kk + 1) + d;
+        const size_t stride = (size_t)nch * (kk + 1);
+#pragma unroll 8
+        for (int b = 0; b < nblk; ++b) cv += pp[b * stride];
+    }
+    float wv = 0.f;
+    if (d < kk) {
         dw[(size_t)ch * kk + d] = scale[ch] * cv;
-        dsv = fmaf(wt[(size_t)ch * kk + d], cv, dsv);
+        wv = wt[(size_t)ch * kk + d] * cv;
     }
-    ds[ch] = dsv;
-    if (db) {
-        float s = 0.f;
-        for (int b = 0; b < nblk; ++b) s += part[((size_t)b * nch + ch) * (kk + 1) + kk];
-        db[ch] = s;
-    }
+    if (d == kk && db) db[ch] = cv;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wv += __shfl_xor(wv, o, 64);
+    if (d == 0) ds[ch] = wv;
 }
 
 template <typename T>
@@ -389,7 +394,7 @@ void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const 
     const size_t lds = tile_lds_floats(t, K, true) * sizeof(float);
     hipLaunchKernelGGL((k_tcorr<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, nblk,
                        part);
-    hipLaunchKernelGGL(k_corr_finalize, dim3((nch + 63) / 64), dim3(64), 0, st, part, nch, nblk, K, wt, scale, dw,
+    hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, K, wt, scale, dw,
                        ds, db);
 }
 
