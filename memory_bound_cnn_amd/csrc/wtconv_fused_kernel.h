@@ -311,12 +311,13 @@ struct CtGeom {
     __device__ static constexpr int P() { return partial_len(K, LM); }
 };
 
-// Workgroup barrier for LDS communication only.  __syncthreads() also fences
-// device memory, i.e. it waits for every outstanding global load and store of
-// the wave -- which would drain the next planes' prefetch and the previous
-// plane's stores at every phase boundary.  All inter-wave communication in
-// these kernels goes through LDS, so waiting for the LDS counter suffices; the
-// empty asm statements keep the compiler from moving memory accesses across.
+// Workgroup barrier for LDS communication only: waits for this wave's LDS
+// operations (lgkmcnt) and meets the other waves at s_barrier, leaving global
+// loads (the next planes' prefetch) and stores in flight.  All inter-wave
+// communication in these kernels goes through LDS.  Unlike __syncthreads() it
+// carries no memory-model fence, so what it waits for does not depend on how
+// the compiler lowers one; the empty asm statements keep the compiler from
+// moving memory accesses across it.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt untouched
