@@ -112,7 +112,7 @@ struct FusedArgs {
     Layout lay;
     int wts_off;       // folded weights (per workgroup)
     int red_off;       // reduction scratch (backward)
-    int dsub;          // position subsets of the deep-level correlation
+    int dsub;          // band-row subsets of the deep-level (>= 3) correlation roles
     int P;             // partial record length (floats)
 };
 

@@ -70,7 +70,6 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         double best = 2.0;
         for (int np = np_fit; np >= std::max(1, np_fit / 2); --np) {
             int nt = round_up(4 * a.qpp * np, 64);
-            if (bwd && a.Lm >= 3) nt = std::max(nt, round_up(4 * KK, 64));
             const double idle = 1.0 - (double)(4 * a.qpp * np) / nt;
             if (idle < best - 1e-9) {
                 best = idle;
@@ -78,7 +77,6 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
             }
         }
         nthr = round_up(4 * a.qpp * NP, 64);
-        if (bwd && a.Lm >= 3) nthr = std::max(nthr, round_up(4 * KK, 64));
     } else if (a.qpp <= 128) {
         nthr = 512;
     } else if (a.qpp <= 256) {
@@ -95,13 +93,12 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         a.pf_on = (units * (a.vec ? 4 : 1) <= 16) ? 1 : 0;
         if (NP * per >= 65536) return WTC_ESHAPE;   // fast in-kernel index division range
     }
-    a.dsub = std::max(1, nthr / (4 * KK));
-    if (bwd && a.Lm >= 3 && nthr < 4 * KK) return WTC_ESHAPE;
+    a.dsub = std::max(1, nthr / (4 * k));
     a.wts_off = NP * slot;
     a.P = partial_len(k, a.Lm);
     // reduction scratch reuses the plane slots after the last plane
     a.red_off = 0;
-    const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * KK * a.dsub;
+    const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * k * a.dsub * k;
     size_t lds_floats = (size_t)std::max(NP * slot + wts_n, bwd ? red_n : 0);
     p->lds = lds_floats * 4;
     if (p->lds > kLdsLimit) return WTC_ESHAPE;

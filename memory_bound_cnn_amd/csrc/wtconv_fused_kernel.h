@@ -307,7 +307,7 @@ struct CtGeom {
     __device__ static constexpr int tail_off() { return lay.tail_off; }
     __device__ static constexpr int wts_off() { return NPV * lay.slot; }
     __device__ static constexpr int red_off() { return 0; }
-    __device__ static constexpr int dsub() { return NTHR / (4 * K * K) > 0 ? NTHR / (4 * K * K) : 1; }
+    __device__ static constexpr int dsub() { return NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1; }
     __device__ static constexpr int P() { return partial_len(K, LM); }
 };
 
@@ -439,17 +439,20 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
         for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KK + (KK >> 1)];
 
     // ---- persistent backward accumulators ----
-    float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm];
+    float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm - 2][K];
 #pragma unroll
     for (int i = 0; i < KK; ++i) corr0[i] = corr1[i] = corr2[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxLm; ++i) cdeep[i] = 0.f;
+    for (int q = 0; q < kMaxLm - 2; ++q)
+#pragma unroll
+        for (int kx = 0; kx < K; ++kx) cdeep[q][kx] = 0.f;
     float sumg = 0.f, tailc = 0.f;
-    // deep-level correlation role: subband du, tap dtap, position subset dsb
+    // deep-level (>= 3) correlation role: subband du, kernel row dky, band rows
+    // dsb, dsb + dsub, ...; one accumulator per kernel column
     const int drole = tid;
-    const bool dactive = BWD && drole < 4 * KK * g.dsub();
-    const int du = drole & 3, dtap = (drole >> 2) % KK, dsb = (drole >> 2) / KK;
-    const int ddy = dtap / K - R, ddx = dtap % K - R;
+    const int droles = 4 * K * g.dsub();
+    const bool dactive = BWD && drole < droles;
+    const int du = drole & 3, dky = (drole >> 2) % K, dsb = (drole >> 2) / K;
 
     const ST* srcp = reinterpret_cast<const ST*>(a.src);
     const ST* auxp = reinterpret_cast<const ST*>(a.aux);
@@ -767,30 +770,39 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                 Sl[g.yd_off(i) + u * hi * wi + j] = accv;
             }
             if constexpr (BWD) {
-                // output-stationary correlation: C_i^du[d] over this role's positions
+                // C_i^du[ky][kx] = sum_m X[m] G[m - (ky - R, kx - R)] (G with its zero
+                // halo): this role takes kernel row dky and its band rows; a chunk of
+                // 4 X values and 4 + 2R values of one G row serve all K columns.
                 if (dactive) {
-                    float cv = 0.f;
+                    float cv[K];
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) cv[kx] = 0.f;
                     for (int s2 = 0; s2 < g.NP(); ++s2) {
                         if (bb + s2 >= b_end) break;
                         const float* Sl = lds + s2 * g.slot();
-                        const float* XB = Sl + g.xb_off(i) + du * hi * wi;
-                        const float* Gb = Sl + g.b_off(i) + du * bs;
-                        // positions m = dsb, dsb + dsub, ... walked as (row, col) without division
-                        int my = fdiv(dsb, dwi), mx = dsb - my * wi;
-                        const int stepy = fdiv(g.dsub(), dwi), stepx = g.dsub() - stepy * wi;
-                        for (int m = dsb; m < hi * wi; m += g.dsub()) {
-                            cv = fmaf(XB[m], Gb[(my - ddy + R) * Si + (mx - ddx + R)], cv);
-                            mx += stepx;
-                            my += stepy;
-                            if (mx >= wi) {
-                                mx -= wi;
-                                ++my;
+                        for (int my = dsb; my < hi; my += g.dsub()) {
+                            const float* XR = Sl + g.xb_off(i) + du * hi * wi + my * wi;
+                            const float* GR = Sl + g.b_off(i) + du * bs + (my - dky + 2 * R) * Si;
+#pragma unroll
+                            for (int mx0 = 0; mx0 < wi; mx0 += 4) {
+                                float xv[4], gv[4 + 2 * R];
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) xv[q] = (mx0 + q < wi) ? XR[mx0 + q] : 0.f;
+#pragma unroll
+                                for (int q = 0; q < 4 + 2 * R; ++q)
+                                    gv[q] = (mx0 + q < wi + 2 * R) ? GR[mx0 + q] : 0.f;
+#pragma unroll
+                                for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                                    for (int q = 0; q < 4; ++q) cv[kx] = fmaf(xv[q], gv[q + 2 * R - kx], cv[kx]);
                             }
                         }
                     }
 #pragma unroll
-                    for (int q = 0; q < kMaxLm; ++q)
-                        if (q == i - 3) cdeep[q] += cv;
+                    for (int q = 0; q < kMaxLm - 2; ++q)
+                        if (q == i - 3)
+#pragma unroll
+                            for (int kx = 0; kx < K; ++kx) cdeep[q][kx] += cv[kx];
                 }
             }
         }
@@ -920,8 +932,13 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
             }
         }
         float* dred = red + nw * WR;   // deep: [q][role]
-        if (dactive)
-            for (int q = 0; q + 3 <= Lm; ++q) dred[q * 4 * KK * g.dsub() + drole] = cdeep[q];
+        if (dactive) {
+#pragma unroll
+            for (int q = 0; q < kMaxLm - 2; ++q)
+                if (q + 3 <= Lm)
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) dred[(q * droles + drole) * K + kx] = cdeep[q][kx];
+        }
         lds_barrier();
         float* rec = a.partials + ((size_t)blockIdx.x * 2 + seg) * g.P();
         for (int e = tid; e < g.P(); e += nthr) {
@@ -935,9 +952,9 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                     const int base = (lvl == 1) ? KK : 5 * KK;
                     for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + base + rem];
                 } else {
-                    const int u = rem / KK, tap = rem - u * KK;
+                    const int u = rem / KK, tap = rem - u * KK, ky = tap / K, kx = tap - ky * K;
                     for (int sb = 0; sb < g.dsub(); ++sb)
-                        v += dred[(lvl - 3) * 4 * KK * g.dsub() + (sb * KK + tap) * 4 + u];
+                        v += dred[((lvl - 3) * droles + (sb * K + ky) * 4 + u) * K + kx];
                 }
             } else if (e == g.P() - 2) {
                 for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + 9 * KK];
