@@ -13,12 +13,17 @@ constexpr int kMaxLm = 7;   // levels evaluated on a grid larger than 1x1 (plane
 constexpr int kMaxK = 7;
 
 // LDS layout of one plane slot (all offsets and sizes in floats).
-// Order: [level-1 .. level-early bands][level-0 plane | later arrays][tail].
-// Arrays first written after the level-0 phase (deeper bands, deep conv
-// results, x bands) may overlap the level-0 plane ("overlap").
+// Without band overlap: [level-1 .. level-early bands][level-0 plane | later
+// arrays][tail]; arrays first written after the level-0 phase (deeper bands,
+// deep conv results, x bands) may overlap the level-0 plane ("overlap").
+// With band overlap from level f ("bovl" = f >= 1): [bands of levels < f][bands
+// of levels >= f and the later arrays, over the level-0 plane][tail]; the early
+// bands of levels >= f are then written only after the whole workgroup is done
+// reading the level-0 plane, and their rings are re-zeroed per plane.
 struct Layout {
     int early_lv;      // levels analysed in registers during the level-0 phase (<= 3)
     int overlap;       // later arrays overlap the level-0 plane (rings re-zeroed per plane)
+    int bovl;          // first level whose bands overlap the level-0 plane (0: none)
     int slot;          // floats per plane slot
     int a0_off, a0_S, a0_rows;                 // level-0 plane with halo k/2
     int b_off[kMaxLm + 1], b_S[kMaxLm + 1];    // level-i raw bands with halo k/2
@@ -32,7 +37,7 @@ constexpr int lay_round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 // The one definition of the slot layout, evaluated on the host for the
 // runtime-geometry kernel and at compile time for the fixed-geometry ones.
-constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd) {
+constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd, int bovl) {
     Layout L{};
     const int R = k / 2;
     L.early_lv = Lm < early_req ? Lm : early_req;
@@ -42,6 +47,34 @@ constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool 
         L.b_S[i] = lay_round_up((Wq >> i) + 2 * R, 4);
         // band stride = 8 (mod 32) floats: the four subbands start in different LDS banks
         L.b_bs[i] = lay_round_up(L.b_rows[i] * L.b_S[i], 32) + 8;
+    }
+    if (bovl >= 1 && bovl <= Lm) {
+        L.bovl = bovl;
+        L.overlap = 1;
+        for (int i = 1; i < bovl; ++i) {
+            L.b_off[i] = off;
+            off += lay_round_up(4 * L.b_bs[i], 4);
+        }
+        const int base = off;
+        for (int i = bovl; i <= Lm; ++i) {
+            L.b_off[i] = off;
+            off += lay_round_up(4 * L.b_bs[i], 4);
+        }
+        for (int i = 3; i <= Lm; ++i) {
+            L.yd_off[i] = off;
+            off += lay_round_up(4 * (Hq >> i) * (Wq >> i), 4);
+            if (bwd) {
+                L.xb_off[i] = off;
+                off += lay_round_up(4 * (Hq >> i) * (Wq >> i), 4);
+            }
+        }
+        L.a0_off = base;
+        L.a0_rows = Hq + 2 * R;
+        L.a0_S = lay_round_up(Wq + 2 * R, 4);
+        const int a0_size = lay_round_up(L.a0_rows * L.a0_S, 4);
+        L.tail_off = off > base + a0_size ? off : base + a0_size;
+        L.slot = lay_round_up(L.tail_off + 4, 4);
+        return L;
     }
     for (int i = 1; i <= L.early_lv; ++i) {
         L.b_off[i] = off;

@@ -11,7 +11,6 @@ namespace wtc {
 namespace {
 
 constexpr size_t kLdsLimit = 160 * 1024;       // gfx950 LDS per workgroup
-constexpr size_t kMultiPlaneBudget = 64 * 1024; // small planes: leave room for >= 2 workgroups / CU
 constexpr int kComputeUnits = 256;             // MI355X
 
 int ceil_log2(int v) {
@@ -54,44 +53,69 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.nqx = a.Wq / 8;
     a.qpp = (a.Hq / 8) * a.nqx;
     a.vec = (d->W % 4 == 0) ? 1 : 0;
-    // levels 2 and 3 are analysed in registers when their bands fit beside the
-    // level-0 plane; otherwise (large planes) in flat loops after it
+    // Launch plan: the LDS layout (levels 2 and 3 analysed in registers when
+    // their bands fit; bands beside the level-0 plane, or from level 1 or 2
+    // over it), planes per workgroup and threads.  Chosen to maximise the
+    // lanes doing work per CU (resident workgroups are limited by LDS and by
+    // registers: the kernels are compiled for 3 waves per SIMD forward, 2
+    // backward or with two blocks per quad); on a tie the plan without band
+    // overlap (one barrier less per plane), then overlap from level 2, then
+    // the smaller workgroup.  Overlapping bands must have their zero rings
+    // rewritten for every plane; the forward pass, with half the arithmetic
+    // per pixel of the backward, only overlaps when those ring cells are at
+    // most as many as the plane's pixels.
     const int wts_n = round_up(KK * (1 + 4 * d->L) + 4, 4);
-    a.lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd);
-    if ((size_t)(a.lay.slot + wts_n) * 4 > kLdsLimit) a.lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd);
-    const int slot = a.lay.slot;
-
-    int nthr, bpq = 1, NP = 1;
-    if (a.qpp <= 64) {
-        // several planes per workgroup when planes are small; pick the plane
-        // count (within the LDS budget) that leaves the fewest idle lanes
-        int np_fit = 64 / a.qpp;
-        while (np_fit > 1 && (size_t)(np_fit * slot + wts_n) * 4 > kMultiPlaneBudget) --np_fit;
-        double best = 2.0;
-        for (int np = np_fit; np >= std::max(1, np_fit / 2); --np) {
-            int nt = round_up(4 * a.qpp * np, 64);
-            const double idle = 1.0 - (double)(4 * a.qpp * np) / nt;
-            if (idle < best - 1e-9) {
-                best = idle;
-                NP = np;
-            }
+    const int per_units = a.vec ? d->H * (d->W / 4) : d->H * d->W;
+    struct Cand {
+        Layout lay;
+        int NP, nthr, bpq, wgs;
+        long score;
+    };
+    Cand best{};
+    best.score = -1;
+    auto consider = [&](const Layout& lay, int NP, int nthr, int bpq) {
+        const int dsub = std::max(1, nthr / (4 * k));
+        const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * k * dsub * k;
+        const size_t lds = (size_t)std::max(NP * lay.slot + wts_n, bwd ? red_n : 0) * 4;
+        if (lds > kLdsLimit || NP * per_units >= 65536) return;   // fast in-kernel division range
+        const int wpe = (bwd || bpq > 1) ? 2 : 3;
+        const int lds_wgs = (int)(kLdsLimit / lds);
+        const int reg_wgs = std::max(1, 4 * wpe / (nthr / 64));
+        const int wgs = std::max(1, std::min(lds_wgs, reg_wgs));
+        const long score = (long)wgs * std::min(nthr, 4 * a.qpp * NP / bpq);
+        const bool better = score > best.score ||
+                            (score == best.score && best.lay.bovl == lay.bovl && nthr < best.nthr);
+        if (better) best = Cand{lay, NP, nthr, bpq, wgs, score};
+    };
+    if (a.qpp > 256) return WTC_ESHAPE;
+    for (const int bovl : {0, 2, 1}) {
+        if (bovl > a.Lm) continue;
+        Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl);
+        if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl);
+        if (bovl > 0 && !bwd) {
+            long ring = (long)lay.a0_rows * lay.a0_S - (long)d->H * d->W;
+            for (int i = bovl; i <= a.Lm; ++i)
+                ring += 4L * ((long)lay.b_rows[i] * lay.b_S[i] - (long)(a.Hq >> i) * (a.Wq >> i));
+            if (ring > (long)a.Hq * a.Wq) continue;
         }
-        nthr = round_up(4 * a.qpp * NP, 64);
-    } else if (a.qpp <= 128) {
-        nthr = 512;
-    } else if (a.qpp <= 256) {
-        nthr = 512;
-        bpq = 2;
-    } else {
-        return WTC_ESHAPE;
+        if (a.qpp <= 64) {
+            // several planes per workgroup when planes are small
+            for (int np = 1; np <= 64 / a.qpp; ++np) consider(lay, np, round_up(4 * a.qpp * np, 64), 1);
+        } else if (a.qpp <= 128) {
+            consider(lay, 1, 512, 1);
+        } else {
+            consider(lay, 1, 512, 2);
+        }
     }
+    if (best.score < 0) return WTC_ESHAPE;
+    a.lay = best.lay;
+    const int slot = a.lay.slot;
+    const int NP = best.NP, nthr = best.nthr, bpq = best.bpq;
     a.NP = NP;
     {
         // prefetch when every thread's share of a plane group fits 16 floats
-        const int per = a.vec ? d->H * (d->W / 4) : d->H * d->W;
-        const int units = cdiv(NP * per, nthr);
+        const int units = cdiv(NP * per_units, nthr);
         a.pf_on = (units * (a.vec ? 4 : 1) <= 16) ? 1 : 0;
-        if (NP * per >= 65536) return WTC_ESHAPE;   // fast in-kernel index division range
     }
     a.dsub = std::max(1, nthr / (4 * k));
     a.wts_off = NP * slot;
@@ -104,13 +128,8 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     if (p->lds > kLdsLimit) return WTC_ESHAPE;
 
     // Work split over the batch: one resident "wave" of workgroups over the
-    // whole chip, each walking a chunk of planes of one channel.  Resident
-    // workgroups per CU: LDS-limited, and register-limited to about 4 (forward)
-    // or 2 (backward) waves per SIMD.
-    const int waves_per_wg = nthr / 64;
-    const int lds_wgs = (int)std::max<size_t>(1, kLdsLimit / std::max<size_t>(p->lds, 1));
-    const int reg_wgs = std::max(1, (4 * (bwd ? 2 : 4)) / waves_per_wg);
-    const int wgs_per_cu = std::max(1, std::min(lds_wgs, reg_wgs));
+    // whole chip, each walking a chunk of planes of one channel.
+    const int wgs_per_cu = best.wgs;
     const long qtot = (long)d->B * d->C;
     const long slots = (long)kComputeUnits * wgs_per_cu;
     long ppw = (qtot + slots - 1) / slots;

@@ -139,6 +139,15 @@ __device__ void zero_ring(float* base, int rows, int S, int r0, int h, int c0, i
     }
 }
 
+// Zero the rings of `na` arrays in every plane slot (array j of a slot at
+// off + j * astride; rows x S floats, interior [R, R+h) x [R, R+w)), one work
+// item per array row: a halo row is cleared whole with 16-byte stores, an
+// interior row only left and right of the interior.  Rows start 16-byte
+// aligned (slot, offsets, strides and S are multiples of 4 floats).
+template <int R, class G>
+__device__ __forceinline__ void zero_rings(float* lds, const G& g, int off, int astride, int na, int rows, int S, int h, int w,
+                           int tid, int nthr);
+
 // Integer division of 0 <= e < 2^16 by a loop-invariant 1 <= d <= 4096 with a
 // biased float reciprocal (exact in that range: checked exhaustively on the
 // host, including a reciprocal one ulp off).  Three full-rate VALU ops instead
@@ -154,6 +163,25 @@ __device__ __forceinline__ FastDiv make_div(int d) {
     return f;
 }
 __device__ __forceinline__ int fdiv(int e, const FastDiv& f) { return (int)((float)e * f.r); }
+
+template <int R, class G>
+__device__ __forceinline__ void zero_rings(float* lds, const G& g, int off, int astride, int na, int rows, int S, int h, int w,
+                           int tid, int nthr) {
+    const int per_slot = na * rows;
+    const FastDiv dps = make_div(per_slot), drows = make_div(rows);
+    for (int e = tid; e < g.NP() * per_slot; e += nthr) {
+        const int s2 = fdiv(e, dps), rem = e - s2 * per_slot;
+        const int j = fdiv(rem, drows), r = rem - j * rows;
+        float* row = lds + s2 * g.slot() + off + j * astride + r * S;
+        if (r < R || r >= R + h) {
+            for (int c = 0; c < S; c += 4) *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+        } else {
+#pragma unroll
+            for (int c = 0; c < R; ++c) row[c] = 0.f;
+            for (int c = R + w; c < S; ++c) row[c] = 0.f;
+        }
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Register-blocked stencil: OH x OW outputs from an (OH+K-1) x (OW+K-1) LDS
@@ -263,6 +291,7 @@ struct RtGeom {
     __device__ int nqx() const { return a.nqx; }
     __device__ int nthr() const { return blockDim.x; }
     __device__ bool ovl() const { return a.lay.overlap != 0; }
+    __device__ int bovl() const { return a.lay.bovl; }
     __device__ int slot() const { return a.lay.slot; }
     __device__ int a0_off() const { return a.lay.a0_off; }
     __device__ int a0_S() const { return a.lay.a0_S; }
@@ -280,9 +309,9 @@ struct RtGeom {
     __device__ int P() const { return a.P; }
 };
 
-template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL>
+template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL>
 struct CtGeom {
-    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL);
+    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL);
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -294,6 +323,7 @@ struct CtGeom {
     __device__ static constexpr int nqx() { return WQ / 8; }
     __device__ static constexpr int nthr() { return NTHR; }
     __device__ static constexpr bool ovl() { return lay.overlap != 0; }
+    __device__ static constexpr int bovl() { return lay.bovl; }
     __device__ static constexpr int slot() { return lay.slot; }
     __device__ static constexpr int a0_off() { return lay.a0_off; }
     __device__ static constexpr int a0_S() { return lay.a0_S; }
@@ -344,7 +374,7 @@ __device__ __forceinline__ void haar4(float a, float b, float c, float d, float 
 }
 
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD || BPQ > 1) ? 2 : 4))) wtc_fused_kernel(const FusedArgs a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD || BPQ > 1) ? 2 : 3))) wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
     constexpr int PFF = 16;                     // prefetch capacity, floats per thread
     constexpr int PFU = VEC ? PFF / 4 : PFF;    // prefetch units (4-pixel groups or pixels)
@@ -529,15 +559,45 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                 }
             }
         }
-        if (g.ovl())
+        if (g.bovl() > 0) {
+            zero_rings<R>(lds, g, g.a0_off(), 0, 1, g.a0_rows(), g.a0_S(), a.H, a.W, tid, nthr);
+        } else if (g.ovl()) {
             for (int s2 = 0; s2 < g.NP(); ++s2)
                 zero_ring(lds + s2 * g.slot() + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
+        }
         lds_barrier();
         // the next planes' loads fly while this plane is computed
         if (pf_on && bb + g.NP() < b_end) pf_issue(bb + g.NP());
 
         // ---------------- phase 2: base conv; analysis of levels 1..3 ----------------
         float acc[BPQ][4][4];
+        // raw bands of this lane's block: level 1 at its 2x2 positions [jy][jx][u],
+        // level 2 at its position [u], level 3 (band t) at the quad's position
+        float hv1[BPQ][2][2][4], hv2[BPQ][4], hv3[BPQ];
+        // write the early bands of levels lo..hi of block s
+        auto put_bands = [&](int s, int lo, int hi) {
+            const int qy = qyv[s], qx = qxv[s];
+            const int py0 = 8 * qy + 4 * sy, px0 = 8 * qx + 4 * sx;
+            if (lo <= 1 && 1 <= hi) {
+                float* B1 = S + g.b_off(1);
+#pragma unroll
+                for (int jy = 0; jy < 2; ++jy)
+#pragma unroll
+                    for (int jx = 0; jx < 2; ++jx) {
+                        const int off = (py0 / 2 + jy + R) * g.b_S(1) + (px0 / 2 + jx + R);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) B1[u * g.b_bs(1) + off] = hv1[s][jy][jx][u];
+                    }
+            }
+            if (g.early() >= 2 && lo <= 2 && 2 <= hi) {
+                float* B2 = S + g.b_off(2);
+                const int off2 = (2 * qy + sy + R) * g.b_S(2) + 2 * qx + sx + R;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) B2[u * g.b_bs(2) + off2] = hv2[s][u];
+            }
+            if (g.early() >= 3 && lo <= 3 && 3 <= hi)
+                S[g.b_off(3) + t * g.b_bs(3) + (qy + R) * g.b_S(3) + qx + R] = hv3[s];
+        };
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
             if (!(pok && qok[s])) continue;
@@ -573,37 +633,30 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                     for (int j = 0; j < 4; ++j) sumg += ctr[i][j];
             }
             if (Lm >= 1) {
-                float ll1[2][2];
-                float* B1 = S + g.b_off(1);
-                const int S1 = g.b_S(1), bs1 = g.b_bs(1);
 #pragma unroll
                 for (int jy = 0; jy < 2; ++jy)
 #pragma unroll
                     for (int jx = 0; jx < 2; ++jx) {
-                        float r[4];
                         haar4(ctr[2 * jy][2 * jx], ctr[2 * jy][2 * jx + 1], ctr[2 * jy + 1][2 * jx],
-                              ctr[2 * jy + 1][2 * jx + 1], r);
-                        const int off = (py0 / 2 + jy + R) * S1 + (px0 / 2 + jx + R);
+                              ctr[2 * jy + 1][2 * jx + 1], hv1[s][jy][jx]);
+                        if (g.bovl() != 1) {   // level 1 is not over the level-0 plane: write at once
+                            const int off = (py0 / 2 + jy + R) * g.b_S(1) + (px0 / 2 + jx + R);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) B1[u * bs1 + off] = r[u];
-                        ll1[jy][jx] = r[0];
+                            for (int u = 0; u < 4; ++u) S[g.b_off(1) + u * g.b_bs(1) + off] = hv1[s][jy][jx][u];
+                        }
                     }
                 if (g.early() >= 2) {
                     // this lane's 4x4 block is one level-2 position
-                    float r2[4];
-                    haar4(ll1[0][0], ll1[0][1], ll1[1][0], ll1[1][1], r2);
-                    float* B2 = S + g.b_off(2);
-                    const int off2 = (2 * qy + sy + R) * g.b_S(2) + 2 * qx + sx + R;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) B2[u * g.b_bs(2) + off2] = r2[u];
+                    haar4(hv1[s][0][0][0], hv1[s][0][1][0], hv1[s][1][0][0], hv1[s][1][1][0], hv2[s]);
+                    if (g.bovl() == 0 || g.bovl() > 2) put_bands(s, 2, 2);
                     if (g.early() >= 3) {
                         // the quad's 8x8 block is one level-3 position: lane t
-                        // gathers the quad's four level-2 LL values, writes band t
+                        // gathers the quad's four level-2 LL values, keeps band t
                         const int qb = (tid & 63) & ~3;
-                        const float l0 = __shfl(r2[0], qb + 0, 64), l1 = __shfl(r2[0], qb + 1, 64);
-                        const float l2 = __shfl(r2[0], qb + 2, 64), l3 = __shfl(r2[0], qb + 3, 64);
-                        const float b3 = fmaf(sgy, fmaf(sgx, l3, l2), fmaf(sgx, l1, l0));
-                        S[g.b_off(3) + t * g.b_bs(3) + (qy + R) * g.b_S(3) + qx + R] = b3;
+                        const float l0 = __shfl(hv2[s][0], qb + 0, 64), l1 = __shfl(hv2[s][0], qb + 1, 64);
+                        const float l2 = __shfl(hv2[s][0], qb + 2, 64), l3 = __shfl(hv2[s][0], qb + 3, 64);
+                        hv3[s] = fmaf(sgy, fmaf(sgx, l3, l2), fmaf(sgx, l1, l0));
+                        if (g.bovl() == 0 || g.bovl() > 3) put_bands(s, 3, 3);
                     }
                 }
             } else if (tail && py0 == 0 && px0 == 0) {
@@ -611,6 +664,17 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                 S[g.tail_off()] = ctr[0][0] * kappa;
                 if constexpr (BWD) tailc = fmaf(ctr[0][0], xo[0][0], tailc);
             }
+        }
+        if (g.bovl() >= 1 && g.bovl() <= Lm) {
+            // these bands live over the level-0 plane: write them once every wave
+            // is done reading it, and restore the zero rings the plane covered
+            lds_barrier();
+#pragma unroll
+            for (int s = 0; s < BPQ; ++s)
+                if (pok && qok[s]) put_bands(s, g.bovl(), 3);
+            for (int i = g.bovl(); i <= Lm; ++i)
+                zero_rings<R>(lds, g, g.b_off(i), g.b_bs(i), 4, g.b_rows(i), g.b_S(i), g.Hq() >> i, g.Wq() >> i, tid,
+                              nthr);
         }
         lds_barrier();
 
@@ -632,11 +696,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
 #pragma unroll
                 for (int u = 0; u < 4; ++u) Bi[u * bs] = r[u];
             }
-            if (g.ovl())  // this level lives where the level-0 plane was staged
-                for (int s2 = 0; s2 < g.NP(); ++s2)
-                    for (int u = 0; u < 4; ++u)
-                        zero_ring(lds + s2 * g.slot() + g.b_off(i) + u * bs, g.b_rows(i), Si, R, hi,
-                                  R, wi, tid, nthr);
+            if (g.ovl() && g.bovl() == 0)  // this level lives where the level-0 plane was staged
+                zero_rings<R>(lds, g, g.b_off(i), bs, 4, g.b_rows(i), Si, hi, wi, tid, nthr);
             lds_barrier();
         }
 
@@ -1009,14 +1070,14 @@ namespace fused_detail {
 
 // Launch the fixed-geometry instantiation if the plan matches it exactly.
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
-          int NTHR>
+          int NTHR, int BOVL>
 bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
                 hipError_t* err) {
     if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
-        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC)
+        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL)
         return false;
-    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD>>(a, nthr, lds,
-                                                                                    grid, st);
+    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL>>(a, nthr, lds,
+                                                                                          grid, st);
     return true;
 }
 

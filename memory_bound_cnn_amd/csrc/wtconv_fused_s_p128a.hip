@@ -12,13 +12,13 @@ bool launch_fused_static_p128a(const FusedArgs& a, int dtype, int bwd, int bpq, 
     hipError_t e = hipSuccess;
     bool hit = false;
     if (!hit && dtype == WTC_FP32 && bwd == 0)
-        hit = try_static<5, float, 0, 2, true, 128, 128, 1, 1, 1, 512>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 0, 2, true, 128, 128, 1, 1, 1, 512, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
-        hit = try_static<5, float, 1, 2, true, 128, 128, 1, 1, 1, 512>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 1, 2, true, 128, 128, 1, 1, 1, 512, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 0)
-        hit = try_static<5, float, 0, 2, true, 128, 128, 2, 1, 1, 512>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 0, 2, true, 128, 128, 2, 1, 1, 512, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
-        hit = try_static<5, float, 1, 2, true, 128, 128, 2, 1, 1, 512>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 1, 2, true, 128, 128, 2, 1, 1, 512, 0>(a, bpq, nthr, lds, grid, st, &e);
     *err = (int)e;
     return hit;
 }

@@ -12,13 +12,13 @@ bool launch_fused_static_small(const FusedArgs& a, int dtype, int bwd, int bpq, 
     hipError_t e = hipSuccess;
     bool hit = false;
     if (!hit && dtype == WTC_FP32 && bwd == 0)
-        hit = try_static<5, float, 0, 1, false, 16, 16, 2, 2, 8, 128>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 0, 1, false, 16, 16, 2, 2, 4, 64, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
-        hit = try_static<5, float, 1, 1, false, 16, 16, 2, 2, 8, 128>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 1, 1, false, 16, 16, 2, 2, 4, 64, 2>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 0)
-        hit = try_static<5, float, 0, 1, false, 8, 8, 1, 1, 32, 128>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 0, 1, false, 8, 8, 1, 1, 31, 128, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
-        hit = try_static<5, float, 1, 1, false, 8, 8, 1, 1, 32, 128>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 1, 1, false, 8, 8, 1, 1, 16, 64, 1>(a, bpq, nthr, lds, grid, st, &e);
     *err = (int)e;
     return hit;
 }
