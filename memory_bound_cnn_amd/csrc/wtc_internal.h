@@ -149,6 +149,10 @@ struct FusedArgs {
     int P;             // partial record length (floats)
 };
 
+// Next-plane prefetch capacity in floats per thread: the forward kernel with
+// two blocks per quad (large planes) has the registers for a whole plane.
+constexpr int pf_capacity(bool bwd, int bpq) { return (!bwd && bpq > 1) ? 32 : 16; }
+
 // Partial record of one (workgroup, channel segment): [C_0 (k*k)] [levels 1..Lm: 4 bands x k*k]
 // [sum g] [tail correlation]; all correlations in natural tap order.
 constexpr int partial_len(int k, int Lm) { return k * k * (1 + 4 * Lm) + 2; }

@@ -113,9 +113,9 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     const int NP = best.NP, nthr = best.nthr, bpq = best.bpq;
     a.NP = NP;
     {
-        // prefetch when every thread's share of a plane group fits 16 floats
+        // prefetch when every thread's share of a plane group fits its capacity
         const int units = cdiv(NP * per_units, nthr);
-        a.pf_on = (units * (a.vec ? 4 : 1) <= 16) ? 1 : 0;
+        a.pf_on = (units * (a.vec ? 4 : 1) <= pf_capacity(bwd, bpq)) ? 1 : 0;
     }
     a.dsub = std::max(1, nthr / (4 * k));
     a.wts_off = NP * slot;

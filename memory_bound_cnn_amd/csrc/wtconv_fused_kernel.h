@@ -376,7 +376,7 @@ __device__ __forceinline__ void haar4(float a, float b, float c, float d, float 
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD || BPQ > 1) ? 2 : 3))) wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
-    constexpr int PFF = 16;                     // prefetch capacity, floats per thread
+    constexpr int PFF = pf_capacity(BWD, BPQ);  // prefetch capacity, floats per thread
     constexpr int PFU = VEC ? PFF / 4 : PFF;    // prefetch units (4-pixel groups or pixels)
     constexpr int UW = VEC ? 4 : 1;
     extern __shared__ __align__(16) float lds[];
