@@ -116,6 +116,8 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         // prefetch when every thread's share of a plane group fits its capacity
         const int units = cdiv(NP * per_units, nthr);
         a.pf_on = (units * (a.vec ? 4 : 1) <= pf_capacity(bwd, bpq)) ? 1 : 0;
+        // the kernel keeps unit offsets within a plane group in 32 bits
+        if ((long)NP * d->C * d->H * d->W >= (1L << 31)) a.pf_on = 0;
     }
     a.dsub = std::max(1, nthr / (4 * k));
     a.wts_off = NP * slot;

@@ -492,38 +492,67 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
     const int wv = VEC ? (a.W >> 2) : a.W;
     const int per = a.H * wv;
     const FastDiv dper = make_div(per), dwv = make_div(wv);
-    const bool pf_on = a.pf_on != 0;
+    // (the backward kernel with two blocks per quad never has the capacity)
+    const bool pf_on = !(BWD && BPQ > 1) && a.pf_on != 0;
     float pf[PFU][UW];
-    // issue the global loads of the NP planes starting at batch index bbn
-    auto pf_issue = [&](int bbn) {
+    // With 4-pixel units the decode of each unit is done once per segment: its
+    // offset within a plane group in device memory, and (packed) its plane
+    // slot (bits 16+) and LDS offset (bits 0-15; slots fit in 64K floats);
+    // -1 = no unit.  Single-pixel units decode on the fly (16 of them would
+    // take too many registers).
+    const int cplane = a.C * (int)plane_sz;   // < 2^31 / NP when prefetching
+    int pf_goff[VEC ? PFU : 1], pf_lds[VEC ? PFU : 1];
+    if (VEC && pf_on) {
 #pragma unroll
         for (int k = 0; k < PFU; ++k) {
             const int e = tid + k * nthr;
+            pf_goff[k] = 0;
+            pf_lds[k] = -1;
             if (e < g.NP() * per) {
                 const int s2 = fdiv(e, dper), m = e - s2 * per;
                 const int y = fdiv(m, dwv), xq = m - y * wv;
-                if (bbn + s2 < b_end) {
-                    const ST* pl = srcp + ((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)y * a.W + xq * UW;
-                    if constexpr (VEC) {
-                        load4(pl, pf[k]);
-                    } else {
-                        pf[k][0] = to_f32(pl[0]);
-                    }
+                pf_goff[k] = s2 * cplane + y * a.W + xq * UW;
+                pf_lds[k] = (s2 << 16) | (s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW);
+            }
+        }
+    }
+    // issue the global loads of the NP planes starting at batch index bbn
+    auto pf_issue = [&](int bbn) {
+        if constexpr (VEC) {
+            const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
+#pragma unroll
+            for (int k = 0; k < PFU; ++k)
+                if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) load4(base + pf_goff[k], pf[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < PFU; ++k) {
+                const int e = tid + k * nthr;
+                if (e < g.NP() * per) {
+                    const int s2 = fdiv(e, dper), m = e - s2 * per;
+                    const int y = fdiv(m, dwv), xq = m - y * wv;
+                    if (bbn + s2 < b_end)
+                        pf[k][0] = to_f32(srcp[((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)y * a.W + xq]);
                 }
             }
         }
     };
     auto pf_commit = [&](int bbn) {
+        if constexpr (VEC) {
 #pragma unroll
-        for (int k = 0; k < PFU; ++k) {
-            const int e = tid + k * nthr;
-            if (e < g.NP() * per) {
-                const int s2 = fdiv(e, dper), m = e - s2 * per;
-                const int y = fdiv(m, dwv), xq = m - y * wv;
-                if (bbn + s2 < b_end) {
-                    float* d = lds + s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW;
+            for (int k = 0; k < PFU; ++k)
+                if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) {
+                    float* d = lds + (pf_lds[k] & 0xFFFF);
 #pragma unroll
                     for (int i = 0; i < UW; ++i) d[i] = pf[k][i];
+                }
+        } else {
+#pragma unroll
+            for (int k = 0; k < PFU; ++k) {
+                const int e = tid + k * nthr;
+                if (e < g.NP() * per) {
+                    const int s2 = fdiv(e, dper), m = e - s2 * per;
+                    const int y = fdiv(m, dwv), xq = m - y * wv;
+                    if (bbn + s2 < b_end) lds[s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq] = pf[k][0];
                 }
             }
         }
