@@ -175,6 +175,12 @@ struct FinalizeArgs {
 int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nthr,
                  size_t lds_bytes, int grid, void* stream);
 int launch_finalize(const FinalizeArgs& f, void* stream);
+// Register-resident kernel for planes of at most 8 x 8 (k = 5, 1 <= L = Lm <= 2):
+// one 64-lane workgroup per ppw planes, same record layout as the plane pipeline.
+int launch_tiny(const FusedArgs& a, int dtype, int bwd, int grid, void* stream);
+constexpr bool tiny_supported(int k, int Hq, int Wq, int L, int Lm) {
+    return k == 5 && Hq == 8 && Wq == 8 && L == Lm && Lm >= 1 && Lm <= 2;
+}
 
 // ---------------------------------------------------------------------------
 // Unfused (level-by-level) baseline

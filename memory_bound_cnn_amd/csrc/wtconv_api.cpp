@@ -34,6 +34,7 @@ struct FusedPlan {
     FusedArgs a;
     int nthr, bpq, grid, nchunk;
     size_t lds;
+    int tiny;   // register-resident kernel for planes of at most 8 x 8
 };
 
 int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
@@ -53,6 +54,24 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.nqx = a.Wq / 8;
     a.qpp = (a.Hq / 8) * a.nqx;
     a.vec = (d->W % 4 == 0) ? 1 : 0;
+    p->tiny = 0;
+    if (tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm)) {
+        // one wave per workgroup, 16 planes per pass; one resident round of
+        // waves (registers allow 3 per SIMD forward, 2 backward)
+        p->tiny = 1;
+        a.P = partial_len(k, a.Lm);
+        const long qtot = (long)d->B * d->C;
+        const long slots = (long)kComputeUnits * 4 * (bwd ? 2 : 3);
+        long ppw = (qtot + slots - 1) / slots;
+        ppw = (ppw + 15) / 16 * 16;
+        ppw = std::min<long>(ppw, d->B);
+        a.ppw = (int)std::max<long>(1, ppw);
+        p->grid = p->nchunk = (int)((qtot + a.ppw - 1) / a.ppw);
+        p->nthr = 64;
+        p->bpq = 1;
+        p->lds = 0;
+        return WTC_OK;
+    }
     // Launch plan: the LDS layout (levels 2 and 3 analysed in registers when
     // their bands fit; bands beside the level-0 plane, or from level 1 or 2
     // over it), planes per workgroup and threads.  Chosen to maximise the
@@ -197,7 +216,8 @@ int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const floa
     a.w0 = w0; a.s0 = s0; a.b0 = b0; a.wl = wl; a.sl = sl;
     a.dst = out;
     a.partials = nullptr;
-    const int e = launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
+    const int e = p.tiny ? launch_tiny(a, d->dtype, 0, p.grid, stream)
+                         : launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
     return e == 0 ? WTC_OK : WTC_EHIP;
 }
 
@@ -226,7 +246,8 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     a.w0 = w0; a.s0 = s0; a.b0 = nullptr; a.wl = wl; a.sl = sl;
     a.dst = dx;
     a.partials = static_cast<float*>(workspace);
-    int e = launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
+    int e = p.tiny ? launch_tiny(a, d->dtype, 1, p.grid, stream)
+                   : launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
     if (e != 0) return WTC_EHIP;
     FinalizeArgs f;
     f.partials = a.partials;

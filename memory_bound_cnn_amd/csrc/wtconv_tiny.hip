@@ -1,0 +1,446 @@
+// Register-resident WTConv for planes of at most 8 x 8 pixels (gfx950).
+//
+// Same operator and reformulations as the LDS plane pipeline (analysis
+// recomputed on chip, closed-form synthesis, scales and Haar factors folded
+// into the weights), organised for tiny planes: one quad of lanes holds one
+// plane zero-extended to 8 x 8, each lane a 4 x 4 quadrant.  Convolution
+// halos and subband exchanges travel between the four lanes of the quad by
+// DPP quad permutes, so the kernel uses no LDS and no barrier; a workgroup is
+// one wave, 16 planes in flight.
+//
+// Level 1 (4 x 4 grid) and level 2 (2 x 2 grid) use the band-per-lane scheme:
+// lane t gathers subband t over the whole grid in canonical order, convolves
+// it with its own folded weights (taps that fall outside the grid are skipped
+// at compile time) and, for the synthesis, hands every other lane the values
+// at that lane's positions.  Supported: k = 5, 1 <= L = Lm <= 2, H, W <= 8.
+#include <hip/hip_runtime.h>
+
+#include "wtc_internal.h"
+
+namespace wtc {
+namespace tiny {
+
+constexpr int K = 5, R = K / 2, KK = K * K;
+constexpr int WN = 4 + 2 * R;   // window side of a 4 x 4 block
+
+struct bf16v {
+    uint16_t bits;
+};
+__device__ __forceinline__ float ld(const float* p) { return *p; }
+__device__ __forceinline__ float ld(const bf16v* p) { return __uint_as_float(((uint32_t)p->bits) << 16); }
+__device__ __forceinline__ void st(float* p, float v) { *p = v; }
+__device__ __forceinline__ void st(bf16v* p, float v) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite values)
+    p->bits = (uint16_t)(u >> 16);
+}
+
+// Value of `v` in quad lane (lane ^ X); X = 0 is the lane itself.
+constexpr int quad_xor_ctrl(int x) {
+    // quad_perm selector: lane i of each quad reads lane sel[i]
+    return ((0 ^ x) << 0) | ((1 ^ x) << 2) | ((2 ^ x) << 4) | ((3 ^ x) << 6);
+}
+template <int X>
+__device__ __forceinline__ float qx(float v) {
+    if constexpr (X == 0) {
+        return v;
+    } else {
+        return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), quad_xor_ctrl(X), 0xF, 0xF, true));
+    }
+}
+
+// a[i] for a lane-dependent index 0 <= i < 4 (two selects on its bits)
+__device__ __forceinline__ float sel4(const float (&a)[4], int i) {
+    const float lo = (i & 1) ? a[1] : a[0];
+    const float hi = (i & 1) ? a[3] : a[2];
+    return (i & 2) ? hi : lo;
+}
+
+// Raw +-1 butterfly of a 2 x 2 block a=(0,0), b=(0,1), c=(1,0), d=(1,1).
+__device__ __forceinline__ void haar4(float a, float b, float c, float d, float (&r)[4]) {
+    const float s01 = a + b, d01 = a - b, s23 = c + d, d23 = c - d;
+    r[0] = s01 + s23;
+    r[1] = d01 + d23;
+    r[2] = s01 - s23;
+    r[3] = d01 - d23;
+}
+
+// Halo of this lane's 4 x 4 block of a plane held by the quad (block of lane t
+// at quadrant (t >> 1, t & 1)): the vertical partner (lane ^ 2) sends its R rows
+// next to us, the horizontal one (lane ^ 1) its R columns, the diagonal one
+// (lane ^ 3) its R x R corner.  Zero where the partner lies outside the plane.
+struct Halo {
+    float vr[R][4], hc[4][R], dg[R][R];
+};
+__device__ __forceinline__ void exchange_halo(const float (&X)[4][4], int sy, int sx, Halo& h) {
+    auto& vr = h.vr;
+    auto& hc = h.hc;
+    auto& dg = h.dg;
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vr[k][j] = qx<2>(sy ? X[k][j] : X[4 - R + k][j]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < R; ++k) hc[i][k] = qx<1>(sx ? X[i][k] : X[i][4 - R + k]);
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+        for (int l = 0; l < R; ++l) dg[k][l] = qx<3>(X[sy ? k : 4 - R + k][sx ? l : 4 - R + l]);
+    // keep only the halo that lies inside the plane: the partners' blocks are above
+    // (sy = 1) or below, left (sx = 1) or right; the other side is the plane border
+}
+
+// Row r of the (4 + 2R)^2 window around the lane's block (rows/cols -R .. 3+R).
+__device__ __forceinline__ void window_row(const float (&X)[4][4], const Halo& h, bool above, bool left, int r,
+                                           float (&row)[WN]) {
+    const int rb = r < R ? 0 : (r < R + 4 ? 1 : 2);   // 0 above, 1 own, 2 below
+    const int rr = rb == 0 ? r : (rb == 1 ? r - R : r - R - 4);
+#pragma unroll
+    for (int c = 0; c < WN; ++c) {
+        const int cb = c < R ? 0 : (c < R + 4 ? 1 : 2);
+        const int cc = cb == 0 ? c : (cb == 1 ? c - R : c - R - 4);
+        float v;
+        if (rb == 1 && cb == 1) {
+            v = X[rr][cc];
+        } else if (cb == 1) {
+            v = ((rb == 0) == above) ? h.vr[rr][cc] : 0.f;
+        } else if (rb == 1) {
+            v = ((cb == 0) == left) ? h.hc[rr][cc] : 0.f;
+        } else {
+            v = ((rb == 0) == above && (cb == 0) == left) ? h.dg[rr][cc] : 0.f;
+        }
+        row[c] = v;
+    }
+}
+
+// Gather subband t of the quad's N x N level grid in canonical order: lane q
+// holds bands[jy][jx][u] at its (N/2 x N/2) block (quadrant (q >> 1, q & 1)).
+template <int NB>   // block side (N = 2 NB)
+__device__ __forceinline__ void gather_band(const float (&bands)[NB][NB][4], int t, float (&G)[2 * NB][2 * NB]) {
+    float rv[4][NB][NB];
+#pragma unroll
+    for (int jy = 0; jy < NB; ++jy)
+#pragma unroll
+        for (int jx = 0; jx < NB; ++jx) {
+            // round r: the partner t ^ r receives its own band (t ^ r) of our block
+            rv[0][jy][jx] = sel4(bands[jy][jx], t);
+            rv[1][jy][jx] = qx<1>(sel4(bands[jy][jx], t ^ 1));
+            rv[2][jy][jx] = qx<2>(sel4(bands[jy][jx], t ^ 2));
+            rv[3][jy][jx] = qx<3>(sel4(bands[jy][jx], t ^ 3));
+        }
+    // block (Y, X) came from lane (Y, X), i.e. in round ((Y << 1) | X) ^ t
+#pragma unroll
+    for (int Y = 0; Y < 2; ++Y)
+#pragma unroll
+        for (int Xb = 0; Xb < 2; ++Xb)
+#pragma unroll
+            for (int jy = 0; jy < NB; ++jy)
+#pragma unroll
+                for (int jx = 0; jx < NB; ++jx) {
+                    const float c4[4] = {rv[0][jy][jx], rv[1][jy][jx], rv[2][jy][jx], rv[3][jy][jx]};
+                    G[Y * NB + jy][Xb * NB + jx] = sel4(c4, ((Y << 1) | Xb) ^ t);
+                }
+}
+
+// Depthwise K x K correlation on an N x N grid with zero padding, taps outside
+// the grid skipped at compile time.  CORR: also cr[ky][kx] += xs[y][x] g[y+ky-R][x+kx-R].
+template <int N, bool CORR>
+__device__ __forceinline__ void grid_conv(const float (&G)[N][N], const float (&w)[KK], float (&Y)[N][N],
+                                          const float (&xs)[N][N], float (&cr)[KK]) {
+#pragma unroll
+    for (int y = 0; y < N; ++y)
+#pragma unroll
+        for (int x = 0; x < N; ++x) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx) {
+                    const int gy = y + ky - R, gx = x + kx - R;
+                    if (gy < 0 || gy >= N || gx < 0 || gx >= N) continue;
+                    acc = fmaf(w[ky * K + kx], G[gy][gx], acc);
+                    if constexpr (CORR) cr[ky * K + kx] = fmaf(xs[y][x], G[gy][gx], cr[ky * K + kx]);
+                }
+            Y[y][x] = acc;
+        }
+}
+
+// Synthesis hand-over: lane t holds band t on the canonical N x N grid; every lane
+// receives, for each band u, the values at its own block and adds them with the
+// signs of the inverse butterfly: z[2jy+dy][2jx+dx] += (-1)^(u_y dy + u_x dx) Y^u[jy][jx]
+// (NB x NB positions per block, z is 2NB x 2NB).
+template <int NB>
+__device__ __forceinline__ void synth_band(const float (&Yc)[2 * NB][2 * NB], int t, float (&z)[2 * NB][2 * NB]) {
+    float rv[4][NB][NB];
+#pragma unroll
+    for (int jy = 0; jy < NB; ++jy)
+#pragma unroll
+        for (int jx = 0; jx < NB; ++jx) {
+            // round r: the partner p = t ^ r needs our band at its block (p >> 1, p & 1)
+            float blk[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) blk[b] = Yc[(b >> 1) * NB + jy][(b & 1) * NB + jx];
+            rv[0][jy][jx] = sel4(blk, t);
+            rv[1][jy][jx] = qx<1>(sel4(blk, t ^ 1));
+            rv[2][jy][jx] = qx<2>(sel4(blk, t ^ 2));
+            rv[3][jy][jx] = qx<3>(sel4(blk, t ^ 3));
+        }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int u = t ^ r;   // band received in round r
+        const float sgx = (u & 1) ? -1.f : 1.f, sgy = (u & 2) ? -1.f : 1.f, sgxy = sgx * sgy;
+#pragma unroll
+        for (int jy = 0; jy < NB; ++jy)
+#pragma unroll
+            for (int jx = 0; jx < NB; ++jx) {
+                const float v = rv[r][jy][jx];
+                z[2 * jy][2 * jx] += v;
+                z[2 * jy][2 * jx + 1] = fmaf(sgx, v, z[2 * jy][2 * jx + 1]);
+                z[2 * jy + 1][2 * jx] = fmaf(sgy, v, z[2 * jy + 1][2 * jx]);
+                z[2 * jy + 1][2 * jx + 1] = fmaf(sgxy, v, z[2 * jy + 1][2 * jx + 1]);
+            }
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v, int from) {
+    for (int m = from; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// The lane's 4 x 4 quadrant of a plane, zero outside H x W and everywhere when
+// !ok (a quad past the end of the batch; `plane` is then any valid plane).
+// Branch-free: an out-of-plane pixel loads the plane's first pixel and is then
+// replaced by 0.
+template <typename ST>
+__device__ __forceinline__ void load_quadrant(const ST* plane, int H, int W, int sy, int sx, bool ok,
+                                              float (&X)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int y = 4 * sy + i, x = 4 * sx + j;
+            const bool in = y < H && x < W;
+            const float v = ld(plane + (in ? y * W + x : 0));
+            X[i][j] = (in && ok) ? v : 0.f;
+        }
+}
+
+// Opaque copy: keeps the compiler from hoisting lane-dependent values out of
+// the plane loop (they are cheap to recompute, expensive to keep live).
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// One wave per workgroup: a range of ppw planes in channel-major order (at most
+// two channel segments); quad i takes planes i, i + 16, ... of a segment.
+template <typename ST, bool BWD, int LM>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BWD ? 2 : 3)))
+wtc_tiny_kernel(const FusedArgs a) {
+    // weights of the current channel: [base][level 1, bands 0..3][level 2, bands 0..3]
+    __shared__ float wsh[KK * 9];
+    const int lane = threadIdx.x;
+    const long qtot = (long)a.C * a.B;
+    const long q0 = (long)blockIdx.x * a.ppw, q1 = min(q0 + (long)a.ppw, qtot);
+    const int c_first = (int)(q0 / a.B);
+    const int HW = a.H * a.W;
+    const ST* srcp = reinterpret_cast<const ST*>(a.src);
+    const ST* auxp = reinterpret_cast<const ST*>(a.aux);
+    ST* dstp = reinterpret_cast<ST*>(a.dst);
+
+    for (int seg = 0; seg < 2; ++seg) {
+        const int c = c_first + seg;
+        const long qs = max(q0, (long)c * a.B), qe = min(q1, (long)(c + 1) * a.B);
+        if (qs >= qe) break;
+        const int b_begin = (int)(qs - (long)c * a.B), b_end = (int)(qe - (long)c * a.B);
+        // weights of this channel: base (unfolded, scale applied at the output), and
+        // each band of each level folded with its scale and 4^-i; rotated for the backward
+        __syncthreads();   // the previous segment is done with the table
+        for (int e = lane; e < KK * (1 + 4 * LM); e += 64) {
+            const int blk = e / KK, q = e - blk * KK, tap = BWD ? KK - 1 - q : q;
+            float v;
+            if (blk == 0) {
+                v = a.w0[(size_t)c * KK + tap];
+            } else {
+                const int i = (blk - 1) >> 2, u = (blk - 1) & 3;   // level i + 1, band u
+                const size_t pu = ((size_t)i * a.C + c) * 4 + u;
+                v = ldexpf(a.sl[pu], -2 * (i + 1)) * a.wl[pu * KK + tap];
+            }
+            wsh[e] = v;
+        }
+        __syncthreads();
+        const float s0 = a.s0[c];
+        const float bias = BWD ? 0.f : a.b0[c];
+        float corr0[KK], corr1[KK], corr2[KK];
+#pragma unroll
+        for (int q = 0; q < KK; ++q) corr0[q] = corr1[q] = corr2[q] = 0.f;
+        float sumg = 0.f;
+
+        for (int b0 = b_begin; b0 < b_end; b0 += 16) {
+            const int ln = opaque(lane);
+            const int t = ln & 3, quad = ln >> 2;
+            const int sy = t >> 1, sx = t & 1;
+            const int b = b0 + quad;
+            const bool ok = b < b_end;   // quad-uniform
+            const size_t poff = ((size_t)(ok ? b : b_begin) * a.C + c) * HW;   // a valid plane
+            float X[4][4];
+            load_quadrant(srcp + poff, a.H, a.W, sy, sx, ok, X);
+            float xs[4][4];
+            if constexpr (BWD) load_quadrant(auxp + poff, a.H, a.W, sy, sx, ok, xs);
+
+            // ---- base convolution (and correlation of x with g), one window row at a time ----
+            float acc[4][4];
+            {
+                Halo h;
+                exchange_halo(X, sy, sx, h);
+                float w0[KK];
+#pragma unroll
+                for (int q = 0; q < KK; ++q) w0[q] = wsh[q];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll
+                for (int r = 0; r < WN; ++r) {
+                    float row[WN];
+                    window_row(X, h, sy != 0, sx != 0, r, row);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int ky = r - i;
+                        if (ky < 0 || ky >= K) continue;
+#pragma unroll
+                        for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                acc[i][j] = fmaf(w0[ky * K + kx], row[j + kx], acc[i][j]);
+                                if constexpr (BWD)
+                                    corr0[ky * K + kx] = fmaf(xs[i][j], row[j + kx], corr0[ky * K + kx]);
+                            }
+                    }
+                }
+            }
+            if constexpr (BWD) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sumg += X[i][j];
+            }
+            // phase boundary: keeps the scheduler from overlapping the phases' live ranges
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- level 1: raw bands of this lane's 2 x 2 positions ----
+            float hv[2][2][4], hx[2][2][4];
+#pragma unroll
+            for (int jy = 0; jy < 2; ++jy)
+#pragma unroll
+                for (int jx = 0; jx < 2; ++jx) {
+                    haar4(X[2 * jy][2 * jx], X[2 * jy][2 * jx + 1], X[2 * jy + 1][2 * jx], X[2 * jy + 1][2 * jx + 1],
+                          hv[jy][jx]);
+                    if constexpr (BWD)
+                        haar4(xs[2 * jy][2 * jx], xs[2 * jy][2 * jx + 1], xs[2 * jy + 1][2 * jx],
+                              xs[2 * jy + 1][2 * jx + 1], hx[jy][jx]);
+                }
+            float G1[4][4], Y1[4][4], X1[4][4];
+            gather_band<2>(hv, t, G1);
+            if constexpr (BWD) gather_band<2>(hx, t, X1);
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                float w1[KK];
+#pragma unroll
+                for (int q = 0; q < KK; ++q) w1[q] = wsh[KK + t * KK + q];
+                grid_conv<4, BWD>(G1, w1, Y1, X1, corr1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            float z[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) z[i][j] = 0.f;
+
+            // ---- level 2 (this lane's block is one level-2 position) ----
+            if constexpr (LM >= 2) {
+                float h2[1][1][4], x2[1][1][4];
+                haar4(hv[0][0][0], hv[0][1][0], hv[1][0][0], hv[1][1][0], h2[0][0]);
+                if constexpr (BWD) haar4(hx[0][0][0], hx[0][1][0], hx[1][0][0], hx[1][1][0], x2[0][0]);
+                float G2[2][2], Y2[2][2], X2[2][2];
+                gather_band<1>(h2, t, G2);
+                if constexpr (BWD) gather_band<1>(x2, t, X2);
+                float w2[KK];
+#pragma unroll
+                for (int q = 0; q < KK; ++q) w2[q] = wsh[5 * KK + t * KK + q];
+                grid_conv<2, BWD>(G2, w2, Y2, X2, corr2);
+                // level-2 synthesis: the LL input of level 1 at this lane's 2 x 2 positions
+                float z2[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+                synth_band<1>(Y2, t, z2);
+                // enters the level-1 butterfly through band 0: +z2 at all four pixels
+#pragma unroll
+                for (int jy = 0; jy < 2; ++jy)
+#pragma unroll
+                    for (int jx = 0; jx < 2; ++jx)
+#pragma unroll
+                        for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+                            for (int dx = 0; dx < 2; ++dx) z[2 * jy + dy][2 * jx + dx] += z2[jy][jx];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- level-1 synthesis fused with the output ----
+            synth_band<2>(Y1, t, z);
+            if (ok) {
+                ST* op = dstp + poff;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int y = 4 * sy + i, x = 4 * sx + j;
+                        if (y < a.H && x < a.W) st(op + y * a.W + x, fmaf(s0, acc[i][j], bias + z[i][j]));
+                    }
+            }
+        }
+
+        if constexpr (BWD) {
+            // per-segment record: [C_0][level 1: 4 bands][level 2: 4 bands][sum g][tail = 0],
+            // correlations in weight-gradient tap order (accumulator q holds tap KK-1-q)
+            float* rec = a.partials + ((size_t)blockIdx.x * 2 + seg) * a.P;
+            const int t = lane & 3;
+#pragma unroll
+            for (int q = 0; q < KK; ++q) {
+                const float v0 = wave_sum(corr0[q], 1);
+                const float v1 = wave_sum(corr1[q], 4);
+                if (lane == 0) rec[KK - 1 - q] = v0;
+                if (lane < 4) rec[KK + lane * KK + (KK - 1 - q)] = v1;
+                if constexpr (LM >= 2) {
+                    const float v2 = wave_sum(corr2[q], 4);
+                    if (lane < 4) rec[5 * KK + lane * KK + (KK - 1 - q)] = v2;
+                }
+            }
+            const float vs = wave_sum(sumg, 1);
+            if (lane == 0) {
+                rec[a.P - 2] = vs;
+                rec[a.P - 1] = 0.f;
+            }
+        }
+    }
+}
+
+template <typename ST, bool BWD>
+hipError_t launch_dt(const FusedArgs& a, int grid, hipStream_t st) {
+    if (a.Lm == 1)
+        hipLaunchKernelGGL((wtc_tiny_kernel<ST, BWD, 1>), dim3(grid), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((wtc_tiny_kernel<ST, BWD, 2>), dim3(grid), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace tiny
+
+int launch_tiny(const FusedArgs& a, int dtype, int bwd, int grid, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    using namespace tiny;
+    if (dtype == WTC_BF16) return (int)(bwd ? launch_dt<bf16v, true>(a, grid, st) : launch_dt<bf16v, false>(a, grid, st));
+    return (int)(bwd ? launch_dt<float, true>(a, grid, st) : launch_dt<float, false>(a, grid, st));
+}
+
+}  // namespace wtc

@@ -65,6 +65,24 @@ def test_edge_cases(B, C, H, W, L, k, seed):
     _case(B, C, H, W, L, k, seed)
 
 
+# Planes of at most 8 x 8 with k = 5 and 1 <= L <= 2 take the register-resident
+# kernel (one quad of lanes per plane): full and partial quads, both levels,
+# unequal and tiny sides.
+TINY = [
+    (3, 5, 8, 8, 2, 5, 70, "fp32"),
+    (2, 3, 5, 7, 1, 5, 71, "fp32"),
+    (4, 6, 8, 3, 2, 5, 72, "fp32"),
+    (17, 2, 7, 7, 2, 5, 73, "fp32"),
+    (3, 4, 7, 7, 2, 5, 74, "bf16"),
+    (5, 3, 2, 2, 1, 5, 75, "fp32"),
+]
+
+
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", TINY)
+def test_tiny_planes(B, C, H, W, L, k, seed, dtype):
+    _case(B, C, H, W, L, k, seed, dtype)
+
+
 def test_bf16_odd_plane():
     _case(3, 4, 14, 14, 2, 5, 60, "bf16")
 
