@@ -55,7 +55,9 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.qpp = (a.Hq / 8) * a.nqx;
     a.vec = (d->W % 4 == 0) ? 1 : 0;
     p->tiny = 0;
-    if (tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm)) {
+    const long esize = d->dtype == WTC_BF16 ? 2 : 4;
+    if (tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm) &&
+        ((long)d->B + 16) * d->C * d->H * d->W * esize < (1L << 31)) {   // 32-bit buffer offsets
         // one wave per workgroup, 16 planes per pass; one resident round of
         // waves (registers allow 3 per SIMD forward, 2 backward)
         p->tiny = 1;

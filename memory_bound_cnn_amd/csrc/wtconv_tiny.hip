@@ -26,13 +26,30 @@ constexpr int WN = 4 + 2 * R;   // window side of a 4 x 4 block
 struct bf16v {
     uint16_t bits;
 };
-__device__ __forceinline__ float ld(const float* p) { return *p; }
-__device__ __forceinline__ float ld(const bf16v* p) { return __uint_as_float(((uint32_t)p->bits) << 16); }
-__device__ __forceinline__ void st(float* p, float v) { *p = v; }
-__device__ __forceinline__ void st(bf16v* p, float v) {
+
+// Plane I/O through raw buffer resources: the hardware range check returns 0 for
+// a load at or beyond `num_records` bytes and drops such a store, so every load
+// and store of a pass is issued unconditionally (a pixel outside the plane, or a
+// quad past the end of the batch, simply addresses beyond the range).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw 32-bit data format (gfx9)
+constexpr int kOutOfRange = 0x7FFFFFF0;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ float bload(rsrc_t r, int off, float*) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float bload(rsrc_t r, int off, bf16v*) {
+    return __uint_as_float(((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0)) << 16);
+}
+__device__ __forceinline__ void bstore(rsrc_t r, int off, float v, float*) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore(rsrc_t r, int off, float v, bf16v*) {
     uint32_t u = __float_as_uint(v);
     u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite values)
-    p->bits = (uint16_t)(u >> 16);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(u >> 16), r, off, 0, 0);
 }
 
 // Value of `v` in quad lane (lane ^ X); X = 0 is the lane itself.
@@ -209,22 +226,22 @@ __device__ __forceinline__ float wave_sum(float v, int from) {
     return v;
 }
 
-// The lane's 4 x 4 quadrant of a plane, zero outside H x W and everywhere when
-// !ok (a quad past the end of the batch; `plane` is then any valid plane).
-// Branch-free: an out-of-plane pixel loads the plane's first pixel and is then
-// replaced by 0.
+// Byte offset of pixel (i, j) of the lane's quadrant in a plane starting at
+// byte `pbyte` of the resource; out of range outside H x W.
 template <typename ST>
-__device__ __forceinline__ void load_quadrant(const ST* plane, int H, int W, int sy, int sx, bool ok,
-                                              float (&X)[4][4]) {
+__device__ __forceinline__ int pix_off(int pbyte, int H, int W, int sy, int sx, int i, int j) {
+    const int y = 4 * sy + i, x = 4 * sx + j;
+    return (y < H && x < W) ? pbyte + (y * W + x) * (int)sizeof(ST) : kOutOfRange;
+}
+
+// The lane's 4 x 4 quadrant of the plane at byte `pbyte` (zero outside H x W and
+// beyond the resource's range).
+template <typename ST>
+__device__ __forceinline__ void load_quadrant(rsrc_t r, int pbyte, int H, int W, int sy, int sx, float (&X)[4][4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int y = 4 * sy + i, x = 4 * sx + j;
-            const bool in = y < H && x < W;
-            const float v = ld(plane + (in ? y * W + x : 0));
-            X[i][j] = (in && ok) ? v : 0.f;
-        }
+        for (int j = 0; j < 4; ++j) X[i][j] = bload(r, pix_off<ST>(pbyte, H, W, sy, sx, i, j), (ST*)nullptr);
 }
 
 // Opaque copy: keeps the compiler from hoisting lane-dependent values out of
@@ -249,6 +266,7 @@ wtc_tiny_kernel(const FusedArgs a) {
     const ST* srcp = reinterpret_cast<const ST*>(a.src);
     const ST* auxp = reinterpret_cast<const ST*>(a.aux);
     ST* dstp = reinterpret_cast<ST*>(a.dst);
+    const int pstride = a.C * HW * (int)sizeof(ST);   // bytes between planes b and b + 1 of a channel
 
     for (int seg = 0; seg < 2; ++seg) {
         const int c = c_first + seg;
@@ -271,6 +289,13 @@ wtc_tiny_kernel(const FusedArgs a) {
             wsh[e] = v;
         }
         __syncthreads();
+        // resources over this segment's planes (b_begin .. b_end - 1 of channel c)
+        const size_t pbase = ((size_t)b_begin * a.C + c) * HW;
+        const uint32_t nbytes = (uint32_t)((b_end - 1 - b_begin) * pstride + HW * (int)sizeof(ST));
+        const rsrc_t rs = make_rsrc(srcp + pbase, nbytes);
+        const rsrc_t rd = make_rsrc(dstp + pbase, nbytes);
+        rsrc_t rx = rs;
+        if constexpr (BWD) rx = make_rsrc(auxp + pbase, nbytes);
         const float s0 = a.s0[c];
         const float bias = BWD ? 0.f : a.b0[c];
         float corr0[KK], corr1[KK], corr2[KK];
@@ -278,17 +303,30 @@ wtc_tiny_kernel(const FusedArgs a) {
         for (int q = 0; q < KK; ++q) corr0[q] = corr1[q] = corr2[q] = 0.f;
         float sumg = 0.f;
 
+        // the next pass's planes are loaded while the current one is computed
+        float Xn[4][4], xn[4][4];
+        {
+            const int ln = opaque(lane), t = ln & 3, pb = (ln >> 2) * pstride;
+            load_quadrant<ST>(rs, pb, a.H, a.W, t >> 1, t & 1, Xn);
+            if constexpr (BWD) load_quadrant<ST>(rx, pb, a.H, a.W, t >> 1, t & 1, xn);
+        }
         for (int b0 = b_begin; b0 < b_end; b0 += 16) {
             const int ln = opaque(lane);
             const int t = ln & 3, quad = ln >> 2;
             const int sy = t >> 1, sx = t & 1;
-            const int b = b0 + quad;
-            const bool ok = b < b_end;   // quad-uniform
-            const size_t poff = ((size_t)(ok ? b : b_begin) * a.C + c) * HW;   // a valid plane
-            float X[4][4];
-            load_quadrant(srcp + poff, a.H, a.W, sy, sx, ok, X);
-            float xs[4][4];
-            if constexpr (BWD) load_quadrant(auxp + poff, a.H, a.W, sy, sx, ok, xs);
+            const int pbyte = (b0 - b_begin + quad) * pstride;   // beyond the range past b_end
+            float X[4][4], xs[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    X[i][j] = Xn[i][j];
+                    if constexpr (BWD) xs[i][j] = xn[i][j];
+                }
+            if (b0 + 16 < b_end) {
+                load_quadrant<ST>(rs, pbyte + 16 * pstride, a.H, a.W, sy, sx, Xn);
+                if constexpr (BWD) load_quadrant<ST>(rx, pbyte + 16 * pstride, a.H, a.W, sy, sx, xn);
+            }
 
             // ---- base convolution (and correlation of x with g), one window row at a time ----
             float acc[4][4];
@@ -388,16 +426,12 @@ wtc_tiny_kernel(const FusedArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             // ---- level-1 synthesis fused with the output ----
             synth_band<2>(Y1, t, z);
-            if (ok) {
-                ST* op = dstp + poff;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int y = 4 * sy + i, x = 4 * sx + j;
-                        if (y < a.H && x < a.W) st(op + y * a.W + x, fmaf(s0, acc[i][j], bias + z[i][j]));
-                    }
-            }
+                for (int j = 0; j < 4; ++j)
+                    bstore(rd, pix_off<ST>(pbyte, a.H, a.W, sy, sx, i, j), fmaf(s0, acc[i][j], bias + z[i][j]),
+                           (ST*)nullptr);
         }
 
         if constexpr (BWD) {
