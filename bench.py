@@ -219,7 +219,8 @@ def kernel_role(name):
     import re
     if "wtc_finalize_kernel" in name:
         return "bwd"
-    m = re.search(r"wtc_fused_kernel<\s*\d+\s*,[^,]+,\s*(true|false)", name)
+    m = re.search(r"wtc_fused_kernel<\s*\d+\s*,[^,]+,\s*(true|false)", name) or \
+        re.search(r"wtc_tiny_kernel<[^,]+,\s*(true|false)", name)
     if m:
         return "bwd" if m.group(1) == "true" else "fwd"
     return None

@@ -169,6 +169,7 @@ struct FinalizeArgs {
     float* dwl;
     float* dsl;
     int C, B, L, Lm, k, ppw, P;
+    int chunks;   // > 0: records laid out [chunk][channel] (small-plane kernel)
 };
 
 // Launchers (defined in the .hip files); return a hipError_t as int.
@@ -176,7 +177,8 @@ int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nth
                  size_t lds_bytes, int grid, void* stream);
 int launch_finalize(const FinalizeArgs& f, void* stream);
 // Register-resident kernel for planes of at most 8 x 8 (k = 5, 1 <= L = Lm <= 2):
-// one 64-lane workgroup per ppw planes, same record layout as the plane pipeline.
+// one 64-lane workgroup per 16 consecutive channels and ppw batch entries
+// (grid = ceil(C / 16) x ceil(B / ppw)); backward records [chunk][channel].
 int launch_tiny(const FusedArgs& a, int dtype, int bwd, int grid, void* stream);
 constexpr bool tiny_supported(int k, int Hq, int Wq, int L, int Lm) {
     return k == 5 && Hq == 8 && Wq == 8 && L == Lm && Lm >= 1 && Lm <= 2;

@@ -35,6 +35,7 @@ struct FusedPlan {
     int nthr, bpq, grid, nchunk;
     size_t lds;
     int tiny;   // register-resident kernel for planes of at most 8 x 8
+    long nrec;  // backward partial records
 };
 
 int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
@@ -58,17 +59,18 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     const long esize = d->dtype == WTC_BF16 ? 2 : 4;
     if (tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm) &&
         ((long)d->B + 16) * d->C * d->H * d->W * esize < (1L << 31)) {   // 32-bit buffer offsets
-        // one wave per workgroup, 16 planes per pass; one resident round of
-        // waves (registers allow 3 per SIMD forward, 2 backward)
+        // one wave per workgroup: 16 consecutive channels, ppw batch entries (one
+        // pass per entry); one resident round of waves (registers allow 3 per
+        // SIMD forward, 2 backward)
         p->tiny = 1;
         a.P = partial_len(k, a.Lm);
-        const long qtot = (long)d->B * d->C;
+        const long ngrp = (d->C + 15) / 16;
         const long slots = (long)kComputeUnits * 4 * (bwd ? 2 : 3);
-        long ppw = (qtot + slots - 1) / slots;
-        ppw = (ppw + 15) / 16 * 16;
-        ppw = std::min<long>(ppw, d->B);
-        a.ppw = (int)std::max<long>(1, ppw);
-        p->grid = p->nchunk = (int)((qtot + a.ppw - 1) / a.ppw);
+        const long nchunk = std::max<long>(1, std::min<long>(d->B, slots / ngrp));
+        a.ppw = (int)((d->B + nchunk - 1) / nchunk);
+        p->nchunk = (int)((d->B + a.ppw - 1) / a.ppw);
+        p->grid = (int)(ngrp * p->nchunk);
+        p->nrec = (long)p->nchunk * d->C;
         p->nthr = 64;
         p->bpq = 1;
         p->lds = 0;
@@ -162,6 +164,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     const int grid = (int)((qtot + a.ppw - 1) / a.ppw);
     p->nchunk = grid;
     p->grid = grid;
+    p->nrec = 2L * grid;
     p->nthr = nthr;
     p->bpq = bpq;
     return WTC_OK;
@@ -226,7 +229,7 @@ int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const floa
 size_t wtconv_backward_workspace(const wtc_desc* d) {
     FusedPlan p;
     if (plan_fused(d, true, &p) != WTC_OK) return 0;
-    return (size_t)p.grid * 2 * p.a.P * sizeof(float);
+    return (size_t)p.nrec * p.a.P * sizeof(float);
 }
 
 int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -240,7 +243,7 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     FusedPlan p;
     st = plan_fused(d, true, &p);
     if (st != WTC_OK) return st;
-    const size_t need = (size_t)p.grid * 2 * p.a.P * sizeof(float);
+    const size_t need = (size_t)p.nrec * p.a.P * sizeof(float);
     if (!workspace || workspace_bytes < need) return WTC_EWORKSPACE;
     FusedArgs& a = p.a;
     a.src = g;
@@ -256,6 +259,7 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     f.w0 = w0; f.s0 = s0; f.wl = wl; f.sl = sl;
     f.dw0 = dw0; f.ds0 = ds0; f.db0 = db0; f.dwl = dwl; f.dsl = dsl;
     f.C = d->C; f.B = d->B; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.ppw = a.ppw; f.P = a.P;
+    f.chunks = p.tiny ? p.nchunk : 0;
     e = launch_finalize(f, stream);
     return e == 0 ? WTC_OK : WTC_EHIP;
 }
@@ -337,7 +341,7 @@ double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
         if (dir == 0) return 2.0 * N * e + params;
         FusedPlan p;
         if (plan_fused(d, true, &p) != WTC_OK) return -1.0;
-        const double partials = 4.0 * (double)p.grid * 2 * p.a.P;
+        const double partials = 4.0 * (double)p.nrec * p.a.P;
         // read x and g, write dx; params read; partials written then read; grads written
         return 3.0 * N * e + params + 2.0 * partials + params;
     }

@@ -33,9 +33,14 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
     const int w_hi = (int)(((long)(c + 1) * f.B - 1) / f.ppw);
     for (int e = tid; e < f.P; e += nthr) {
         float v = 0.f;
-        for (int w = w_lo; w <= w_hi; ++w) {
-            const int seg = ((long)w * f.ppw) / f.B == c ? 0 : 1;
-            v += f.partials[((size_t)w * 2 + seg) * f.P + e];
+        if (f.chunks > 0) {
+            // small-plane kernel: one record per (batch chunk, channel)
+            for (int j = 0; j < f.chunks; ++j) v += f.partials[((size_t)j * f.C + c) * f.P + e];
+        } else {
+            for (int w = w_lo; w <= w_hi; ++w) {
+                const int seg = ((long)w * f.ppw) / f.B == c ? 0 : 1;
+                v += f.partials[((size_t)w * 2 + seg) * f.P + e];
+            }
         }
         tot[e] = v;
     }

@@ -5,8 +5,8 @@
 // into the weights), organised for tiny planes: one quad of lanes holds one
 // plane zero-extended to 8 x 8, each lane a 4 x 4 quadrant.  Convolution
 // halos and subband exchanges travel between the four lanes of the quad by
-// DPP quad permutes, so the kernel uses no LDS and no barrier; a workgroup is
-// one wave, 16 planes in flight.
+// DPP quad permutes; a workgroup is one wave, 16 planes of 16 consecutive
+// channels in flight, and LDS holds only the group's folded weights.
 //
 // Level 1 (4 x 4 grid) and level 2 (2 x 2 grid) use the band-per-lane scheme:
 // lane t gathers subband t over the whole grid in canonical order, convolves
@@ -66,11 +66,21 @@ __device__ __forceinline__ float qx(float v) {
     }
 }
 
-// a[i] for a lane-dependent index 0 <= i < 4 (two selects on its bits)
+// a[i] for a lane-dependent index 0 <= i < 4 (two selects on its bits).  The
+// candidates are pinned to registers first: otherwise the optimizer may turn the
+// selects into a dynamically indexed (hence memory-resident) array.
 __device__ __forceinline__ float sel4(const float (&a)[4], int i) {
-    const float lo = (i & 1) ? a[1] : a[0];
-    const float hi = (i & 1) ? a[3] : a[2];
+    float a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+    asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
+    const float lo = (i & 1) ? a1 : a0;
+    const float hi = (i & 1) ? a3 : a2;
     return (i & 2) ? hi : lo;
+}
+
+// c ? x : y on register values (pinned, for the same reason as sel4)
+__device__ __forceinline__ float selv(bool c, float x, float y) {
+    asm volatile("" : "+v"(x), "+v"(y));
+    return c ? x : y;
 }
 
 // Raw +-1 butterfly of a 2 x 2 block a=(0,0), b=(0,1), c=(1,0), d=(1,1).
@@ -96,15 +106,17 @@ __device__ __forceinline__ void exchange_halo(const float (&X)[4][4], int sy, in
 #pragma unroll
     for (int k = 0; k < R; ++k)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) vr[k][j] = qx<2>(sy ? X[k][j] : X[4 - R + k][j]);
+        for (int j = 0; j < 4; ++j) vr[k][j] = qx<2>(selv(sy != 0, X[k][j], X[4 - R + k][j]));
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int k = 0; k < R; ++k) hc[i][k] = qx<1>(sx ? X[i][k] : X[i][4 - R + k]);
+        for (int k = 0; k < R; ++k) hc[i][k] = qx<1>(selv(sx != 0, X[i][k], X[i][4 - R + k]));
 #pragma unroll
     for (int k = 0; k < R; ++k)
 #pragma unroll
-        for (int l = 0; l < R; ++l) dg[k][l] = qx<3>(X[sy ? k : 4 - R + k][sx ? l : 4 - R + l]);
+        for (int l = 0; l < R; ++l)
+            dg[k][l] = qx<3>(selv(sy != 0, selv(sx != 0, X[k][l], X[k][4 - R + l]),
+                                  selv(sx != 0, X[4 - R + k][l], X[4 - R + k][4 - R + l])));
     // keep only the halo that lies inside the plane: the partners' blocks are above
     // (sy = 1) or below, left (sx = 1) or right; the other side is the plane border
 }
@@ -251,210 +263,212 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
-// One wave per workgroup: a range of ppw planes in channel-major order (at most
-// two channel segments); quad i takes planes i, i + 16, ... of a segment.
+// One wave per workgroup: 16 consecutive channels c0 .. c0 + 15 (quad i takes
+// channel c0 + i) and the batch entries of one chunk, one pass per entry.  The
+// 16 planes of a pass are adjacent in memory, so a pass reads and writes one
+// contiguous span; each quad keeps its channel, hence its weights and its
+// weight-gradient accumulators, for the whole workgroup.
 template <typename ST, bool BWD, int LM>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BWD ? 2 : 3)))
 wtc_tiny_kernel(const FusedArgs a) {
-    // weights of the current channel: [base][level 1, bands 0..3][level 2, bands 0..3]
-    __shared__ float wsh[KK * 9];
+    constexpr int WPC = KK * (1 + 4 * LM);   // weights per channel: base, then the bands of each level
+    __shared__ float wsh[16 * WPC];
     const int lane = threadIdx.x;
-    const long qtot = (long)a.C * a.B;
-    const long q0 = (long)blockIdx.x * a.ppw, q1 = min(q0 + (long)a.ppw, qtot);
-    const int c_first = (int)(q0 / a.B);
+    const int ngrp = (a.C + 15) >> 4;
+    const int grp = blockIdx.x % ngrp, chunk = blockIdx.x / ngrp;
+    const int c0 = grp * 16, nch = min(16, a.C - c0);
+    const int b_lo = chunk * a.ppw, b_hi = min(a.B, b_lo + a.ppw);
     const int HW = a.H * a.W;
+    const int pbytes = HW * (int)sizeof(ST);
     const ST* srcp = reinterpret_cast<const ST*>(a.src);
     const ST* auxp = reinterpret_cast<const ST*>(a.aux);
     ST* dstp = reinterpret_cast<ST*>(a.dst);
-    const int pstride = a.C * HW * (int)sizeof(ST);   // bytes between planes b and b + 1 of a channel
 
-    for (int seg = 0; seg < 2; ++seg) {
-        const int c = c_first + seg;
-        const long qs = max(q0, (long)c * a.B), qe = min(q1, (long)(c + 1) * a.B);
-        if (qs >= qe) break;
-        const int b_begin = (int)(qs - (long)c * a.B), b_end = (int)(qe - (long)c * a.B);
-        // weights of this channel: base (unfolded, scale applied at the output), and
-        // each band of each level folded with its scale and 4^-i; rotated for the backward
-        __syncthreads();   // the previous segment is done with the table
-        for (int e = lane; e < KK * (1 + 4 * LM); e += 64) {
-            const int blk = e / KK, q = e - blk * KK, tap = BWD ? KK - 1 - q : q;
-            float v;
-            if (blk == 0) {
-                v = a.w0[(size_t)c * KK + tap];
-            } else {
-                const int i = (blk - 1) >> 2, u = (blk - 1) & 3;   // level i + 1, band u
-                const size_t pu = ((size_t)i * a.C + c) * 4 + u;
-                v = ldexpf(a.sl[pu], -2 * (i + 1)) * a.wl[pu * KK + tap];
-            }
-            wsh[e] = v;
+    // weights of the group's channels: base (unfolded; s0 is applied at the
+    // output) and every band of every level folded with its scale and 4^-i;
+    // rotated by 180 degrees for the backward
+    for (int e = lane; e < nch * WPC; e += 64) {
+        const int cq = e / WPC, r = e - cq * WPC;
+        const int blk = r / KK, q = r - blk * KK, tap = BWD ? KK - 1 - q : q;
+        const int c = c0 + cq;
+        float v;
+        if (blk == 0) {
+            v = a.w0[(size_t)c * KK + tap];
+        } else {
+            const int i = (blk - 1) >> 2, u = (blk - 1) & 3;   // level i + 1, band u
+            const size_t pu = ((size_t)i * a.C + c) * 4 + u;
+            v = ldexpf(a.sl[pu], -2 * (i + 1)) * a.wl[pu * KK + tap];
         }
-        __syncthreads();
-        // resources over this segment's planes (b_begin .. b_end - 1 of channel c)
-        const size_t pbase = ((size_t)b_begin * a.C + c) * HW;
-        const uint32_t nbytes = (uint32_t)((b_end - 1 - b_begin) * pstride + HW * (int)sizeof(ST));
-        const rsrc_t rs = make_rsrc(srcp + pbase, nbytes);
-        const rsrc_t rd = make_rsrc(dstp + pbase, nbytes);
-        rsrc_t rx = rs;
-        if constexpr (BWD) rx = make_rsrc(auxp + pbase, nbytes);
-        const float s0 = a.s0[c];
-        const float bias = BWD ? 0.f : a.b0[c];
-        float corr0[KK], corr1[KK], corr2[KK];
+        wsh[e] = v;
+    }
+    __syncthreads();
+    const int quad0 = lane >> 2;
+    const bool cok = quad0 < nch;   // quad-uniform
+    const int cme = c0 + (cok ? quad0 : 0);
+    const float s0 = cok ? a.s0[cme] : 0.f;
+    const float bias = (BWD || !cok) ? 0.f : a.b0[cme];
+    float corr0[KK], corr1[KK], corr2[KK];
 #pragma unroll
-        for (int q = 0; q < KK; ++q) corr0[q] = corr1[q] = corr2[q] = 0.f;
-        float sumg = 0.f;
+    for (int q = 0; q < KK; ++q) corr0[q] = corr1[q] = corr2[q] = 0.f;
+    float sumg = 0.f;
 
-        // the next pass's planes are loaded while the current one is computed
-        float Xn[4][4], xn[4][4];
-        {
-            const int ln = opaque(lane), t = ln & 3, pb = (ln >> 2) * pstride;
-            load_quadrant<ST>(rs, pb, a.H, a.W, t >> 1, t & 1, Xn);
-            if constexpr (BWD) load_quadrant<ST>(rx, pb, a.H, a.W, t >> 1, t & 1, xn);
+    // pass b covers planes (b, c0) .. (b, c0 + nch - 1): one resource per pass
+    auto pass_rsrc = [&](const ST* base, int b) { return make_rsrc(base + ((size_t)b * a.C + c0) * HW, nch * pbytes); };
+    float Xn[4][4], xn[4][4];
+    {
+        const int ln = opaque(lane), t = ln & 3, pb = (ln >> 2) * pbytes;
+        load_quadrant<ST>(pass_rsrc(srcp, b_lo), pb, a.H, a.W, t >> 1, t & 1, Xn);
+        if constexpr (BWD) load_quadrant<ST>(pass_rsrc(auxp, b_lo), pb, a.H, a.W, t >> 1, t & 1, xn);
+    }
+    for (int b = b_lo; b < b_hi; ++b) {
+        const int ln = opaque(lane);
+        const int t = ln & 3, quad = ln >> 2;
+        const int sy = t >> 1, sx = t & 1;
+        const int pbyte = quad * pbytes;   // beyond the pass's range for a quad past the last channel
+        const float* wq = wsh + quad * WPC;
+        float X[4][4], xs[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                X[i][j] = Xn[i][j];
+                if constexpr (BWD) xs[i][j] = xn[i][j];
+            }
+        if (b + 1 < b_hi) {
+            load_quadrant<ST>(pass_rsrc(srcp, b + 1), pbyte, a.H, a.W, sy, sx, Xn);
+            if constexpr (BWD) load_quadrant<ST>(pass_rsrc(auxp, b + 1), pbyte, a.H, a.W, sy, sx, xn);
         }
-        for (int b0 = b_begin; b0 < b_end; b0 += 16) {
-            const int ln = opaque(lane);
-            const int t = ln & 3, quad = ln >> 2;
-            const int sy = t >> 1, sx = t & 1;
-            const int pbyte = (b0 - b_begin + quad) * pstride;   // beyond the range past b_end
-            float X[4][4], xs[4][4];
+
+        // ---- base convolution (and correlation of x with g), one window row at a time ----
+        float acc[4][4];
+        {
+            Halo h;
+            exchange_halo(X, sy, sx, h);
+            float w0[KK];
+#pragma unroll
+            for (int q = 0; q < KK; ++q) w0[q] = wq[q];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    X[i][j] = Xn[i][j];
-                    if constexpr (BWD) xs[i][j] = xn[i][j];
-                }
-            if (b0 + 16 < b_end) {
-                load_quadrant<ST>(rs, pbyte + 16 * pstride, a.H, a.W, sy, sx, Xn);
-                if constexpr (BWD) load_quadrant<ST>(rx, pbyte + 16 * pstride, a.H, a.W, sy, sx, xn);
-            }
-
-            // ---- base convolution (and correlation of x with g), one window row at a time ----
-            float acc[4][4];
-            {
-                Halo h;
-                exchange_halo(X, sy, sx, h);
-                float w0[KK];
+                for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
 #pragma unroll
-                for (int q = 0; q < KK; ++q) w0[q] = wsh[q];
+            for (int r = 0; r < WN; ++r) {
+                float row[WN];
+                window_row(X, h, sy != 0, sx != 0, r, row);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 4; ++i) {
+                    const int ky = r - i;
+                    if (ky < 0 || ky >= K) continue;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+                    for (int kx = 0; kx < K; ++kx)
 #pragma unroll
-                for (int r = 0; r < WN; ++r) {
-                    float row[WN];
-                    window_row(X, h, sy != 0, sx != 0, r, row);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int ky = r - i;
-                        if (ky < 0 || ky >= K) continue;
-#pragma unroll
-                        for (int kx = 0; kx < K; ++kx)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                acc[i][j] = fmaf(w0[ky * K + kx], row[j + kx], acc[i][j]);
-                                if constexpr (BWD)
-                                    corr0[ky * K + kx] = fmaf(xs[i][j], row[j + kx], corr0[ky * K + kx]);
-                            }
-                    }
+                        for (int j = 0; j < 4; ++j) {
+                            acc[i][j] = fmaf(w0[ky * K + kx], row[j + kx], acc[i][j]);
+                            if constexpr (BWD)
+                                corr0[ky * K + kx] = fmaf(xs[i][j], row[j + kx], corr0[ky * K + kx]);
+                        }
                 }
             }
-            if constexpr (BWD) {
+        }
+        if constexpr (BWD) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sumg += X[i][j];
-            }
-            // phase boundary: keeps the scheduler from overlapping the phases' live ranges
-            __builtin_amdgcn_sched_barrier(0);
+                for (int j = 0; j < 4; ++j) sumg += X[i][j];
+        }
+        // phase boundary: keeps the scheduler from overlapping the phases' live ranges
+        __builtin_amdgcn_sched_barrier(0);
 
-            // ---- level 1: raw bands of this lane's 2 x 2 positions ----
-            float hv[2][2][4], hx[2][2][4];
+        // ---- level 1: raw bands of this lane's 2 x 2 positions ----
+        float hv[2][2][4], hx[2][2][4];
+#pragma unroll
+        for (int jy = 0; jy < 2; ++jy)
+#pragma unroll
+            for (int jx = 0; jx < 2; ++jx) {
+                haar4(X[2 * jy][2 * jx], X[2 * jy][2 * jx + 1], X[2 * jy + 1][2 * jx], X[2 * jy + 1][2 * jx + 1],
+                      hv[jy][jx]);
+                if constexpr (BWD)
+                    haar4(xs[2 * jy][2 * jx], xs[2 * jy][2 * jx + 1], xs[2 * jy + 1][2 * jx], xs[2 * jy + 1][2 * jx + 1],
+                          hx[jy][jx]);
+            }
+        float G1[4][4], Y1[4][4], X1[4][4];
+        gather_band<2>(hv, t, G1);
+        if constexpr (BWD) gather_band<2>(hx, t, X1);
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            float w1[KK];
+#pragma unroll
+            for (int q = 0; q < KK; ++q) w1[q] = wq[KK + t * KK + q];
+            grid_conv<4, BWD>(G1, w1, Y1, X1, corr1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        float z[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) z[i][j] = 0.f;
+
+        // ---- level 2 (this lane's block is one level-2 position) ----
+        if constexpr (LM >= 2) {
+            float h2[1][1][4], x2[1][1][4];
+            haar4(hv[0][0][0], hv[0][1][0], hv[1][0][0], hv[1][1][0], h2[0][0]);
+            if constexpr (BWD) haar4(hx[0][0][0], hx[0][1][0], hx[1][0][0], hx[1][1][0], x2[0][0]);
+            float G2[2][2], Y2[2][2], X2[2][2];
+            gather_band<1>(h2, t, G2);
+            if constexpr (BWD) gather_band<1>(x2, t, X2);
+            float w2[KK];
+#pragma unroll
+            for (int q = 0; q < KK; ++q) w2[q] = wq[5 * KK + t * KK + q];
+            grid_conv<2, BWD>(G2, w2, Y2, X2, corr2);
+            // level-2 synthesis: the LL input of level 1 at this lane's 2 x 2 positions
+            float z2[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+            synth_band<1>(Y2, t, z2);
+            // enters the level-1 butterfly through band 0: +z2 at all four pixels
 #pragma unroll
             for (int jy = 0; jy < 2; ++jy)
 #pragma unroll
-                for (int jx = 0; jx < 2; ++jx) {
-                    haar4(X[2 * jy][2 * jx], X[2 * jy][2 * jx + 1], X[2 * jy + 1][2 * jx], X[2 * jy + 1][2 * jx + 1],
-                          hv[jy][jx]);
-                    if constexpr (BWD)
-                        haar4(xs[2 * jy][2 * jx], xs[2 * jy][2 * jx + 1], xs[2 * jy + 1][2 * jx],
-                              xs[2 * jy + 1][2 * jx + 1], hx[jy][jx]);
-                }
-            float G1[4][4], Y1[4][4], X1[4][4];
-            gather_band<2>(hv, t, G1);
-            if constexpr (BWD) gather_band<2>(hx, t, X1);
-            __builtin_amdgcn_sched_barrier(0);
-            {
-                float w1[KK];
+                for (int jx = 0; jx < 2; ++jx)
 #pragma unroll
-                for (int q = 0; q < KK; ++q) w1[q] = wsh[KK + t * KK + q];
-                grid_conv<4, BWD>(G1, w1, Y1, X1, corr1);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-
-            float z[4][4];
+                    for (int dy = 0; dy < 2; ++dy)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) z[i][j] = 0.f;
-
-            // ---- level 2 (this lane's block is one level-2 position) ----
-            if constexpr (LM >= 2) {
-                float h2[1][1][4], x2[1][1][4];
-                haar4(hv[0][0][0], hv[0][1][0], hv[1][0][0], hv[1][1][0], h2[0][0]);
-                if constexpr (BWD) haar4(hx[0][0][0], hx[0][1][0], hx[1][0][0], hx[1][1][0], x2[0][0]);
-                float G2[2][2], Y2[2][2], X2[2][2];
-                gather_band<1>(h2, t, G2);
-                if constexpr (BWD) gather_band<1>(x2, t, X2);
-                float w2[KK];
-#pragma unroll
-                for (int q = 0; q < KK; ++q) w2[q] = wsh[5 * KK + t * KK + q];
-                grid_conv<2, BWD>(G2, w2, Y2, X2, corr2);
-                // level-2 synthesis: the LL input of level 1 at this lane's 2 x 2 positions
-                float z2[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-                synth_band<1>(Y2, t, z2);
-                // enters the level-1 butterfly through band 0: +z2 at all four pixels
-#pragma unroll
-                for (int jy = 0; jy < 2; ++jy)
-#pragma unroll
-                    for (int jx = 0; jx < 2; ++jx)
-#pragma unroll
-                        for (int dy = 0; dy < 2; ++dy)
-#pragma unroll
-                            for (int dx = 0; dx < 2; ++dx) z[2 * jy + dy][2 * jx + dx] += z2[jy][jx];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- level-1 synthesis fused with the output ----
-            synth_band<2>(Y1, t, z);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    bstore(rd, pix_off<ST>(pbyte, a.H, a.W, sy, sx, i, j), fmaf(s0, acc[i][j], bias + z[i][j]),
-                           (ST*)nullptr);
+                        for (int dx = 0; dx < 2; ++dx) z[2 * jy + dy][2 * jx + dx] += z2[jy][jx];
         }
-
-        if constexpr (BWD) {
-            // per-segment record: [C_0][level 1: 4 bands][level 2: 4 bands][sum g][tail = 0],
-            // correlations in weight-gradient tap order (accumulator q holds tap KK-1-q)
-            float* rec = a.partials + ((size_t)blockIdx.x * 2 + seg) * a.P;
-            const int t = lane & 3;
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- level-1 synthesis fused with the output ----
+        synth_band<2>(Y1, t, z);
+        const rsrc_t rd = pass_rsrc(dstp, b);
 #pragma unroll
-            for (int q = 0; q < KK; ++q) {
-                const float v0 = wave_sum(corr0[q], 1);
-                const float v1 = wave_sum(corr1[q], 4);
-                if (lane == 0) rec[KK - 1 - q] = v0;
-                if (lane < 4) rec[KK + lane * KK + (KK - 1 - q)] = v1;
-                if constexpr (LM >= 2) {
-                    const float v2 = wave_sum(corr2[q], 4);
-                    if (lane < 4) rec[5 * KK + lane * KK + (KK - 1 - q)] = v2;
-                }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bstore(rd, pix_off<ST>(pbyte, a.H, a.W, sy, sx, i, j), fmaf(s0, acc[i][j], bias + z[i][j]),
+                       (ST*)nullptr);
+    }
+
+    if constexpr (BWD) {
+        // record of (chunk, channel): [C_0][level 1: 4 bands][level 2: 4 bands][sum g]
+        // [tail = 0], correlations in weight-gradient tap order (accumulator q holds
+        // tap KK-1-q); lane t of a quad holds band t of levels 1, 2
+        const int t = lane & 3;
+        float* rec = a.partials + ((size_t)chunk * a.C + cme) * a.P;
+#pragma unroll
+        for (int q = 0; q < KK; ++q) {
+            float v0 = corr0[q];
+            v0 += qx<1>(v0);
+            v0 += qx<2>(v0);
+            if (cok) {
+                if (t == 0) rec[KK - 1 - q] = v0;
+                rec[KK + t * KK + (KK - 1 - q)] = corr1[q];
+                if constexpr (LM >= 2) rec[5 * KK + t * KK + (KK - 1 - q)] = corr2[q];
             }
-            const float vs = wave_sum(sumg, 1);
-            if (lane == 0) {
-                rec[a.P - 2] = vs;
-                rec[a.P - 1] = 0.f;
-            }
+        }
+        float vs = sumg;
+        vs += qx<1>(vs);
+        vs += qx<2>(vs);
+        if (cok && t == 0) {
+            rec[a.P - 2] = vs;
+            rec[a.P - 1] = 0.f;
         }
     }
 }
