@@ -35,8 +35,10 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
         float v = 0.f;
         if (f.chunks > 0) {
             // small-plane kernel: one record per (batch chunk, channel)
+#pragma unroll 4
             for (int j = 0; j < f.chunks; ++j) v += f.partials[((size_t)j * f.C + c) * f.P + e];
         } else {
+#pragma unroll 4
             for (int w = w_lo; w <= w_hi; ++w) {
                 const int seg = ((long)w * f.ppw) / f.B == c ? 0 : 1;
                 v += f.partials[((size_t)w * 2 + seg) * f.P + e];
@@ -46,31 +48,34 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
     }
     __syncthreads();
     const float tail = tot[f.P - 1];
-    // level 0
-    for (int e = tid; e < KK; e += nthr) f.dw0[(size_t)c * KK + e] = f.s0[c] * tot[e];
-    if (tid == 0) {
-        float s = 0.f;
-        for (int e = 0; e < KK; ++e) s = fmaf(f.w0[(size_t)c * KK + e], tot[e], s);
-        f.ds0[c] = s;
-        f.db0[c] = tot[f.P - 2];
-    }
-    // levels 1..L
-    for (int e = tid; e < 4 * f.L * KK; e += nthr) {
-        const int i = e / (4 * KK), rem = e - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
-        const float cv = (i < f.Lm) ? tot[KK + e] : ((tap == KK / 2) ? tail : 0.f);
-        const size_t pi = ((size_t)i * f.C + c) * 4 + u;
-        f.dwl[pi * KK + tap] = ldexpf(f.sl[pi], -2 * (i + 1)) * cv;
-    }
-    for (int e = tid; e < 4 * f.L; e += nthr) {
-        const int i = e / 4, u = e - i * 4;
-        const size_t pi = ((size_t)i * f.C + c) * 4 + u;
-        float s = 0.f;
-        if (i < f.Lm) {
-            for (int tap = 0; tap < KK; ++tap) s = fmaf(f.wl[pi * KK + tap], tot[KK + (i * 4 + u) * KK + tap], s);
+    // scale gradients are dot products of the weights with the correlations:
+    // products staged in LDS, then one short sum per scale
+    float* prod = tot + ((f.P + 3) & ~3);   // [level 0 | levels 1..L x 4 bands][tap]
+    const int n0 = KK * (1 + 4 * f.L);
+    for (int e = tid; e < n0; e += nthr) {
+        if (e < KK) {
+            f.dw0[(size_t)c * KK + e] = f.s0[c] * tot[e];
+            prod[e] = f.w0[(size_t)c * KK + e] * tot[e];
         } else {
-            s = f.wl[pi * KK + KK / 2] * tail;
+            const int r = e - KK;
+            const int i = r / (4 * KK), rem = r - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
+            const float cv = (i < f.Lm) ? tot[e] : ((tap == KK / 2) ? tail : 0.f);
+            const size_t pi = ((size_t)i * f.C + c) * 4 + u;
+            f.dwl[pi * KK + tap] = ldexpf(f.sl[pi], -2 * (i + 1)) * cv;
+            prod[e] = f.wl[pi * KK + tap] * cv;
         }
-        f.dsl[pi] = ldexpf(s, -2 * (i + 1));
+    }
+    __syncthreads();
+    for (int e = tid; e < 1 + 4 * f.L; e += nthr) {
+        float s = 0.f;
+        for (int tap = 0; tap < KK; ++tap) s += prod[e * KK + tap];
+        if (e == 0) {
+            f.ds0[c] = s;
+            f.db0[c] = tot[f.P - 2];
+        } else {
+            const int i = (e - 1) >> 2, u = (e - 1) & 3;
+            f.dsl[((size_t)i * f.C + c) * 4 + u] = ldexpf(s, -2 * (i + 1));
+        }
     }
 }
 
@@ -99,7 +104,7 @@ int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nth
 
 int launch_finalize(const FinalizeArgs& f, void* stream) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-    const size_t lds = (size_t)f.P * sizeof(float);
+    const size_t lds = ((size_t)((f.P + 3) & ~3) + (size_t)f.k * f.k * (1 + 4 * f.L)) * sizeof(float);
     hipLaunchKernelGGL(wtc_finalize_kernel, dim3(f.C), dim3(256), lds, st, f);
     return (int)hipGetLastError();
 }
