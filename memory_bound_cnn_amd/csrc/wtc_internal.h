@@ -20,6 +20,9 @@ constexpr int kMaxK = 7;
 // of levels >= f and the later arrays, over the level-0 plane][tail]; the early
 // bands of levels >= f are then written only after the whole workgroup is done
 // reading the level-0 plane, and their rings are re-zeroed per plane.
+// Direct-load layout ("dl"): nothing overlaps the level-0 plane, so the next
+// plane can be copied into it by DMA while the current one is still being
+// processed; the backward adds a plane of x (row stride Wq + 4, no halo).
 struct Layout {
     int early_lv;      // levels analysed in registers during the level-0 phase (<= 3)
     int overlap;       // later arrays overlap the level-0 plane (rings re-zeroed per plane)
@@ -31,16 +34,21 @@ struct Layout {
     int yd_off[kMaxLm + 1];                    // Y'_i (i >= 3), [4][Hq_i][Wq_i]
     int xb_off[kMaxLm + 1];                    // backward: bands of x (i >= 3), [4][Hq_i][Wq_i]
     int tail_off;                              // tail term rho * kappa
+    int dl;                                    // direct-load layout
+    int xp_off, xp_S;                          // dl backward: x plane [Hq][xp_S]
 };
 
 constexpr int lay_round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 // The one definition of the slot layout, evaluated on the host for the
 // runtime-geometry kernel and at compile time for the fixed-geometry ones.
-constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd, int bovl) {
+constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd, int bovl,
+                             bool dl = false) {
     Layout L{};
     const int R = k / 2;
     L.early_lv = Lm < early_req ? Lm : early_req;
+    L.dl = dl ? 1 : 0;
+    if (dl) bovl = 0;
     int off = 0;
     for (int i = 1; i <= Lm; ++i) {
         L.b_rows[i] = (Hq >> i) + 2 * R;
@@ -99,7 +107,7 @@ constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool 
     }
     L.a0_off = off;
     int r2_base = off;
-    if (r2 <= a0_size) {
+    if (r2 <= a0_size && !dl) {
         L.overlap = r2 > 0 ? 1 : 0;
         off += a0_size;
     } else {
@@ -112,6 +120,13 @@ constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool 
     for (int i = 3; i <= Lm; ++i) {
         L.yd_off[i] = r2_base + rel_y[i];
         if (bwd) L.xb_off[i] = r2_base + rel_x[i];
+    }
+    if (dl && bwd) {
+        // x rows 16-byte aligned; stride = 4 (mod 8) floats keeps the 4x4 block
+        // reads of two vertically adjacent lanes in different banks
+        L.xp_off = lay_round_up(off, 4);
+        L.xp_S = lay_round_up(Wq, 4) % 8 == 0 ? lay_round_up(Wq, 4) + 4 : lay_round_up(Wq, 4);
+        off = L.xp_off + lay_round_up(Hq * L.xp_S, 4);
     }
     L.tail_off = off;
     off += 4;

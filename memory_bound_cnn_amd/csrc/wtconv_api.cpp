@@ -112,14 +112,21 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         if (better) best = Cand{lay, NP, nthr, bpq, wgs, score};
     };
     if (a.qpp > 256) return WTC_ESHAPE;
-    for (const int bovl : {0, 2, 1}) {
+    // direct loads (DMA into the LDS slot): fp32 rows of 4-pixel vectors, on the
+    // plane classes with fixed-geometry instances of that mode, one plane per
+    // workgroup; tried first, so it wins ties
+    const bool dl_ok = d->dtype == WTC_FP32 && a.vec && k == 5 && a.Hq == a.Wq && (a.Hq == 32 || a.Hq == 64);
+    for (const int variant : {-1, 0, 2, 1}) {
+        const bool dl = variant < 0;
+        const int bovl = dl ? 0 : variant;
+        if (dl && !dl_ok) continue;
         if (bovl > a.Lm) continue;
-        Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl);
-        if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl);
+        Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl, dl);
+        if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl, dl);
         if (bovl > 0 && !bwd && best.score >= 0) continue;
         if (a.qpp <= 64) {
             // several planes per workgroup when planes are small
-            for (int np = 1; np <= 64 / a.qpp; ++np) consider(lay, np, round_up(4 * a.qpp * np, 64), 1);
+            for (int np = 1; np <= (dl ? 1 : 64 / a.qpp); ++np) consider(lay, np, round_up(4 * a.qpp * np, 64), 1);
         } else if (a.qpp <= 128) {
             consider(lay, 1, 512, 1);
         } else {
@@ -134,7 +141,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     {
         // prefetch when every thread's share of a plane group fits its capacity
         const int units = cdiv(NP * per_units, nthr);
-        a.pf_on = (units * (a.vec ? 4 : 1) <= pf_capacity(bwd, bpq)) ? 1 : 0;
+        a.pf_on = (!a.lay.dl && units * (a.vec ? 4 : 1) <= pf_capacity(bwd, bpq)) ? 1 : 0;
         // the kernel keeps unit offsets within a plane group in 32 bits
         if ((long)NP * d->C * d->H * d->W >= (1L << 31)) a.pf_on = 0;
     }

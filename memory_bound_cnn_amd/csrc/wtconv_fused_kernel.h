@@ -94,25 +94,31 @@ __device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
 // ---------------------------------------------------------------------------
 // LDS helpers
 // ---------------------------------------------------------------------------
+// Native vector types: their loads keep the float type-alias tag, which lets
+// the compiler see that they cannot overlap a pending LDS DMA into another
+// region (it would otherwise wait for the DMA before each of them).
+typedef float lds_f4 __attribute__((ext_vector_type(4)));
+typedef float lds_f2 __attribute__((ext_vector_type(2)));
+
 // Read WW consecutive floats; AL = guaranteed alignment of p in floats (4, 2, 1).
 template <int WW, int AL>
 __device__ __forceinline__ void lds_row(const float* p, float (&row)[WW]) {
     if constexpr (AL == 4) {
 #pragma unroll
         for (int q = 0; q + 4 <= WW; q += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(p + q);
+            const lds_f4 v = *reinterpret_cast<const lds_f4*>(p + q);
             row[q] = v.x; row[q + 1] = v.y; row[q + 2] = v.z; row[q + 3] = v.w;
         }
         constexpr int done = (WW / 4) * 4;
         if constexpr (WW - done >= 2) {
-            const float2 v = *reinterpret_cast<const float2*>(p + done);
+            const lds_f2 v = *reinterpret_cast<const lds_f2*>(p + done);
             row[done] = v.x; row[done + 1] = v.y;
         }
         if constexpr ((WW - done) % 2 == 1) row[WW - 1] = p[WW - 1];
     } else if constexpr (AL == 2) {
 #pragma unroll
         for (int q = 0; q + 2 <= WW; q += 2) {
-            const float2 v = *reinterpret_cast<const float2*>(p + q);
+            const lds_f2 v = *reinterpret_cast<const lds_f2*>(p + q);
             row[q] = v.x; row[q + 1] = v.y;
         }
         if constexpr (WW % 2 == 1) row[WW - 1] = p[WW - 1];
@@ -174,7 +180,7 @@ __device__ __forceinline__ void zero_rings(float* lds, const G& g, int off, int 
         const int j = fdiv(rem, drows), r = rem - j * rows;
         float* row = lds + s2 * g.slot() + off + j * astride + r * S;
         if (r < R || r >= R + h) {
-            for (int c = 0; c < S; c += 4) *reinterpret_cast<float4*>(row + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int c = 0; c < S; c += 4) *reinterpret_cast<lds_f4*>(row + c) = lds_f4{0.f, 0.f, 0.f, 0.f};
         } else {
 #pragma unroll
             for (int c = 0; c < R; ++c) row[c] = 0.f;
@@ -280,6 +286,7 @@ __device__ __forceinline__ float wave_sum(float v, int width_mask_from) {
 // (make_layout), so one kernel body serves both.
 // ---------------------------------------------------------------------------
 struct RtGeom {
+    static constexpr bool kDL = false;   // the runtime-geometry kernel stages planes through registers
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
     __device__ int Lm() const { return a.Lm; }
@@ -303,15 +310,18 @@ struct RtGeom {
     __device__ int yd_off(int i) const { return a.lay.yd_off[i]; }
     __device__ int xb_off(int i) const { return a.lay.xb_off[i]; }
     __device__ int tail_off() const { return a.lay.tail_off; }
+    __device__ int xp_off() const { return a.lay.xp_off; }
+    __device__ int xp_S() const { return a.lay.xp_S; }
     __device__ int wts_off() const { return a.wts_off; }
     __device__ int red_off() const { return a.red_off; }
     __device__ int dsub() const { return a.dsub; }
     __device__ int P() const { return a.P; }
 };
 
-template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL>
+template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, bool DLV>
 struct CtGeom {
-    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL);
+    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, DLV);
+    static constexpr bool kDL = DLV;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -335,6 +345,8 @@ struct CtGeom {
     __device__ static constexpr int yd_off(int i) { return lay.yd_off[i]; }
     __device__ static constexpr int xb_off(int i) { return lay.xb_off[i]; }
     __device__ static constexpr int tail_off() { return lay.tail_off; }
+    __device__ static constexpr int xp_off() { return lay.xp_off; }
+    __device__ static constexpr int xp_S() { return lay.xp_S; }
     __device__ static constexpr int wts_off() { return NPV * lay.slot; }
     __device__ static constexpr int red_off() { return 0; }
     __device__ static constexpr int dsub() { return NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1; }
@@ -376,8 +388,12 @@ __device__ __forceinline__ void haar4(float a, float b, float c, float d, float 
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD || BPQ > 1) ? 2 : 3))) wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
+    // Direct-load mode: planes are copied from device memory into their LDS slot
+    // by DMA (global_load_lds), one plane ahead, with no register staging.
+    constexpr bool DL = G::kDL;
+    static_assert(!DL || (sizeof(ST) == 4 && VEC && BPQ == 1), "direct loads: fp32 rows, one block per quad");
     constexpr int PFF = pf_capacity(BWD, BPQ);  // prefetch capacity, floats per thread
-    constexpr int PFU = VEC ? PFF / 4 : PFF;    // prefetch units (4-pixel groups or pixels)
+    constexpr int PFU = DL ? 1 : (VEC ? PFF / 4 : PFF);   // prefetch units (4-pixel groups or pixels)
     constexpr int UW = VEC ? 4 : 1;
     extern __shared__ __align__(16) float lds[];
 
@@ -493,7 +509,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
     const int per = a.H * wv;
     const FastDiv dper = make_div(per), dwv = make_div(wv);
     // (the backward kernel with two blocks per quad never has the capacity)
-    const bool pf_on = !(BWD && BPQ > 1) && a.pf_on != 0;
+    const bool pf_on = !DL && !(BWD && BPQ > 1) && a.pf_on != 0;
     float pf[PFU][UW];
     // With 4-pixel units the decode of each unit is done once per segment: its
     // offset within a plane group in device memory, and (packed) its plane
@@ -557,7 +573,41 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
             }
         }
     };
+    // Direct loads: rows [0, H) of the NP planes starting at batch index bbn go to
+    // region `roff` of their slots (row stride rS, interior at row rr, column rc),
+    // one 64-pixel row chunk per wave instruction; the LDS destination of lane l
+    // is the chunk start + 4 l bytes, so lanes past the row end are masked off.
+    // Cells outside the interior are never written (zeroed once per segment).
+    auto dl_issue = [&](const ST* base, int roff, int rS, int rr, int rc, int bbn) {
+        if constexpr (DL) {
+            constexpr int CPR = (G::Wq() + 63) / 64;
+            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
+            const int nw = nthr >> 6;
+            const int per_plane = a.H * CPR;
+            for (int j = wave; j < g.NP() * per_plane; j += nw) {
+                const int s2 = g.NP() == 1 ? 0 : j / per_plane;
+                const int m = j - s2 * per_plane;
+                const int r = CPR == 1 ? m : m / CPR, ch = m - r * CPR;
+                if (bbn + s2 >= b_end) continue;
+                const int col = ch * 64 + lane;
+                if (col < a.W)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(base + ((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)r * a.W + col),
+                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc +
+                                                                   ch * 64),
+                        4, 0, 0);
+            }
+        }
+    };
     if (pf_on) pf_issue(b_begin);
+    if constexpr (DL) {
+        if constexpr (BWD) {
+            for (int s2 = 0; s2 < g.NP(); ++s2)
+                zero_ring(lds + s2 * g.slot() + g.xp_off(), g.Hq(), g.xp_S(), 0, a.H, 0, a.W, tid, nthr);
+            dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, b_begin);
+        }
+        dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, b_begin);
+    }
 
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
@@ -566,6 +616,12 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
         float* S = lds + (slot < g.NP() ? slot : 0) * g.slot();
         const size_t poff = ((size_t)b * a.C + c) * plane_sz;
 
+        if constexpr (DL) {
+            // this plane's direct loads have landed (every wave's), and the
+            // previous plane is fully consumed
+            __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+            lds_barrier();
+        } else {
         lds_barrier();  // the previous plane is fully consumed
 
         // ---------------- phase 1: stage the planes in LDS ----------------
@@ -597,6 +653,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
         lds_barrier();
         // the next planes' loads fly while this plane is computed
         if (pf_on && bb + g.NP() < b_end) pf_issue(bb + g.NP());
+        }
 
         // ---------------- phase 2: base conv; analysis of levels 1..3 ----------------
         float acc[BPQ][4][4];
@@ -639,7 +696,11 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
             float w[KK];
             load_w<K, BWD>(wbase, w);
             float xo[4][4];
-            if constexpr (BWD) {
+            if constexpr (BWD && DL) {
+                const float* xr = S + g.xp_off() + py0 * g.xp_S() + px0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lds_row<4, 4>(xr + i * g.xp_S(), xo[i]);
+            } else if constexpr (BWD) {
                 const ST* xp = auxp + poff + opaque(py0 * a.W + px0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ld_row4<VEC>(xp + i * a.W, py0 + i < a.H, px0, a.W, xo[i]);
@@ -706,6 +767,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                               nthr);
         }
         lds_barrier();
+        // the level-0 plane is dead: the next planes' copies land during the rest
+        if (DL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP());
 
         // ---------------- phase 3: analysis of levels early_lv+1..Lm ----------------
         for (int i = g.early() + 1; i <= Lm; ++i) {
@@ -746,11 +809,19 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
                 for (int jy = 0; jy < 4; ++jy) {
                     float r0[2][4], r1[2][4];
                     const int y0 = 8 * qy + 2 * jy;
+                    if constexpr (DL) {
+                        const float* xr = S + g.xp_off() + y0 * g.xp_S() + 8 * qx;
+                        lds_row<4, 4>(xr, r0[0]);
+                        lds_row<4, 4>(xr + 4, r0[1]);
+                        lds_row<4, 4>(xr + g.xp_S(), r1[0]);
+                        lds_row<4, 4>(xr + g.xp_S() + 4, r1[1]);
+                    } else {
                     const ST* p0r = xp + (2 * jy) * a.W;
                     ld_row4<VEC>(p0r, y0 < a.H, 8 * qx, a.W, r0[0]);
                     ld_row4<VEC>(p0r + 4, y0 < a.H, 8 * qx + 4, a.W, r0[1]);
                     ld_row4<VEC>(p0r + a.W, y0 + 1 < a.H, 8 * qx, a.W, r1[0]);
                     ld_row4<VEC>(p0r + a.W + 4, y0 + 1 < a.H, 8 * qx + 4, a.W, r1[1]);
+                    }
 #pragma unroll
                     for (int jx = 0; jx < 4; ++jx) {
                         const float p0 = r0[jx >> 1][(2 * jx) & 3], p1 = r0[jx >> 1][(2 * jx + 1) & 3];
@@ -812,6 +883,8 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
         if constexpr (BWD) {
             if (Lm >= 3) {
                 lds_barrier();  // band 0 of level 3 (x) written in phase 4a
+                // every wave is done with the x plane: the next one lands meanwhile
+                if (DL && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
                 for (int i = 4; i <= Lm; ++i) {
                     const int hi = g.Hq() >> i, wi = g.Wq() >> i, wp = g.Wq() >> (i - 1);
                     const int pi = hi * wi;
@@ -897,6 +970,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD |
             }
         }
         lds_barrier();
+        if (DL && BWD && Lm < 3 && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
 
         // ---------------- phase 4d: levels 1, 2 results in place ----------------
 #pragma unroll
@@ -1099,14 +1173,14 @@ namespace fused_detail {
 
 // Launch the fixed-geometry instantiation if the plan matches it exactly.
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
-          int NTHR, int BOVL>
+          int NTHR, int BOVL, bool DLV = false>
 bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
                 hipError_t* err) {
     if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
-        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL)
+        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || (a.lay.dl != 0) != DLV)
         return false;
-    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL>>(a, nthr, lds,
-                                                                                          grid, st);
+    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, DLV>>(a, nthr, lds,
+                                                                                               grid, st);
     return true;
 }
 
