@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--impl", default="fused", choices=["fused", "unfused"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-summary", action="store_true")
+    p.add_argument("--torch-dwconv", action="store_true",
+                   help="also time PyTorch's depthwise k x k convolution (MIOpen) at the headline shape")
     p.add_argument("--profile-steps", type=int, default=None,
                    help="run only this many steps, no summary / CPU baseline (for rocprofv3)")
     p.add_argument("--copy-probe-mib", type=int, default=None,
@@ -146,6 +148,87 @@ class Runner:
         fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
         bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
         return total_ms / steps, fwd_ms, bwd_ms
+
+
+def dwconv_comparison(wl, torch, binding, with_torch):
+    """WTConv against the plain depthwise convolution it replaces, at one
+    shape: this library's L-level k x k operator, its L = 0 path (a k x k
+    depthwise conv with scale and bias) at k = 5 and at k = 7 (the ConvNeXt
+    block's kernel), and optionally PyTorch's depthwise conv (MIOpen) with
+    autograd for the backward (dx, dW, db).  fwd+bwd ms per call pair."""
+    import dataclasses
+    res = {"shape": {"B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W, "storage": wl.dtype}}
+    cases = {f"wtconv_L{wl.L}_k{wl.k}": (wl.L, wl.k), "dwconv_L0_k5": (0, 5), "dwconv_L0_k7": (0, 7)}
+    for label, (Lc, kc) in cases.items():
+        ww = dataclasses.replace(wl, name=f"{wl.name}_{label}", L=Lc, k=kc, L_max=Lc, sweep=())
+        rr = Runner(ww, Lc, "fused", torch, binding)
+        m, mf, mb = rr.time(50, 5)
+        del rr
+        res[label] = {"ms": round(m, 5), "fwd_ms": round(mf, 5), "bwd_ms": round(mb, 5)}
+    if with_torch:
+        import torch.nn.functional as F
+        sd = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        x = torch.randn(wl.B, wl.C, wl.H, wl.W, device="cuda", dtype=sd, requires_grad=True)
+        g = torch.randn_like(x)
+        w = torch.randn(wl.C, 1, 7, 7, device="cuda", dtype=sd, requires_grad=True)
+        b = torch.randn(wl.C, device="cuda", dtype=sd, requires_grad=True)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        fw, bw = [], []
+        for i in range(25):
+            ev[0].record()
+            y = F.conv2d(x, w, b, padding=3, groups=wl.C)
+            ev[1].record()
+            y.backward(g)
+            ev[2].record()
+            torch.cuda.synchronize()
+            if i >= 5:
+                fw.append(ev[0].elapsed_time(ev[1]))
+                bw.append(ev[1].elapsed_time(ev[2]))
+            x.grad = w.grad = b.grad = None
+        res["torch_dwconv_k7"] = {"ms": round(sum(fw) / len(fw) + sum(bw) / len(bw), 5),
+                                  "fwd_ms": round(sum(fw) / len(fw), 5), "bwd_ms": round(sum(bw) / len(bw), 5)}
+    base = res["dwconv_L0_k7"]["ms"]
+    res["wtconv_over_dwconv_k7"] = round(res[f"wtconv_L{wl.L}_k{wl.k}"]["ms"] / base, 3)
+    return res
+
+
+def memory_comparison(wl, L, torch, binding):
+    """Peak device memory of one training-style step (forward, then backward
+    of <out, g>) through the autograd wrapper, above the memory already held
+    by the inputs and parameters: the fused kernels against the level-by-level
+    baseline."""
+    from memory_bound_cnn_amd.autograd import wtconv
+    from memory_bound_cnn_amd.inputs import workload_inputs
+    d = workload_inputs(wl)
+    sd = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda", 0)
+    x0 = torch.from_numpy(d["x"]).to(dev).to(sd)
+    g = torch.from_numpy(d["g"]).to(dev).to(sd)
+    prm = {k: torch.from_numpy(d[k][:L] if k in ("wl", "sl") else d[k]).to(dev).contiguous()
+           for k in ("w0", "s0", "b0", "wl", "sl")}
+    shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
+    res = {"workload": wl.name, "L": L, "input_bytes": x0.numel() * x0.element_size()}
+    for impl in ("fused", "unfused"):
+        x = x0.clone().requires_grad_(True)
+        p = {k: v.clone().requires_grad_(True) for k, v in prm.items()}
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        y = wtconv(x, p["w0"], p["s0"], p["b0"], p["wl"], p["sl"], L, impl=impl)
+        y.backward(g)
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        if impl == "fused":
+            ws = (binding.wtconv_forward_workspace(*shp), binding.wtconv_backward_workspace(*shp))
+        else:
+            ws = (binding.wtconv_forward_unfused_workspace(*shp), binding.wtconv_backward_unfused_workspace(*shp))
+        res[impl] = {"peak_bytes_above_inputs": int(peak), "fwd_workspace_bytes": ws[0],
+                     "bwd_workspace_bytes": ws[1]}
+        del y, x, p
+    res["unfused_over_fused_peak"] = round(res["unfused"]["peak_bytes_above_inputs"] /
+                                           res["fused"]["peak_bytes_above_inputs"], 3)
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -460,6 +543,8 @@ def main():
                         binding.wtconv_io_model_bytes(*sh, impl=1, direction=1)
                 summary.append(row)
         line["per_workload"] = summary
+        line["dwconv_comparison"] = dwconv_comparison(wl, torch, binding, a.torch_dwconv)
+        line["training_step_memory"] = memory_comparison(wl, L, torch, binding)
 
     if cpu is not None:
         line["cpu_baseline"] = cpu

@@ -14,22 +14,30 @@ __all__ = ["WTConvFunction", "WTConv2d", "wtconv"]
 
 
 class WTConvFunction(torch.autograd.Function):
+    """impl = "fused" (the on-chip kernels) or "unfused" (the level-by-level
+    baseline, whose kernels keep every band and level result in a device
+    workspace while they run)."""
+
     @staticmethod
-    def forward(ctx, x, w0, s0, b0, wl, sl, L):
+    def forward(ctx, x, w0, s0, b0, wl, sl, L, impl="fused"):
+        if impl not in ("fused", "unfused"):
+            raise ValueError(f"impl must be 'fused' or 'unfused', not {impl!r}")
         x = x.contiguous()
-        ctx.L = L
+        ctx.L, ctx.impl = L, impl
         ctx.save_for_backward(x, w0, s0, wl, sl)
-        return binding.wtconv_forward(x, w0, s0, b0, wl, sl, L)
+        fwd = binding.wtconv_forward if impl == "fused" else binding.wtconv_forward_unfused
+        return fwd(x, w0, s0, b0, wl, sl, L)
 
     @staticmethod
     def backward(ctx, g):
         x, w0, s0, wl, sl = ctx.saved_tensors
-        r = binding.wtconv_backward(x, g.contiguous(), w0, s0, wl, sl, ctx.L)
-        return r["dx"], r["dw0"], r["ds0"], r["db0"], r["dwl"], r["dsl"], None
+        bwd = binding.wtconv_backward if ctx.impl == "fused" else binding.wtconv_backward_unfused
+        r = bwd(x, g.contiguous(), w0, s0, wl, sl, ctx.L)
+        return r["dx"], r["dw0"], r["ds0"], r["db0"], r["dwl"], r["dsl"], None, None
 
 
-def wtconv(x, w0, s0, b0, wl, sl, L):
-    return WTConvFunction.apply(x, w0, s0, b0, wl, sl, L)
+def wtconv(x, w0, s0, b0, wl, sl, L, impl="fused"):
+    return WTConvFunction.apply(x, w0, s0, b0, wl, sl, L, impl)
 
 
 class WTConv2d(torch.nn.Module):

@@ -164,6 +164,14 @@ struct FusedArgs {
     int P;             // partial record length (floats)
 };
 
+// Waves per SIMD the fused kernels are compiled for (register budget 512 /
+// waves): 3 forward, 2 backward or with two blocks per quad; the
+// fixed-geometry kernels without wavelet levels (a plain depthwise conv) are
+// small enough for 4 forward and 3 backward.
+constexpr int fused_waves_per_simd(bool bwd, int bpq, bool no_levels_static) {
+    return no_levels_static ? (bwd ? 3 : 4) : ((bwd || bpq > 1) ? 2 : 3);
+}
+
 // Next-plane prefetch capacity in floats per thread: the forward kernel with
 // two blocks per quad (large planes) has the registers for a whole plane.
 constexpr int pf_capacity(bool bwd, int bpq) { return (!bwd && bpq > 1) ? 32 : 16; }

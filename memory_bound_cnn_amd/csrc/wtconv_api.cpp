@@ -102,7 +102,10 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * k * dsub * k;
         const size_t lds = (size_t)std::max(NP * lay.slot + wts_n, bwd ? red_n : 0) * 4;
         if (lds > kLdsLimit || NP * per_units >= 65536) return;   // fast in-kernel division range
-        const int wpe = (bwd || bpq > 1) ? 2 : 3;
+        // plain depthwise conv (no levels) on a plane class with fixed-geometry
+        // direct-load instances: those are compiled for more waves per SIMD
+        const bool nolev = d->L == 0 && lay.dl && a.Hq == 64 && (k == 5 || k == 7);
+        const int wpe = fused_waves_per_simd(bwd, bpq, nolev);
         const int lds_wgs = (int)(kLdsLimit / lds);
         const int reg_wgs = std::max(1, 4 * wpe / (nthr / 64));
         const int wgs = std::max(1, std::min(lds_wgs, reg_wgs));
@@ -115,7 +118,8 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     // direct loads (DMA into the LDS slot): fp32 rows of 4-pixel vectors, on the
     // plane classes with fixed-geometry instances of that mode, one plane per
     // workgroup; tried first, so it wins ties
-    const bool dl_ok = d->dtype == WTC_FP32 && a.vec && k == 5 && a.Hq == a.Wq && (a.Hq == 32 || a.Hq == 64);
+    const bool dl_ok = d->dtype == WTC_FP32 && a.vec && (k == 5 || (k == 7 && d->L == 0)) && a.Hq == a.Wq &&
+                       (a.Hq == 32 || a.Hq == 64);
     for (const int variant : {-1, 0, 2, 1}) {
         const bool dl = variant < 0;
         const int bovl = dl ? 0 : variant;

@@ -15,6 +15,7 @@ bool launch_fused_static_p32(const FusedArgs&, int, int, int, int, size_t, int, 
 bool launch_fused_static_p128a(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
 bool launch_fused_static_p128b(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
 bool launch_fused_static_small(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
+bool launch_fused_static_dw(const FusedArgs&, int, int, int, int, int, size_t, int, void*, int*);
 
 namespace {
 
@@ -83,6 +84,10 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
 
 int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nthr, size_t lds_bytes,
                  int grid, void* stream) {
+    if (k == 5 || k == 7) {
+        int err = 0;
+        if (launch_fused_static_dw(a, k, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err)) return err;
+    }
     if (k == 5) {
         // fixed-geometry kernels for the plane classes compiled in; else runtime geometry
         int err = 0;

@@ -287,6 +287,7 @@ __device__ __forceinline__ float wave_sum(float v, int width_mask_from) {
 // ---------------------------------------------------------------------------
 struct RtGeom {
     static constexpr bool kDL = false;   // the runtime-geometry kernel stages planes through registers
+    static constexpr bool kNoLevels = false;
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
     __device__ int Lm() const { return a.Lm; }
@@ -322,6 +323,7 @@ template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL
 struct CtGeom {
     static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, DLV);
     static constexpr bool kDL = DLV;
+    static constexpr bool kNoLevels = LM == 0;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -386,7 +388,8 @@ __device__ __forceinline__ void haar4(float a, float b, float c, float d, float 
 }
 
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu((BWD || BPQ > 1) ? 2 : 3))) wtc_fused_kernel(const FusedArgs a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(BWD, BPQ, G::kNoLevels))))
+wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
     // Direct-load mode: planes are copied from device memory into their LDS slot
     // by DMA (global_load_lds), one plane ahead, with no register staging.

@@ -205,3 +205,13 @@ def test_full_size_sampled(name):
 @pytest.mark.parametrize("L", [1, 2, 3, 4, 5])
 def test_full_size_sweep_sampled(L):
     _full_sampled(WORKLOADS["sweep_b64c96_128x128"], L)
+
+
+@pytest.mark.parametrize("k", [5, 7])
+def test_full_size_dwconv_sampled(k):
+    """The plain depthwise-conv paths that WTConv is timed against: L = 0 at the
+    headline block shape, k = 5 and k = 7, in the benchmark's launch configuration."""
+    import dataclasses
+    wl_ = dataclasses.replace(WORKLOADS["stage1_b32c96_64x64_L3"], name=f"stage1_L0_k{k}", L=0, k=k, L_max=0,
+                              sweep=())
+    _full_sampled(wl_, 0)
