@@ -20,9 +20,13 @@ constexpr int kMaxK = 7;
 // of levels >= f and the later arrays, over the level-0 plane][tail]; the early
 // bands of levels >= f are then written only after the whole workgroup is done
 // reading the level-0 plane, and their rings are re-zeroed per plane.
-// Direct-load layout ("dl"): nothing overlaps the level-0 plane, so the next
-// plane can be copied into it by DMA while the current one is still being
-// processed; the backward adds a plane of x (row stride Wq + 4, no halo).
+// Layout modes: 0 = later arrays may overlap the level-0 plane (when they fit
+// in it); 2 = nothing overlaps it (no per-plane ring re-zeroing); 1 = direct
+// loads ("dl"): nothing overlaps it, so the next plane can be copied into the
+// slot by DMA while the current one is still being processed.  fp32 planes
+// land in the level-0 plane itself and the backward adds a plane of x (row
+// stride Wq + 4, no halo); bf16 planes land in a staging area of raw 16-bit
+// pixels (H*W/2 words) and are widened into the level-0 plane per plane.
 struct Layout {
     int early_lv;      // levels analysed in registers during the level-0 phase (<= 3)
     int overlap;       // later arrays overlap the level-0 plane (rings re-zeroed per plane)
@@ -34,21 +38,25 @@ struct Layout {
     int yd_off[kMaxLm + 1];                    // Y'_i (i >= 3), [4][Hq_i][Wq_i]
     int xb_off[kMaxLm + 1];                    // backward: bands of x (i >= 3), [4][Hq_i][Wq_i]
     int tail_off;                              // tail term rho * kappa
-    int dl;                                    // direct-load layout
-    int xp_off, xp_S;                          // dl backward: x plane [Hq][xp_S]
+    int mode;                                  // 0, 1 (direct loads) or 2 (no overlap)
+    int dl;                                    // mode == 1
+    int xp_off, xp_S;                          // dl fp32 backward: x plane [Hq][xp_S]
+    int st_off;                                // dl bf16: staging of the raw plane (H*W/2 words)
 };
 
 constexpr int lay_round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 // The one definition of the slot layout, evaluated on the host for the
 // runtime-geometry kernel and at compile time for the fixed-geometry ones.
-constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd, int bovl,
-                             bool dl = false) {
+constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd, int bovl, int mode = 0,
+                             int esize = 4) {
     Layout L{};
     const int R = k / 2;
     L.early_lv = Lm < early_req ? Lm : early_req;
+    L.mode = mode;
+    const bool dl = mode == 1;
     L.dl = dl ? 1 : 0;
-    if (dl) bovl = 0;
+    if (mode != 0) bovl = 0;
     int off = 0;
     for (int i = 1; i <= Lm; ++i) {
         L.b_rows[i] = (Hq >> i) + 2 * R;
@@ -107,7 +115,9 @@ constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool 
     }
     L.a0_off = off;
     int r2_base = off;
-    if (r2 <= a0_size && !dl) {
+    // mode 2 names a layout of its own only where mode 0 would overlap
+    if (mode == 2 && !(r2 > 0 && r2 <= a0_size)) L.mode = mode = 0;
+    if (r2 <= a0_size && mode == 0) {
         L.overlap = r2 > 0 ? 1 : 0;
         off += a0_size;
     } else {
@@ -121,7 +131,11 @@ constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool 
         L.yd_off[i] = r2_base + rel_y[i];
         if (bwd) L.xb_off[i] = r2_base + rel_x[i];
     }
-    if (dl && bwd) {
+    if (dl && esize == 2) {
+        L.st_off = lay_round_up(off, 4);
+        off = L.st_off + lay_round_up(Hq * Wq / 2, 4);
+    }
+    if (dl && bwd && esize == 4) {
         // x rows 16-byte aligned; stride = 4 (mod 8) floats keeps the 4x4 block
         // reads of two vertically adjacent lanes in different banks
         L.xp_off = lay_round_up(off, 4);

@@ -115,18 +115,27 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         if (better) best = Cand{lay, NP, nthr, bpq, wgs, score};
     };
     if (a.qpp > 256) return WTC_ESHAPE;
-    // direct loads (DMA into the LDS slot): fp32 rows of 4-pixel vectors, on the
-    // plane classes with fixed-geometry instances of that mode, one plane per
+    // direct loads (DMA into the LDS slot, layout mode 1): rows of 4-pixel
+    // vectors on the plane classes with fixed-geometry instances of that mode
+    // (fp32 32x32 and 64x64; bf16 32x32 backward only: its forward measured
+    // faster staging through registers, 54 us against 70 us), one plane per
     // workgroup; tried first, so it wins ties
-    const bool dl_ok = d->dtype == WTC_FP32 && a.vec && (k == 5 || (k == 7 && d->L == 0)) && a.Hq == a.Wq &&
-                       (a.Hq == 32 || a.Hq == 64);
-    for (const int variant : {-1, 0, 2, 1}) {
-        const bool dl = variant < 0;
-        const int bovl = dl ? 0 : variant;
+    const int esz = d->dtype == WTC_BF16 ? 2 : 4;
+    const bool dl_ok = a.vec && a.Hq == a.Wq &&
+                       ((d->dtype == WTC_FP32 && (k == 5 || (k == 7 && d->L == 0)) && (a.Hq == 32 || a.Hq == 64)) ||
+                        (d->dtype == WTC_BF16 && bwd && k == 5 && a.Hq == 32));
+    // then the layout without overlap (mode 2), which spares the per-plane ring
+    // re-zeroing and wins ties against the overlapping one (32x32 bf16 forward:
+    // 52 us against 54 us)
+    for (const int variant : {-1, -2, 0, 2, 1}) {
+        const bool dl = variant == -1;
+        const int bovl = variant < 0 ? 0 : variant;
+        const int mode = dl ? 1 : (variant == -2 ? 2 : 0);
         if (dl && !dl_ok) continue;
         if (bovl > a.Lm) continue;
-        Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl, dl);
-        if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl, dl);
+        Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl, mode, esz);
+        if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl, mode, esz);
+        if (variant == -2 && lay.mode != 2) continue;   // same layout as mode 0
         if (bovl > 0 && !bwd && best.score >= 0) continue;
         if (a.qpp <= 64) {
             // several planes per workgroup when planes are small

@@ -313,16 +313,17 @@ struct RtGeom {
     __device__ int tail_off() const { return a.lay.tail_off; }
     __device__ int xp_off() const { return a.lay.xp_off; }
     __device__ int xp_S() const { return a.lay.xp_S; }
+    __device__ int st_off() const { return a.lay.st_off; }
     __device__ int wts_off() const { return a.wts_off; }
     __device__ int red_off() const { return a.red_off; }
     __device__ int dsub() const { return a.dsub; }
     __device__ int P() const { return a.P; }
 };
 
-template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, bool DLV>
+template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, int MODE, int ESZ>
 struct CtGeom {
-    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, DLV);
-    static constexpr bool kDL = DLV;
+    static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, MODE, ESZ);
+    static constexpr bool kDL = MODE == 1;
     static constexpr bool kNoLevels = LM == 0;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
@@ -349,6 +350,7 @@ struct CtGeom {
     __device__ static constexpr int tail_off() { return lay.tail_off; }
     __device__ static constexpr int xp_off() { return lay.xp_off; }
     __device__ static constexpr int xp_S() { return lay.xp_S; }
+    __device__ static constexpr int st_off() { return lay.st_off; }
     __device__ static constexpr int wts_off() { return NPV * lay.slot; }
     __device__ static constexpr int red_off() { return 0; }
     __device__ static constexpr int dsub() { return NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1; }
@@ -394,7 +396,9 @@ wtc_fused_kernel(const FusedArgs a) {
     // Direct-load mode: planes are copied from device memory into their LDS slot
     // by DMA (global_load_lds), one plane ahead, with no register staging.
     constexpr bool DL = G::kDL;
-    static_assert(!DL || (sizeof(ST) == 4 && VEC && BPQ == 1), "direct loads: fp32 rows, one block per quad");
+    static_assert(!DL || (VEC && BPQ == 1), "direct loads: 4-pixel rows, one block per quad");
+    constexpr bool SDL = DL && sizeof(ST) == 2;           // bf16: raw plane staged, widened per plane
+    constexpr bool XDL = DL && BWD && sizeof(ST) == 4;    // fp32 backward: x plane in LDS too
     constexpr int PFF = pf_capacity(BWD, BPQ);  // prefetch capacity, floats per thread
     constexpr int PFU = DL ? 1 : (VEC ? PFF / 4 : PFF);   // prefetch units (4-pixel groups or pixels)
     constexpr int UW = VEC ? 4 : 1;
@@ -582,7 +586,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // is the chunk start + 4 l bytes, so lanes past the row end are masked off.
     // Cells outside the interior are never written (zeroed once per segment).
     auto dl_issue = [&](const ST* base, int roff, int rS, int rr, int rc, int bbn) {
-        if constexpr (DL) {
+        if constexpr (DL && !SDL) {
             constexpr int CPR = (G::Wq() + 63) / 64;
             const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
             const int nw = nthr >> 6;
@@ -602,15 +606,33 @@ wtc_fused_kernel(const FusedArgs a) {
             }
         }
     };
-    if (pf_on) pf_issue(b_begin);
-    if constexpr (DL) {
-        if constexpr (BWD) {
-            for (int s2 = 0; s2 < g.NP(); ++s2)
-                zero_ring(lds + s2 * g.slot() + g.xp_off(), g.Hq(), g.xp_S(), 0, a.H, 0, a.W, tid, nthr);
-            dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, b_begin);
+    // bf16: the raw planes (H*W 16-bit pixels, contiguous) are copied word by
+    // word into the staging area, 64 words per wave instruction
+    auto stage_issue = [&](int bbn) {
+        if constexpr (SDL) {
+            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
+            const int nw = nthr >> 6;
+            const int words = (a.H * a.W) >> 1, chunks = (words + 63) >> 6;
+            for (int j = wave; j < g.NP() * chunks; j += nw) {
+                const int s2 = g.NP() == 1 ? 0 : j / chunks, ch = j - s2 * chunks;
+                if (bbn + s2 >= b_end) continue;
+                const int i = ch * 64 + lane;
+                if (i < words)
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + c) * plane_sz) +
+                                      i),
+                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + ch * 64), 4, 0, 0);
+            }
         }
-        dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, b_begin);
+    };
+    if (pf_on) pf_issue(b_begin);
+    if constexpr (XDL) {
+        for (int s2 = 0; s2 < g.NP(); ++s2)
+            zero_ring(lds + s2 * g.slot() + g.xp_off(), g.Hq(), g.xp_S(), 0, a.H, 0, a.W, tid, nthr);
+        dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, b_begin);
     }
+    if constexpr (DL && !SDL) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, b_begin);
+    if constexpr (SDL) stage_issue(b_begin);
 
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
@@ -624,6 +646,27 @@ wtc_fused_kernel(const FusedArgs a) {
             // previous plane is fully consumed
             __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
             lds_barrier();
+            if constexpr (SDL) {
+                // widen the staged 16-bit pixels into the level-0 plane (4 per unit)
+                typedef uint32_t lds_u2 __attribute__((ext_vector_type(2)));
+                const int wq = a.W >> 2, per_plane = a.H * wq;
+                for (int e = tid; e < g.NP() * per_plane; e += nthr) {
+                    const int s2 = g.NP() == 1 ? 0 : e / per_plane, m = e - s2 * per_plane;
+                    if (bb + s2 >= b_end) continue;
+                    const int y = m / wq, xq = m - y * wq;
+                    float* Sl = lds + s2 * g.slot();
+                    const lds_u2 v = *reinterpret_cast<const lds_u2*>(Sl + g.st_off() + 2 * m);
+                    float* d = Sl + g.a0_off() + (y + R) * g.a0_S() + R + 4 * xq;
+                    *reinterpret_cast<lds_f2*>(d) = lds_f2{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u)};
+                    *reinterpret_cast<lds_f2*>(d + 2) =
+                        lds_f2{__uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u)};
+                }
+                lds_barrier();
+                // the staging area is free: the next planes' copies land meanwhile
+                // (backward: after this plane's last x load, whose wait would
+                // otherwise also wait for the copy, vector-memory counts being in order)
+                if (!BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP());
+            }
         } else {
         lds_barrier();  // the previous plane is fully consumed
 
@@ -699,7 +742,7 @@ wtc_fused_kernel(const FusedArgs a) {
             float w[KK];
             load_w<K, BWD>(wbase, w);
             float xo[4][4];
-            if constexpr (BWD && DL) {
+            if constexpr (XDL) {
                 const float* xr = S + g.xp_off() + py0 * g.xp_S() + px0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lds_row<4, 4>(xr + i * g.xp_S(), xo[i]);
@@ -771,7 +814,7 @@ wtc_fused_kernel(const FusedArgs a) {
         }
         lds_barrier();
         // the level-0 plane is dead: the next planes' copies land during the rest
-        if (DL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP());
+        if (DL && !SDL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP());
 
         // ---------------- phase 3: analysis of levels early_lv+1..Lm ----------------
         for (int i = g.early() + 1; i <= Lm; ++i) {
@@ -812,7 +855,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 for (int jy = 0; jy < 4; ++jy) {
                     float r0[2][4], r1[2][4];
                     const int y0 = 8 * qy + 2 * jy;
-                    if constexpr (DL) {
+                    if constexpr (XDL) {
                         const float* xr = S + g.xp_off() + y0 * g.xp_S() + 8 * qx;
                         lds_row<4, 4>(xr, r0[0]);
                         lds_row<4, 4>(xr + 4, r0[1]);
@@ -882,12 +925,14 @@ wtc_fused_kernel(const FusedArgs a) {
             if (tail && qpb[s] == 0 && t == 0) S[g.tail_off()] = S[g.b_off(Lm) + R * g.b_S(Lm) + R] * kappa;
         }
 
+        if (SDL && BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP());
+
         // ---------------- phase 4b: x bands of levels >= 4 (backward) ----------------
         if constexpr (BWD) {
             if (Lm >= 3) {
                 lds_barrier();  // band 0 of level 3 (x) written in phase 4a
                 // every wave is done with the x plane: the next one lands meanwhile
-                if (DL && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
+                if (XDL && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
                 for (int i = 4; i <= Lm; ++i) {
                     const int hi = g.Hq() >> i, wi = g.Wq() >> i, wp = g.Wq() >> (i - 1);
                     const int pi = hi * wi;
@@ -973,7 +1018,7 @@ wtc_fused_kernel(const FusedArgs a) {
             }
         }
         lds_barrier();
-        if (DL && BWD && Lm < 3 && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
+        if (XDL && Lm < 3 && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
 
         // ---------------- phase 4d: levels 1, 2 results in place ----------------
 #pragma unroll
@@ -1176,14 +1221,14 @@ namespace fused_detail {
 
 // Launch the fixed-geometry instantiation if the plan matches it exactly.
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
-          int NTHR, int BOVL, bool DLV = false>
+          int NTHR, int BOVL, int MODE = 0>
 bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
                 hipError_t* err) {
     if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
-        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || (a.lay.dl != 0) != DLV)
+        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || a.lay.mode != MODE)
         return false;
-    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, DLV>>(a, nthr, lds,
-                                                                                               grid, st);
+    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST)>>(
+        a, nthr, lds, grid, st);
     return true;
 }
 

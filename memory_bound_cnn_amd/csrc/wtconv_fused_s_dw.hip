@@ -14,13 +14,13 @@ bool launch_fused_static_dw(const FusedArgs& a, int k, int dtype, int bwd, int b
     bool hit = false;
     if (dtype != WTC_FP32 || a.L != 0) return false;
     if (!hit && k == 5 && bwd == 0)
-        hit = try_static<5, float, 0, 1, true, 64, 64, 0, 0, 1, 256, 0, true>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 0, 1, true, 64, 64, 0, 0, 1, 256, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && k == 5 && bwd == 1)
-        hit = try_static<5, float, 1, 1, true, 64, 64, 0, 0, 1, 256, 0, true>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 1, 1, true, 64, 64, 0, 0, 1, 256, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && k == 7 && bwd == 0)
-        hit = try_static<7, float, 0, 1, true, 64, 64, 0, 0, 1, 256, 0, true>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<7, float, 0, 1, true, 64, 64, 0, 0, 1, 256, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && k == 7 && bwd == 1)
-        hit = try_static<7, float, 1, 1, true, 64, 64, 0, 0, 1, 256, 0, true>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<7, float, 1, 1, true, 64, 64, 0, 0, 1, 256, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     *err = (int)e;
     return hit;
 }

@@ -12,9 +12,9 @@ bool launch_fused_static_p64(const FusedArgs& a, int dtype, int bwd, int bpq, in
     hipError_t e = hipSuccess;
     bool hit = false;
     if (!hit && dtype == WTC_FP32 && bwd == 0)
-        hit = try_static<5, float, 0, 1, true, 64, 64, 3, 3, 1, 256, 0, true>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 0, 1, true, 64, 64, 3, 3, 1, 256, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
-        hit = try_static<5, float, 1, 1, true, 64, 64, 3, 3, 1, 256, 0, true>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, float, 1, 1, true, 64, 64, 3, 3, 1, 256, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     *err = (int)e;
     return hit;
 }
