@@ -240,12 +240,17 @@ struct UnfusedPlan {
 // workgroups per channel of the baseline's weight-gradient correlation
 int unfused_corr_blocks(int nb, int nch);
 int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p);
+// stage 0: the whole pipeline; 1: only the analysis cascades (into the
+// workspace); 2: everything after them, with `zext` (may be null) added to the
+// LL band of the deepest level in the synthesis -- the term of deeper levels
+// computed elsewhere (forward: their output Z_{L+1}; backward: dLL_L).
 int unfused_forward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const float* w0,
                     const float* s0, const float* b0, const float* wl, const float* sl, void* out,
-                    char* ws, void* stream);
+                    char* ws, void* stream, int stage = 0, const float* zext = nullptr);
 int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const void* g,
                      const float* w0, const float* s0, const float* wl, const float* sl, void* dx,
                      float* dw0, float* ds0, float* db0, float* dwl, float* dsl, char* ws,
-                     void* stream);
+                     void* stream, int stage = 0, const float* zext = nullptr);
+int launch_fill_zero(float* p, int n, void* stream);
 
 }  // namespace wtc

@@ -186,6 +186,179 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     return WTC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Planes beyond the on-chip pipeline: peel one wavelet level.
+// The levels >= 2 of WTConv are WTConv itself (one level fewer, no base conv)
+// applied to the level-1 LL band, so such a plane runs level 1 and the base
+// conv with the level-by-level kernels, and its LL band (half the size in each
+// direction) recursively through the fused entry points -- fused as soon as it
+// fits.  Workspace: [level-1 tensors][LL copies][deeper result][zero / scratch
+// parameters][the sub-problem's workspace].
+// ---------------------------------------------------------------------------
+constexpr int kMaxPeel = 8;
+size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+struct PeelPlan {
+    wtc_desc d1, sub;   // level 1 of this plane; the LL problem (L - 1 levels, fp32)
+    UnfusedPlan u;
+    size_t n1;          // floats of one LL tensor [B, C, h1, w1]
+    size_t a_off, b_off, c_off, par_off, sub_off, total;
+};
+
+size_t fused_fwd_ws(const wtc_desc* d, int depth, int* st);
+size_t fused_bwd_ws(const wtc_desc* d, int depth, int* st);
+
+int peel_plan(const wtc_desc* d, bool bwd, int depth, PeelPlan* pp) {
+    if (depth >= kMaxPeel) return WTC_ESHAPE;
+    pp->d1 = *d;
+    pp->d1.L = std::min(d->L, 1);
+    int st = unfused_plan(&pp->d1, bwd ? 1 : 0, &pp->u);
+    if (st != WTC_OK) return st;
+    const int h1 = (d->H + 1) / 2, w1 = (d->W + 1) / 2;
+    pp->n1 = (size_t)d->B * d->C * h1 * w1;
+    pp->sub = wtc_desc{d->B, d->C, h1, w1, d->L - 1, d->k, WTC_FP32, 0};
+    size_t off = al256(pp->u.total);
+    pp->a_off = off;   // forward: LL of x;  backward: LL of x
+    pp->b_off = off = off + al256(pp->n1 * 4);   // forward: Z_2;  backward: LL of g
+    pp->c_off = off = off + al256(pp->n1 * 4);   // backward: dLL_1
+    if (bwd) off += al256(pp->n1 * 4);
+    pp->par_off = off;  // zero scale and bias (2C); backward: unused base gradients (C k^2 + 2C)
+    off += al256((size_t)4 * (2 * d->C + (bwd ? d->C * d->k * d->k + 2 * d->C : 0)));
+    pp->sub_off = off;
+    if (d->L < 2) {
+        pp->total = pp->u.total;
+        return WTC_OK;
+    }
+    const size_t sw = bwd ? fused_bwd_ws(&pp->sub, depth + 1, &st) : fused_fwd_ws(&pp->sub, depth + 1, &st);
+    if (st != WTC_OK) return st;
+    pp->total = off + sw;
+    return WTC_OK;
+}
+
+size_t fused_fwd_ws(const wtc_desc* d, int depth, int* st) {
+    FusedPlan p;
+    *st = plan_fused(d, false, &p);
+    if (*st == WTC_OK) return 0;
+    if (*st != WTC_ESHAPE) return 0;
+    PeelPlan pp;
+    *st = peel_plan(d, false, depth, &pp);
+    return *st == WTC_OK ? pp.total : 0;
+}
+
+size_t fused_bwd_ws(const wtc_desc* d, int depth, int* st) {
+    FusedPlan p;
+    *st = plan_fused(d, true, &p);
+    if (*st == WTC_OK) return (size_t)p.nrec * p.a.P * sizeof(float);
+    if (*st != WTC_ESHAPE) return 0;
+    PeelPlan pp;
+    *st = peel_plan(d, true, depth, &pp);
+    return *st == WTC_OK ? pp.total : 0;
+}
+
+// LL band (band 0) of level-1 bands [B*C][4][h1*w1] -> contiguous [B*C][h1*w1]
+int copy_ll(float* dst, const float* bands, const PeelPlan& pp, hipStream_t st) {
+    const size_t plane = pp.n1 / ((size_t)pp.sub.B * pp.sub.C) * sizeof(float);
+    return hipMemcpy2DAsync(dst, plane, bands, 4 * plane, plane, (size_t)pp.sub.B * pp.sub.C,
+                            hipMemcpyDeviceToDevice, st) == hipSuccess ? WTC_OK : WTC_EHIP;
+}
+
+int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
+                  const float* wl, const float* sl, void* out, char* ws, size_t wsb, void* stream, int depth) {
+    FusedPlan p;
+    int st = plan_fused(d, false, &p);
+    if (st == WTC_OK) {
+        FusedArgs& a = p.a;
+        a.src = x;
+        a.aux = nullptr;
+        a.w0 = w0; a.s0 = s0; a.b0 = b0; a.wl = wl; a.sl = sl;
+        a.dst = out;
+        a.partials = nullptr;
+        const int e = p.tiny ? launch_tiny(a, d->dtype, 0, p.grid, stream)
+                             : launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
+        return e == 0 ? WTC_OK : WTC_EHIP;
+    }
+    if (st != WTC_ESHAPE) return st;
+    PeelPlan pp;
+    st = peel_plan(d, false, depth, &pp);
+    if (st != WTC_OK) return st;
+    if (pp.total > 0 && (!ws || wsb < pp.total)) return WTC_EWORKSPACE;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    st = unfused_forward(&pp.d1, pp.u, x, w0, s0, b0, wl, sl, out, ws, stream, 1, nullptr);
+    if (st != WTC_OK) return st;
+    const float* zext = nullptr;
+    if (d->L >= 2) {
+        float* ll = reinterpret_cast<float*>(ws + pp.a_off);
+        float* z2 = reinterpret_cast<float*>(ws + pp.b_off);
+        float* zero = reinterpret_cast<float*>(ws + pp.par_off);
+        const size_t lvl = (size_t)4 * d->C * d->k * d->k;
+        if ((st = copy_ll(ll, reinterpret_cast<const float*>(ws + pp.u.s_off[1]), pp, hs)) != WTC_OK) return st;
+        if (launch_fill_zero(zero, 2 * d->C, stream) != 0) return WTC_EHIP;
+        // Z_2 = WTConv of LL_1 with levels 2..L; scale and bias 0 remove its base conv
+        st = fused_fwd_run(&pp.sub, ll, w0, zero, zero + d->C, wl + lvl, sl + 4 * d->C, z2, ws + pp.sub_off,
+                           wsb - pp.sub_off, stream, depth + 1);
+        if (st != WTC_OK) return st;
+        zext = z2;
+    }
+    return unfused_forward(&pp.d1, pp.u, x, w0, s0, b0, wl, sl, out, ws, stream, 2, zext);
+}
+
+int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
+                  const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0, float* dwl,
+                  float* dsl, char* ws, size_t wsb, void* stream, int depth) {
+    FusedPlan p;
+    int st = plan_fused(d, true, &p);
+    if (st == WTC_OK) {
+        const size_t need = (size_t)p.nrec * p.a.P * sizeof(float);
+        if (!ws || wsb < need) return WTC_EWORKSPACE;
+        FusedArgs& a = p.a;
+        a.src = g;
+        a.aux = x;
+        a.w0 = w0; a.s0 = s0; a.b0 = nullptr; a.wl = wl; a.sl = sl;
+        a.dst = dx;
+        a.partials = reinterpret_cast<float*>(ws);
+        int e = p.tiny ? launch_tiny(a, d->dtype, 1, p.grid, stream)
+                       : launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
+        if (e != 0) return WTC_EHIP;
+        FinalizeArgs f;
+        f.partials = a.partials;
+        f.w0 = w0; f.s0 = s0; f.wl = wl; f.sl = sl;
+        f.dw0 = dw0; f.ds0 = ds0; f.db0 = db0; f.dwl = dwl; f.dsl = dsl;
+        f.C = d->C; f.B = d->B; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.ppw = a.ppw; f.P = a.P;
+        f.chunks = p.tiny ? p.nchunk : 0;
+        e = launch_finalize(f, stream);
+        return e == 0 ? WTC_OK : WTC_EHIP;
+    }
+    if (st != WTC_ESHAPE) return st;
+    PeelPlan pp;
+    st = peel_plan(d, true, depth, &pp);
+    if (st != WTC_OK) return st;
+    if (!ws || wsb < pp.total) return WTC_EWORKSPACE;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    st = unfused_backward(&pp.d1, pp.u, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream, 1, nullptr);
+    if (st != WTC_OK) return st;
+    const float* zext = nullptr;
+    if (d->L >= 2) {
+        float* xll = reinterpret_cast<float*>(ws + pp.a_off);
+        float* gll = reinterpret_cast<float*>(ws + pp.b_off);
+        float* dll = reinterpret_cast<float*>(ws + pp.c_off);
+        float* zero = reinterpret_cast<float*>(ws + pp.par_off);
+        float* scratch = zero + 2 * d->C;   // the sub-problem's base gradients (unused)
+        const int KK = d->k * d->k;
+        const size_t lvl = (size_t)4 * d->C * KK;
+        if ((st = copy_ll(xll, reinterpret_cast<const float*>(ws + pp.u.s_off[1]), pp, hs)) != WTC_OK) return st;
+        if ((st = copy_ll(gll, reinterpret_cast<const float*>(ws + pp.u.dt_off[1]), pp, hs)) != WTC_OK) return st;
+        if (launch_fill_zero(zero, 2 * d->C, stream) != 0) return WTC_EHIP;
+        // levels 2..L: the backward of WTConv(LL_1) with upstream gradient LL_1(g)
+        // (the level-1 synthesis adjoint); scale 0 removes its base conv from dLL_1
+        st = fused_bwd_run(&pp.sub, xll, gll, w0, zero, wl + lvl, sl + 4 * d->C, dll, scratch, scratch + d->C * KK,
+                           scratch + d->C * KK + d->C, dwl + lvl, dsl + 4 * d->C, ws + pp.sub_off, wsb - pp.sub_off,
+                           stream, depth + 1);
+        if (st != WTC_OK) return st;
+        zext = dll;
+    }
+    return unfused_backward(&pp.d1, pp.u, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream, 2, zext);
+}
+
 double spec_level_area(const wtc_desc* d, int i) {
     int h = d->H, w = d->W;
     for (int l = 0; l < i; ++l) {
@@ -193,6 +366,68 @@ double spec_level_area(const wtc_desc* d, int i) {
         w = (w + 1) / 2;
     }
     return (double)h * w;
+}
+
+double io_unfused(const wtc_desc* d, int dir) {
+    const double e = d->dtype == WTC_BF16 ? 2.0 : 4.0;
+    const double KK = (double)d->k * d->k;
+    const double BC = (double)d->B * d->C;
+    const double N = BC * d->H * d->W;
+    const double params = 4.0 * (d->C * KK * (1 + 4.0 * d->L) + d->C * (2.0 + 4.0 * d->L));
+    UnfusedPlan p;
+    if (unfused_plan(d, dir, &p) != WTC_OK) return -1.0;
+    // Level-by-level baseline: the bytes its kernels move, each tensor read or
+    // written once per kernel that touches it (stencil halos hit in cache).
+    // Intermediates are float32; x, g, out and dx use the storage dtype.
+    const double f4 = 4.0;
+    const int kk1 = d->k * d->k + 1;
+    auto band = [&](int i) { return BC * spec_level_area(d, i) * f4; };   // one band of level i
+    double t = 0.0;
+    // analysis cascade (forward: of x; backward: of g and of x): read LL_{i-1}, write 4 bands
+    const double casc_n = dir == 0 ? 1.0 : 2.0;
+    for (int i = 1; i <= d->L; ++i) t += casc_n * ((i == 1 ? N * e : band(i - 1)) + 4.0 * band(i));
+    // subband conv per level: read 4 bands, write 4 bands
+    for (int i = 1; i <= d->L; ++i) t += 8.0 * band(i);
+    // synthesis per level: read 4 bands (+ the deeper partial result), write the finer grid
+    for (int i = 1; i <= d->L; ++i) t += 4.0 * band(i) + (i < d->L ? band(i) : 0.0) + band(i - 1);
+    // base: read the convolved tensor and Z_1 (dLL_0), write out (dx)
+    t += 2.0 * N * e + (d->L > 0 ? band(0) : 0.0);
+    if (dir == 0) return t + params;
+    // correlations: per level read dT_i and S_i (8 bands), base read g and x;
+    // partials written and read back; parameters read twice, gradients written
+    for (int i = 1; i <= d->L; ++i) {
+        t += 8.0 * band(i);
+        t += 2.0 * f4 * unfused_corr_blocks(d->B, 4 * d->C) * 4.0 * d->C * kk1;
+    }
+    t += 2.0 * N * e + 2.0 * f4 * unfused_corr_blocks(d->B, d->C) * (double)d->C * kk1;
+    return t + 3.0 * params;
+}
+
+double io_fused(const wtc_desc* d, int dir, int depth) {
+    const double e = d->dtype == WTC_BF16 ? 2.0 : 4.0;
+    const double KK = (double)d->k * d->k;
+    const double BC = (double)d->B * d->C;
+    const double N = BC * d->H * d->W;
+    const double params = 4.0 * (d->C * KK * (1 + 4.0 * d->L) + d->C * (2.0 + 4.0 * d->L));
+    FusedPlan p;
+    const int st = plan_fused(d, dir == 1, &p);
+    if (st == WTC_OK) {
+        if (dir == 0) return 2.0 * N * e + params;
+        const double partials = 4.0 * (double)p.nrec * p.a.P;
+        // read x and g, write dx; params read; partials written then read; grads written
+        return 3.0 * N * e + params + 2.0 * partials + params;
+    }
+    // peeled plane: level 1 and the base level by level, the LL band recursively
+    PeelPlan pp;
+    if (st != WTC_ESHAPE || peel_plan(d, dir == 1, depth, &pp) != WTC_OK) return -1.0;
+    double t = io_unfused(&pp.d1, dir);
+    if (d->L >= 2) {
+        const double ll = 4.0 * (double)pp.n1;
+        // LL copies (forward: x; backward: x and g), read and written; the deeper
+        // term read once more by the level-1 synthesis
+        t += (dir == 0 ? 2.0 : 4.0) * ll + ll + io_fused(&pp.sub, dir, depth + 1);
+    }
+    return t;
 }
 
 }  // namespace
@@ -206,7 +441,7 @@ const char* wtconv_status_string(int s) {
     switch (s) {
         case WTC_OK: return "ok";
         case WTC_EINVAL: return "invalid argument";
-        case WTC_ESHAPE: return "plane too large for the on-chip plane pipeline";
+        case WTC_ESHAPE: return "shape outside the supported limits";
         case WTC_EDTYPE: return "unsupported dtype or layout";
         case WTC_EWORKSPACE: return "workspace missing or too small";
         case WTC_EHIP: return "HIP launch or runtime error";
@@ -215,37 +450,27 @@ const char* wtconv_status_string(int s) {
 }
 
 size_t wtconv_forward_workspace(const wtc_desc* d) {
-    (void)d;
-    return 0;
+    if (check_desc(d) != WTC_OK) return 0;
+    int st = WTC_OK;
+    const size_t n = fused_fwd_ws(d, 0, &st);
+    return st == WTC_OK ? n : 0;
 }
 
 int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0,
                    const float* b0, const float* wl, const float* sl, void* out, void* workspace,
                    size_t workspace_bytes, void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     int st = check_desc(d);
     if (st != WTC_OK) return st;
     if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
-    FusedPlan p;
-    st = plan_fused(d, false, &p);
-    if (st != WTC_OK) return st;
-    FusedArgs& a = p.a;
-    a.src = x;
-    a.aux = nullptr;
-    a.w0 = w0; a.s0 = s0; a.b0 = b0; a.wl = wl; a.sl = sl;
-    a.dst = out;
-    a.partials = nullptr;
-    const int e = p.tiny ? launch_tiny(a, d->dtype, 0, p.grid, stream)
-                         : launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
-    return e == 0 ? WTC_OK : WTC_EHIP;
+    return fused_fwd_run(d, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes, stream, 0);
 }
 
 size_t wtconv_backward_workspace(const wtc_desc* d) {
-    FusedPlan p;
-    if (plan_fused(d, true, &p) != WTC_OK) return 0;
-    return (size_t)p.nrec * p.a.P * sizeof(float);
+    if (check_desc(d) != WTC_OK) return 0;
+    int st = WTC_OK;
+    const size_t n = fused_bwd_ws(d, 0, &st);
+    return st == WTC_OK ? n : 0;
 }
 
 int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -256,28 +481,8 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     if (st != WTC_OK) return st;
     if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
-    FusedPlan p;
-    st = plan_fused(d, true, &p);
-    if (st != WTC_OK) return st;
-    const size_t need = (size_t)p.nrec * p.a.P * sizeof(float);
-    if (!workspace || workspace_bytes < need) return WTC_EWORKSPACE;
-    FusedArgs& a = p.a;
-    a.src = g;
-    a.aux = x;
-    a.w0 = w0; a.s0 = s0; a.b0 = nullptr; a.wl = wl; a.sl = sl;
-    a.dst = dx;
-    a.partials = static_cast<float*>(workspace);
-    int e = p.tiny ? launch_tiny(a, d->dtype, 1, p.grid, stream)
-                   : launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
-    if (e != 0) return WTC_EHIP;
-    FinalizeArgs f;
-    f.partials = a.partials;
-    f.w0 = w0; f.s0 = s0; f.wl = wl; f.sl = sl;
-    f.dw0 = dw0; f.ds0 = ds0; f.db0 = db0; f.dwl = dwl; f.dsl = dsl;
-    f.C = d->C; f.B = d->B; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.ppw = a.ppw; f.P = a.P;
-    f.chunks = p.tiny ? p.nchunk : 0;
-    e = launch_finalize(f, stream);
-    return e == 0 ? WTC_OK : WTC_EHIP;
+    return fused_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, static_cast<char*>(workspace),
+                         workspace_bytes, stream, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,46 +553,7 @@ double wtconv_flops(const wtc_desc* d, int dir) {
 
 double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
     if (check_desc(d) != WTC_OK || (dir != 0 && dir != 1) || (impl != 0 && impl != 1)) return -1.0;
-    const double e = d->dtype == WTC_BF16 ? 2.0 : 4.0;
-    const double KK = (double)d->k * d->k;
-    const double BC = (double)d->B * d->C;
-    const double N = BC * d->H * d->W;
-    const double params = 4.0 * (d->C * KK * (1 + 4.0 * d->L) + d->C * (2.0 + 4.0 * d->L));
-    if (impl == 0) {
-        if (dir == 0) return 2.0 * N * e + params;
-        FusedPlan p;
-        if (plan_fused(d, true, &p) != WTC_OK) return -1.0;
-        const double partials = 4.0 * (double)p.nrec * p.a.P;
-        // read x and g, write dx; params read; partials written then read; grads written
-        return 3.0 * N * e + params + 2.0 * partials + params;
-    }
-    UnfusedPlan p;
-    if (unfused_plan(d, dir, &p) != WTC_OK) return -1.0;
-    // Level-by-level baseline: the bytes its kernels move, each tensor read or
-    // written once per kernel that touches it (stencil halos hit in cache).
-    // Intermediates are float32; x, g, out and dx use the storage dtype.
-    const double f4 = 4.0;
-    const int kk1 = d->k * d->k + 1;
-    auto band = [&](int i) { return BC * spec_level_area(d, i) * f4; };   // one band of level i
-    double t = 0.0;
-    // analysis cascade (forward: of x; backward: of g and of x): read LL_{i-1}, write 4 bands
-    const double casc_n = dir == 0 ? 1.0 : 2.0;
-    for (int i = 1; i <= d->L; ++i) t += casc_n * ((i == 1 ? N * e : band(i - 1)) + 4.0 * band(i));
-    // subband conv per level: read 4 bands, write 4 bands
-    for (int i = 1; i <= d->L; ++i) t += 8.0 * band(i);
-    // synthesis per level: read 4 bands (+ the deeper partial result), write the finer grid
-    for (int i = 1; i <= d->L; ++i) t += 4.0 * band(i) + (i < d->L ? band(i) : 0.0) + band(i - 1);
-    // base: read the convolved tensor and Z_1 (dLL_0), write out (dx)
-    t += 2.0 * N * e + (d->L > 0 ? band(0) : 0.0);
-    if (dir == 0) return t + params;
-    // correlations: per level read dT_i and S_i (8 bands), base read g and x;
-    // partials written and read back; parameters read twice, gradients written
-    for (int i = 1; i <= d->L; ++i) {
-        t += 8.0 * band(i);
-        t += 2.0 * f4 * unfused_corr_blocks(d->B, 4 * d->C) * 4.0 * d->C * kk1;
-    }
-    t += 2.0 * N * e + 2.0 * f4 * unfused_corr_blocks(d->B, d->C) * (double)d->C * kk1;
-    return t + 3.0 * params;
+    return impl == 0 ? io_fused(d, dir, 0) : io_unfused(d, dir);
 }
 
 }  // extern "C"

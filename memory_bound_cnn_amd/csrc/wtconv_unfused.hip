@@ -400,23 +400,25 @@ void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const 
 
 template <int K, typename T>
 int fwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const float* w0, const float* s0,
-          const float* b0, const float* wl, const float* sl, T* out, char* ws, hipStream_t st) {
+          const float* b0, const float* wl, const float* sl, T* out, char* ws, hipStream_t st, int stage,
+          const float* zext) {
     const int B = d->B, C = d->C, L = d->L;
     const int P = B * C;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    for (int i = 1; i <= L; ++i) {
+    for (int i = 1; i <= L && stage != 2; ++i) {
         if (i == 1)
             launch_analysis<T>(x, (uint32_t)(p.h[0] * p.w[0]), P, p.h[0], p.w[0], F(p.s_off[1]), p.h[1], p.w[1], st);
         else
             launch_analysis<float>(F(p.s_off[i - 1]), (uint32_t)(4 * p.h[i - 1] * p.w[i - 1]), P, p.h[i - 1],
                                    p.w[i - 1], F(p.s_off[i]), p.h[i], p.w[i], st);
     }
+    if (stage == 1) return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
     for (int i = 1; i <= L; ++i)
         launch_conv<K, float, float>(false, F(p.s_off[i]), 4 * P, 4 * C, p.h[i], p.w[i],
                                      wl + (size_t)(i - 1) * 4 * C * K * K, sl + (size_t)(i - 1) * 4 * C, nullptr,
                                      nullptr, F(p.y_off[i]), st);
     for (int i = L; i >= 1; --i)
-        launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : nullptr, P, p.h[i], p.w[i], F(p.z_off[i]),
+        launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : zext, P, p.h[i], p.w[i], F(p.z_off[i]),
                          p.h[i - 1], p.w[i - 1], st);
     launch_conv<K, T, T>(false, x, P, C, d->H, d->W, w0, s0, b0, L > 0 ? F(p.z_off[1]) : nullptr, out, st);
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
@@ -425,13 +427,13 @@ int fwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const float* w0, 
 template <int K, typename T>
 int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const float* w0, const float* s0,
           const float* wl, const float* sl, T* dx, float* dw0, float* ds0, float* db0, float* dwl, float* dsl,
-          char* ws, hipStream_t st) {
+          char* ws, hipStream_t st, int stage, const float* zext) {
     const int B = d->B, C = d->C, L = d->L;
     const int P = B * C;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     float* part = F(p.part_off);
     // analysis cascades of g (the adjoint of the synthesis) and of x
-    for (int i = 1; i <= L; ++i) {
+    for (int i = 1; i <= L && stage != 2; ++i) {
         if (i == 1) {
             const uint32_t ps = (uint32_t)(p.h[0] * p.w[0]);
             launch_analysis<T>(g, ps, P, p.h[0], p.w[0], F(p.dt_off[1]), p.h[1], p.w[1], st);
@@ -444,6 +446,7 @@ int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const
                                    st);
         }
     }
+    if (stage == 1) return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
     // per level: dS = s * (rot W * dY);  dW, ds from corr(dY, S)
     for (int i = 1; i <= L; ++i) {
         const float* wli = wl + (size_t)(i - 1) * 4 * C * K * K;
@@ -456,7 +459,7 @@ int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const
     }
     // adjoint of the analysis: synthesis of dS, deepest first
     for (int i = L; i >= 1; --i)
-        launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : nullptr, P, p.h[i], p.w[i], F(p.z_off[i]),
+        launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : zext, P, p.h[i], p.w[i], F(p.z_off[i]),
                          p.h[i - 1], p.w[i - 1], st);
     // base: dx = s0 * (rot W0 * g) + dLL_0;  dW0, ds0, db0 from corr(g, x)
     launch_conv<K, T, T>(true, g, P, C, d->H, d->W, w0, s0, nullptr, L > 0 ? F(p.z_off[1]) : nullptr, dx, st);
@@ -515,49 +518,63 @@ namespace {
 
 template <int K>
 int fwd_k(const wtc_desc* d, const UnfusedPlan& p, const void* x, const float* w0, const float* s0,
-          const float* b0, const float* wl, const float* sl, void* out, char* ws, hipStream_t st) {
+          const float* b0, const float* wl, const float* sl, void* out, char* ws, hipStream_t st, int stage,
+          const float* zext) {
     if (d->dtype == WTC_BF16)
         return fwd_t<K, uint16_t>(d, p, static_cast<const uint16_t*>(x), w0, s0, b0, wl, sl,
-                                  static_cast<uint16_t*>(out), ws, st);
-    return fwd_t<K, float>(d, p, static_cast<const float*>(x), w0, s0, b0, wl, sl, static_cast<float*>(out), ws, st);
+                                  static_cast<uint16_t*>(out), ws, st, stage, zext);
+    return fwd_t<K, float>(d, p, static_cast<const float*>(x), w0, s0, b0, wl, sl, static_cast<float*>(out), ws, st,
+                           stage, zext);
 }
 
 template <int K>
 int bwd_k(const wtc_desc* d, const UnfusedPlan& p, const void* x, const void* g, const float* w0,
           const float* s0, const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0,
-          float* dwl, float* dsl, char* ws, hipStream_t st) {
+          float* dwl, float* dsl, char* ws, hipStream_t st, int stage, const float* zext) {
     if (d->dtype == WTC_BF16)
         return bwd_t<K, uint16_t>(d, p, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(g), w0, s0, wl,
-                                  sl, static_cast<uint16_t*>(dx), dw0, ds0, db0, dwl, dsl, ws, st);
+                                  sl, static_cast<uint16_t*>(dx), dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
     return bwd_t<K, float>(d, p, static_cast<const float*>(x), static_cast<const float*>(g), w0, s0, wl, sl,
-                           static_cast<float*>(dx), dw0, ds0, db0, dwl, dsl, ws, st);
+                           static_cast<float*>(dx), dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
+}
+
+__global__ void __launch_bounds__(256) k_fill_zero(float* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.f;
 }
 
 }  // namespace
 
 int unfused_forward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const float* w0, const float* s0,
-                    const float* b0, const float* wl, const float* sl, void* out, char* ws, void* stream) {
+                    const float* b0, const float* wl, const float* sl, void* out, char* ws, void* stream,
+                    int stage, const float* zext) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     switch (d->k) {
-        case 1: return fwd_k<1>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
-        case 3: return fwd_k<3>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
-        case 5: return fwd_k<5>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
-        case 7: return fwd_k<7>(d, p, x, w0, s0, b0, wl, sl, out, ws, st);
+        case 1: return fwd_k<1>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
+        case 3: return fwd_k<3>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
+        case 5: return fwd_k<5>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
+        case 7: return fwd_k<7>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
         default: return WTC_ESHAPE;
     }
 }
 
 int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, const void* g, const float* w0,
                      const float* s0, const float* wl, const float* sl, void* dx, float* dw0, float* ds0,
-                     float* db0, float* dwl, float* dsl, char* ws, void* stream) {
+                     float* db0, float* dwl, float* dsl, char* ws, void* stream, int stage, const float* zext) {
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     switch (d->k) {
-        case 1: return bwd_k<1>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
-        case 3: return bwd_k<3>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
-        case 5: return bwd_k<5>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
-        case 7: return bwd_k<7>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st);
+        case 1: return bwd_k<1>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
+        case 3: return bwd_k<3>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
+        case 5: return bwd_k<5>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
+        case 7: return bwd_k<7>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
         default: return WTC_ESHAPE;
     }
+}
+
+int launch_fill_zero(float* p, int n, void* stream) {
+    if (n <= 0) return 0;
+    hipLaunchKernelGGL(k_fill_zero, dim3((n + 255) / 256), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), p, n);
+    return (int)hipGetLastError();
 }
 
 }  // namespace wtc

@@ -60,6 +60,9 @@ WORKLOADS = {
     # odd / small spatial shapes
     "odd_b128c384_14x14_L2": Workload("odd_b128c384_14x14_L2", 128, 384, 14, 14, 2, 5, "fp32", 40),
     "odd_b128c768_7x7_L1": Workload("odd_b128c768_7x7_L1", 128, 768, 7, 7, 1, 5, "fp32", 41),
+    # planes beyond the on-chip pipeline (a high-resolution first stage): level 1
+    # level by level, the LL band (112 x 112) fused
+    "large_b8c64_224x224_L3": Workload("large_b8c64_224x224_L3", 8, 64, 224, 224, 3, 5, "fp32", 50),
 }
 
 

@@ -39,7 +39,8 @@ FAKE = ctypes.c_void_p(16)   # never dereferenced: every case below fails valida
 @pytest.mark.parametrize("kw,status", [
     (dict(k=4), binding.WTC_EINVAL), (dict(k=0), binding.WTC_EINVAL), (dict(L=-1), binding.WTC_EINVAL),
     (dict(B=0), binding.WTC_EINVAL), (dict(H=0), binding.WTC_EINVAL), (dict(dtype=7), binding.WTC_EDTYPE),
-    (dict(layout=1), binding.WTC_EDTYPE), (dict(H=512, W=512), binding.WTC_ESHAPE), (dict(k=9), binding.WTC_ESHAPE),
+    (dict(layout=1), binding.WTC_EDTYPE), (dict(H=512, W=512), binding.WTC_EWORKSPACE),
+    (dict(k=9), binding.WTC_ESHAPE),
 ])
 def test_forward_rejects(kw, status):
     lib = binding.load_library()
@@ -152,3 +153,28 @@ def test_io_model_unfused_counts_intermediates():
             fu = binding.wtconv_io_model_bytes(32, 96, 64, 64, L, k, "fp32", 1, dr)
             fz = binding.wtconv_io_model_bytes(32, 96, 64, 64, L, k, "fp32", 0, dr)
             assert fu >= fz * (0.99 if L == 0 else 1.5), (L, dr)
+
+
+def test_large_planes_take_the_peeled_path():
+    """Planes beyond the on-chip pipeline run level 1 level by level and their
+    LL band recursively: both directions need a workspace there, none (forward)
+    or only the partial records (backward) where the fused kernels fit."""
+    assert binding.wtconv_forward_workspace(32, 96, 64, 64, 3, 5) == 0
+    small_b = binding.wtconv_backward_workspace(32, 96, 64, 64, 3, 5)
+    assert 0 < small_b < 4 * 32 * 96 * 64 * 64
+    for H, W, L in [(200, 150, 3), (300, 260, 4), (512, 512, 5), (260, 130, 0), (140, 140, 1)]:
+        f = binding.wtconv_forward_workspace(2, 3, H, W, L, 5)
+        b = binding.wtconv_backward_workspace(2, 3, H, W, L, 5)
+        if L == 0:
+            assert f == 0 and b > 0
+        else:
+            # at least the level-1 bands and their conv outputs
+            h1, w1 = (H + 1) // 2, (W + 1) // 2
+            assert f >= 2 * 4 * 2 * 3 * h1 * w1 * 4 and b > f, (H, W, L, f, b)
+    # the analytic traffic of the peeled forward exceeds the fused one's 2 N e
+    n = 2 * 3 * 200 * 150 * 4
+    assert binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=0, direction=0) > 2 * n
+    assert binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=0, direction=0) < \
+        binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=1, direction=0)
+    # limits that no path lifts
+    assert binding.wtconv_forward_workspace(2, 3, 64, 64, 2, 9) == 0

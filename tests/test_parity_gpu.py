@@ -163,7 +163,8 @@ def test_finite_differences_tiny():
         assert abs((lp - lm) / 2.0 - gdx[i]) <= 1e-3 * rms, i
 
 
-FULL = ["stage1_b32c96_64x64_L3", "bf16_b64c192_32x32_L3", "odd_b128c384_14x14_L2", "odd_b128c768_7x7_L1"]
+FULL = ["stage1_b32c96_64x64_L3", "bf16_b64c192_32x32_L3", "odd_b128c384_14x14_L2", "odd_b128c768_7x7_L1",
+        "large_b8c64_224x224_L3"]
 
 
 def _full_sampled(wl_, L):
@@ -215,3 +216,20 @@ def test_full_size_dwconv_sampled(k):
     wl_ = dataclasses.replace(WORKLOADS["stage1_b32c96_64x64_L3"], name=f"stage1_L0_k{k}", L=0, k=k, L_max=0,
                               sweep=())
     _full_sampled(wl_, 0)
+
+
+# Planes beyond the on-chip pipeline: level 1 and the base conv level by level,
+# the LL band recursively (fused once it fits).
+LARGE = [
+    (2, 3, 200, 150, 3, 5, 80, "fp32"),    # one peel, LL 100x75 fused with 2 levels
+    (1, 2, 300, 260, 4, 3, 81, "fp32"),    # two peels (150x130 is still too large), k = 3
+    (2, 2, 160, 144, 2, 5, 82, "bf16"),    # bf16 storage at the top, fp32 LL below
+    (1, 2, 260, 130, 0, 7, 83, "fp32"),    # L = 0: the plain depthwise conv
+    (2, 2, 140, 141, 1, 5, 84, "fp32"),    # L = 1: nothing below the peeled level, ragged side
+    (1, 2, 257, 129, 9, 5, 85, "fp32"),    # levels deeper than the plane (tail), odd sides
+]
+
+
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", LARGE)
+def test_large_planes(B, C, H, W, L, k, seed, dtype):
+    _case(B, C, H, W, L, k, seed, dtype)
