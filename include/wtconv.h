@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
     WTC_OK = 0,
     WTC_EINVAL = -1,     /* null pointer, k even or < 1, L < 0, B/C/H/W < 1, bad impl/dir */
-    WTC_ESHAPE = -2,     /* plane too large for the on-chip (LDS) plane pipeline */
+    WTC_ESHAPE = -2,     /* k > 7, or a tensor of 2^31 elements or more */
     WTC_EDTYPE = -3,     /* dtype or layout not supported */
     WTC_EWORKSPACE = -4, /* workspace NULL or smaller than the queried size */
     WTC_EHIP = -5        /* a HIP launch or runtime call failed */
@@ -69,18 +69,28 @@ typedef struct {
     int layout;     /* 0 = NCHW (the only layout)                             */
 } wtc_desc;
 
-/* Bytes of device workspace wtconv_forward needs (0: none). */
+/* Bytes of device workspace wtconv_forward needs (0: none).  It is 0 for every
+ * plane the on-chip pipeline holds (up to about 128 x 128 with k = 5); larger
+ * planes peel one wavelet level (below) and need float32 tensors of their
+ * level-1 bands, LL band and deeper result.  0 is also returned for a
+ * descriptor that the forward pass rejects. */
 size_t wtconv_forward_workspace(const wtc_desc* d);
 
 /* Forward pass: out = WTConv(x).  `workspace` may be NULL when the queried
- * size is 0. */
+ * size is 0.
+ * Planes beyond the on-chip pipeline: the levels >= 2 of the operator are the
+ * operator itself (one level fewer, no base conv) applied to the level-1 LL
+ * band, so level 1 and the base conv run level by level (the "_unfused"
+ * kernels) and the LL band (half the size per side) recursively through this
+ * path -- on chip as soon as it fits.  Same results, same contract. */
 int wtconv_forward(const wtc_desc* d, const void* x,
                    const float* w0, const float* s0, const float* b0,
                    const float* wl, const float* sl,
                    void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace wtconv_backward needs (per-workgroup partial
- * sums of the weight-gradient correlations). */
+ * sums of the weight-gradient correlations; for planes beyond the on-chip
+ * pipeline also the tensors of the peeled level and of the LL problem). */
 size_t wtconv_backward_workspace(const wtc_desc* d);
 
 /* Backward pass: given g = d loss / d out, writes
