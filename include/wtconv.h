@@ -27,9 +27,13 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library never allocates, frees or synchronises on these paths; calls
  *     are asynchronous on `stream` (a hipStream_t; NULL = default stream).
- *   - x, out, g (= d loss / d out) and dx are [B, C, H, W], NCHW contiguous,
- *     stored as float32 (dtype WTC_FP32) or bfloat16 bits (WTC_BF16; out and
- *     dx are rounded to nearest even).  All arithmetic is float32.
+ *   - x, out, g (= d loss / d out) and dx are [B, C, H, W], NCHW contiguous
+ *     (layout 0) or channels-last [B, H, W, C] contiguous (layout 1), stored as
+ *     float32 (dtype WTC_FP32) or bfloat16 bits (WTC_BF16; out and dx are
+ *     rounded to nearest even).  All arithmetic is float32.  Channels-last
+ *     tensors are transposed into NCHW copies at the front of the workspace,
+ *     computed there and transposed back (two extra tensors of workspace
+ *     forward, three backward; four and six extra tensor passes of traffic).
  *   - Parameters and their gradients are float32:
  *       w0 [C, k, k] (PyTorch depthwise [C,1,k,k] order), s0 [C], b0 [C],
  *       wl [L, 4C, k, k] with flat index ((l*C + c)*4 + u)*k*k + ky*k + kx,
@@ -54,7 +58,7 @@ typedef enum {
     WTC_OK = 0,
     WTC_EINVAL = -1,     /* null pointer, k even or < 1, L < 0, B/C/H/W < 1, bad impl/dir */
     WTC_ESHAPE = -2,     /* k > 7, or a tensor of 2^31 elements or more */
-    WTC_EDTYPE = -3,     /* dtype or layout not supported */
+    WTC_EDTYPE = -3,     /* dtype or layout not supported (layout > 1) */
     WTC_EWORKSPACE = -4, /* workspace NULL or smaller than the queried size */
     WTC_EHIP = -5        /* a HIP launch or runtime call failed */
 } wtc_status;
@@ -66,7 +70,7 @@ typedef struct {
     int L;          /* wavelet levels (>= 0)                                  */
     int k;          /* kernel size (odd, 1..7 on the fused path)              */
     int dtype;      /* wtc_dtype: storage type of x / out / g / dx           */
-    int layout;     /* 0 = NCHW (the only layout)                             */
+    int layout;     /* 0 = NCHW, 1 = channels-last (NHWC)                     */
 } wtc_desc;
 
 /* Bytes of device workspace wtconv_forward needs (0: none).  It is 0 for every

@@ -80,9 +80,10 @@ def wtconv_status_string(status):
     return load_library().wtconv_status_string(int(status)).decode()
 
 
-def make_desc(B, C, H, W, L, k, dtype="fp32"):
+def make_desc(B, C, H, W, L, k, dtype="fp32", layout=0):
+    """layout 0: NCHW; 1: channels-last (NHWC), adapted by transposes in the library."""
     dt = {"fp32": WTC_FP32, "bf16": WTC_BF16, torch.float32: WTC_FP32, torch.bfloat16: WTC_BF16}[dtype]
-    return wtc_desc(int(B), int(C), int(H), int(W), int(L), int(k), dt, 0)
+    return wtc_desc(int(B), int(C), int(H), int(W), int(L), int(k), dt, int(layout))
 
 
 def _ptr(t):
@@ -93,22 +94,35 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_tensor(t, name, dtypes, device, shape=None):
+def _layout_of(t):
+    """0 for an NCHW-contiguous activation tensor, 1 for a channels-last one."""
+    if t.is_contiguous():
+        return 0
+    if t.dim() == 4 and t.is_contiguous(memory_format=torch.channels_last):
+        return 1
+    raise ValueError("activation tensors must be contiguous in NCHW or in channels-last order")
+
+
+def _check_tensor(t, name, dtypes, device, shape=None, layout=None):
+    """layout None: a parameter (plain contiguous); else the activation layout
+    every tensor of the call must share."""
     if t is None:
         return
     if not t.is_cuda or t.device != device:
         raise ValueError(f"{name} must be a CUDA tensor on {device}")
     if t.dtype not in dtypes:
         raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
-    if not t.is_contiguous():
+    if layout is None and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if layout is not None and _layout_of(t) != layout:
+        raise ValueError(f"{name} must have the memory layout of x")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _desc_of(x, L, k):
     B, C, H, W = x.shape
-    return make_desc(B, C, H, W, L, k, x.dtype)
+    return make_desc(B, C, H, W, L, k, x.dtype, _layout_of(x))
 
 
 def _check_params(x, w0, s0, b0, wl, sl, L):
@@ -116,7 +130,7 @@ def _check_params(x, w0, s0, b0, wl, sl, L):
     k = w0.shape[-1]
     dev = x.device
     f32 = (torch.float32,)
-    _check_tensor(x, "x", (torch.float32, torch.bfloat16), dev)
+    _check_tensor(x, "x", (torch.float32, torch.bfloat16), dev, layout=_layout_of(x))
     _check_tensor(w0, "w0", f32, dev, (C, k, k))
     _check_tensor(s0, "s0", f32, dev, (C,))
     _check_tensor(b0, "b0", f32, dev, (C,))
@@ -145,7 +159,7 @@ def _fwd_common(fn_name, ws_name, x, w0, s0, b0, wl, sl, L, out, workspace):
     d = _desc_of(x, L, k)
     if out is None:
         out = torch.empty_like(x)
-    _check_tensor(out, "out", (x.dtype,), x.device, x.shape)
+    _check_tensor(out, "out", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
     ws, wsb = _workspace(getattr(lib, ws_name)(ctypes.byref(d)), x.device, workspace)
     st = getattr(lib, fn_name)(ctypes.byref(d), _ptr(x), _ptr(w0), _ptr(s0), _ptr(b0),
                                _ptr(wl if L > 0 else None), _ptr(sl if L > 0 else None),
@@ -158,11 +172,12 @@ def _fwd_common(fn_name, ws_name, x, w0, s0, b0, wl, sl, L, out, workspace):
 def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace):
     C = x.shape[1]
     k = _check_params(x, w0, s0, None, wl, sl, L)
-    _check_tensor(g, "g", (x.dtype,), x.device, x.shape)
+    _check_tensor(g, "g", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
     lib = load_library()
     d = _desc_of(x, L, k)
     if dx is None:
         dx = torch.empty_like(x)
+    _check_tensor(dx, "dx", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
     if grads is None:
         f32 = dict(dtype=torch.float32, device=x.device)
         grads = dict(dw0=torch.empty(C, k, k, **f32), ds0=torch.empty(C, **f32), db0=torch.empty(C, **f32),
@@ -203,29 +218,29 @@ def wtconv_backward_unfused(x, g, w0, s0, wl, sl, L, dx=None, grads=None, worksp
                        dx, grads, workspace)
 
 
-def _ws_query(name, B, C, H, W, L, k, dtype):
-    d = make_desc(B, C, H, W, L, k, dtype)
+def _ws_query(name, B, C, H, W, L, k, dtype, layout=0):
+    d = make_desc(B, C, H, W, L, k, dtype, layout)
     return int(getattr(load_library(), name)(ctypes.byref(d)))
 
 
-def wtconv_forward_workspace(B, C, H, W, L, k, dtype="fp32"):
-    return _ws_query("wtconv_forward_workspace", B, C, H, W, L, k, dtype)
+def wtconv_forward_workspace(B, C, H, W, L, k, dtype="fp32", layout=0):
+    return _ws_query("wtconv_forward_workspace", B, C, H, W, L, k, dtype, layout)
 
 
-def wtconv_backward_workspace(B, C, H, W, L, k, dtype="fp32"):
-    return _ws_query("wtconv_backward_workspace", B, C, H, W, L, k, dtype)
+def wtconv_backward_workspace(B, C, H, W, L, k, dtype="fp32", layout=0):
+    return _ws_query("wtconv_backward_workspace", B, C, H, W, L, k, dtype, layout)
 
 
-def wtconv_forward_unfused_workspace(B, C, H, W, L, k, dtype="fp32"):
-    return _ws_query("wtconv_forward_unfused_workspace", B, C, H, W, L, k, dtype)
+def wtconv_forward_unfused_workspace(B, C, H, W, L, k, dtype="fp32", layout=0):
+    return _ws_query("wtconv_forward_unfused_workspace", B, C, H, W, L, k, dtype, layout)
 
 
-def wtconv_backward_unfused_workspace(B, C, H, W, L, k, dtype="fp32"):
-    return _ws_query("wtconv_backward_unfused_workspace", B, C, H, W, L, k, dtype)
+def wtconv_backward_unfused_workspace(B, C, H, W, L, k, dtype="fp32", layout=0):
+    return _ws_query("wtconv_backward_unfused_workspace", B, C, H, W, L, k, dtype, layout)
 
 
-def wtconv_io_model_bytes(B, C, H, W, L, k, dtype="fp32", impl=0, direction=0):
-    d = make_desc(B, C, H, W, L, k, dtype)
+def wtconv_io_model_bytes(B, C, H, W, L, k, dtype="fp32", impl=0, direction=0, layout=0):
+    d = make_desc(B, C, H, W, L, k, dtype, layout)
     return float(load_library().wtconv_io_model_bytes(ctypes.byref(d), int(impl), int(direction)))
 
 

@@ -252,5 +252,7 @@ int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, con
                      float* dw0, float* ds0, float* db0, float* dwl, float* dsl, char* ws,
                      void* stream, int stage = 0, const float* zext = nullptr);
 int launch_fill_zero(float* p, int n, void* stream);
+// [batch][rows][cols] -> [batch][cols][rows], elements of esize (4 or 2) bytes
+int launch_transpose(const void* src, void* dst, int batch, int rows, int cols, int esize, void* stream);
 
 }  // namespace wtc

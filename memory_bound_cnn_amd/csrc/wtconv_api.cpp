@@ -26,8 +26,16 @@ int check_desc(const wtc_desc* d) {
     if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->L < 0) return WTC_EINVAL;
     if (d->k < 1 || d->k % 2 == 0) return WTC_EINVAL;
     if (d->dtype != WTC_FP32 && d->dtype != WTC_BF16) return WTC_EDTYPE;
-    if (d->layout != 0) return WTC_EDTYPE;
+    if (d->layout != 0 && d->layout != 1) return WTC_EDTYPE;
+    if (d->layout == 1 && d->B > 65535) return WTC_ESHAPE;   // transpose grid
     return WTC_OK;
+}
+
+// NCHW twin of a descriptor (the compute paths are NCHW; layout 1 is adapted)
+wtc_desc nchw_of(const wtc_desc* d) {
+    wtc_desc n = *d;
+    n.layout = 0;
+    return n;
 }
 
 struct FusedPlan {
@@ -359,6 +367,90 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
     return unfused_backward(&pp.d1, pp.u, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream, 2, zext);
 }
 
+int unf_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
+                const float* wl, const float* sl, void* out, char* ws, size_t wsb, void* stream) {
+    UnfusedPlan p;
+    const int st = unfused_plan(d, 0, &p);
+    if (st != WTC_OK) return st;
+    if (p.total > 0 && (!ws || wsb < p.total)) return WTC_EWORKSPACE;
+    return unfused_forward(d, p, x, w0, s0, b0, wl, sl, out, ws, stream);
+}
+
+int unf_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
+                const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0, float* dwl,
+                float* dsl, char* ws, size_t wsb, void* stream) {
+    UnfusedPlan p;
+    const int st = unfused_plan(d, 1, &p);
+    if (st != WTC_OK) return st;
+    if (!ws || wsb < p.total) return WTC_EWORKSPACE;
+    return unfused_backward(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Channels-last (NHWC) tensors: transposed into NCHW copies at the front of
+// the workspace, computed there, the result transposed back.
+// ---------------------------------------------------------------------------
+size_t nhwc_tensor_bytes(const wtc_desc* d) {
+    return al256((size_t)d->B * d->C * d->H * d->W * (d->dtype == WTC_BF16 ? 2 : 4));
+}
+
+int nhwc_forward(const wtc_desc* d, bool unf, const void* x, const float* w0, const float* s0, const float* b0,
+                 const float* wl, const float* sl, void* out, char* ws, size_t wsb, void* stream) {
+    const wtc_desc n = nchw_of(d);
+    const size_t T = nhwc_tensor_bytes(d);
+    size_t inner = 0;
+    if (unf) {
+        UnfusedPlan p;
+        const int st = unfused_plan(&n, 0, &p);
+        if (st != WTC_OK) return st;
+        inner = p.total;
+    } else {
+        int st = WTC_OK;
+        inner = fused_fwd_ws(&n, 0, &st);
+        if (st != WTC_OK) return st;
+    }
+    if (!ws || wsb < 2 * T + inner) return WTC_EWORKSPACE;
+    const int HW = d->H * d->W, e = d->dtype == WTC_BF16 ? 2 : 4;
+    char* xt = ws;
+    char* ot = ws + T;
+    if (launch_transpose(x, xt, d->B, HW, d->C, e, stream) != 0) return WTC_EHIP;
+    const int st = unf ? unf_fwd_run(&n, xt, w0, s0, b0, wl, sl, ot, ws + 2 * T, wsb - 2 * T, stream)
+                       : fused_fwd_run(&n, xt, w0, s0, b0, wl, sl, ot, ws + 2 * T, wsb - 2 * T, stream, 0);
+    if (st != WTC_OK) return st;
+    return launch_transpose(ot, out, d->B, d->C, HW, e, stream) == 0 ? WTC_OK : WTC_EHIP;
+}
+
+int nhwc_backward(const wtc_desc* d, bool unf, const void* x, const void* g, const float* w0, const float* s0,
+                  const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0, float* dwl,
+                  float* dsl, char* ws, size_t wsb, void* stream) {
+    const wtc_desc n = nchw_of(d);
+    const size_t T = nhwc_tensor_bytes(d);
+    size_t inner = 0;
+    if (unf) {
+        UnfusedPlan p;
+        const int st = unfused_plan(&n, 1, &p);
+        if (st != WTC_OK) return st;
+        inner = p.total;
+    } else {
+        int st = WTC_OK;
+        inner = fused_bwd_ws(&n, 0, &st);
+        if (st != WTC_OK) return st;
+    }
+    if (!ws || wsb < 3 * T + inner) return WTC_EWORKSPACE;
+    const int HW = d->H * d->W, e = d->dtype == WTC_BF16 ? 2 : 4;
+    char* xt = ws;
+    char* gt = ws + T;
+    char* dxt = ws + 2 * T;
+    if (launch_transpose(x, xt, d->B, HW, d->C, e, stream) != 0) return WTC_EHIP;
+    if (launch_transpose(g, gt, d->B, HW, d->C, e, stream) != 0) return WTC_EHIP;
+    const int st = unf ? unf_bwd_run(&n, xt, gt, w0, s0, wl, sl, dxt, dw0, ds0, db0, dwl, dsl, ws + 3 * T,
+                                     wsb - 3 * T, stream)
+                       : fused_bwd_run(&n, xt, gt, w0, s0, wl, sl, dxt, dw0, ds0, db0, dwl, dsl, ws + 3 * T,
+                                       wsb - 3 * T, stream, 0);
+    if (st != WTC_OK) return st;
+    return launch_transpose(dxt, dx, d->B, d->C, HW, e, stream) == 0 ? WTC_OK : WTC_EHIP;
+}
+
 double spec_level_area(const wtc_desc* d, int i) {
     int h = d->H, w = d->W;
     for (int l = 0; l < i; ++l) {
@@ -451,9 +543,11 @@ const char* wtconv_status_string(int s) {
 
 size_t wtconv_forward_workspace(const wtc_desc* d) {
     if (check_desc(d) != WTC_OK) return 0;
+    const wtc_desc n = nchw_of(d);
     int st = WTC_OK;
-    const size_t n = fused_fwd_ws(d, 0, &st);
-    return st == WTC_OK ? n : 0;
+    const size_t inner = fused_fwd_ws(&n, 0, &st);
+    if (st != WTC_OK) return 0;
+    return d->layout == 1 ? 2 * nhwc_tensor_bytes(d) + inner : inner;
 }
 
 int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0,
@@ -463,14 +557,19 @@ int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const floa
     if (st != WTC_OK) return st;
     if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
+    if (d->layout == 1)
+        return nhwc_forward(d, false, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes,
+                            stream);
     return fused_fwd_run(d, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes, stream, 0);
 }
 
 size_t wtconv_backward_workspace(const wtc_desc* d) {
     if (check_desc(d) != WTC_OK) return 0;
+    const wtc_desc n = nchw_of(d);
     int st = WTC_OK;
-    const size_t n = fused_bwd_ws(d, 0, &st);
-    return st == WTC_OK ? n : 0;
+    const size_t inner = fused_bwd_ws(&n, 0, &st);
+    if (st != WTC_OK) return 0;
+    return d->layout == 1 ? 3 * nhwc_tensor_bytes(d) + inner : inner;
 }
 
 int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -481,6 +580,9 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
     if (st != WTC_OK) return st;
     if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
+    if (d->layout == 1)
+        return nhwc_backward(d, false, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
+                             static_cast<char*>(workspace), workspace_bytes, stream);
     return fused_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, static_cast<char*>(workspace),
                          workspace_bytes, stream, 0);
 }
@@ -489,9 +591,11 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
 // Unfused baseline
 // ---------------------------------------------------------------------------
 size_t wtconv_forward_unfused_workspace(const wtc_desc* d) {
+    if (check_desc(d) != WTC_OK) return 0;
+    const wtc_desc n = nchw_of(d);
     UnfusedPlan p;
-    if (unfused_plan(d, 0, &p) != WTC_OK) return 0;
-    return p.total;
+    if (unfused_plan(&n, 0, &p) != WTC_OK) return 0;
+    return d->layout == 1 ? 2 * nhwc_tensor_bytes(d) + p.total : p.total;
 }
 
 int wtconv_forward_unfused(const wtc_desc* d, const void* x, const float* w0, const float* s0,
@@ -501,17 +605,18 @@ int wtconv_forward_unfused(const wtc_desc* d, const void* x, const float* w0, co
     if (st != WTC_OK) return st;
     if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
-    UnfusedPlan p;
-    st = unfused_plan(d, 0, &p);
-    if (st != WTC_OK) return st;
-    if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return WTC_EWORKSPACE;
-    return unfused_forward(d, p, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), stream);
+    if (d->layout == 1)
+        return nhwc_forward(d, true, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes,
+                            stream);
+    return unf_fwd_run(d, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes, stream);
 }
 
 size_t wtconv_backward_unfused_workspace(const wtc_desc* d) {
+    if (check_desc(d) != WTC_OK) return 0;
+    const wtc_desc n = nchw_of(d);
     UnfusedPlan p;
-    if (unfused_plan(d, 1, &p) != WTC_OK) return 0;
-    return p.total;
+    if (unfused_plan(&n, 1, &p) != WTC_OK) return 0;
+    return d->layout == 1 ? 3 * nhwc_tensor_bytes(d) + p.total : p.total;
 }
 
 int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -522,12 +627,11 @@ int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g, con
     if (st != WTC_OK) return st;
     if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
-    UnfusedPlan p;
-    st = unfused_plan(d, 1, &p);
-    if (st != WTC_OK) return st;
-    if (!workspace || workspace_bytes < p.total) return WTC_EWORKSPACE;
-    return unfused_backward(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
-                            static_cast<char*>(workspace), stream);
+    if (d->layout == 1)
+        return nhwc_backward(d, true, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
+                             static_cast<char*>(workspace), workspace_bytes, stream);
+    return unf_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, static_cast<char*>(workspace),
+                       workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -553,7 +657,12 @@ double wtconv_flops(const wtc_desc* d, int dir) {
 
 double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
     if (check_desc(d) != WTC_OK || (dir != 0 && dir != 1) || (impl != 0 && impl != 1)) return -1.0;
-    return impl == 0 ? io_fused(d, dir, 0) : io_unfused(d, dir);
+    const wtc_desc n = nchw_of(d);
+    const double t = impl == 0 ? io_fused(&n, dir, 0) : io_unfused(&n, dir);
+    if (t < 0 || d->layout == 0) return t;
+    // channels-last: x (and g) transposed in, out (dx) transposed back, each read and written
+    const double N = (double)d->B * d->C * d->H * d->W * (d->dtype == WTC_BF16 ? 2.0 : 4.0);
+    return t + (dir == 0 ? 4.0 : 6.0) * N;
 }
 
 }  // extern "C"

@@ -1,0 +1,50 @@
+// Layout adapter for channels-last (NHWC) tensors: a batched transpose through
+// LDS, [batch][rows][cols] -> [batch][cols][rows].  NHWC -> NCHW is rows = H*W,
+// cols = C; NCHW -> NHWC is rows = C, cols = H*W.  Both sides are read and
+// written in whole 64-element row segments (coalesced); the LDS tile is padded
+// by one element per row so the transposed reads hit distinct banks.
+#include <hip/hip_runtime.h>
+
+#include "wtc_internal.h"
+
+namespace wtc {
+namespace {
+
+constexpr int kTile = 64;
+
+template <typename T>
+__global__ void __launch_bounds__(256) k_transpose(const T* __restrict__ src, T* __restrict__ dst, int rows,
+                                                   int cols) {
+    __shared__ T tile[kTile][kTile + 1];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int r0 = blockIdx.y * kTile, c0 = blockIdx.x * kTile;
+    const size_t base = (size_t)blockIdx.z * rows * cols;
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i) {
+        const int r = r0 + ty + 4 * i, c = c0 + tx;
+        if (r < rows && c < cols) tile[ty + 4 * i][tx] = src[base + (size_t)r * cols + c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTile / 4; ++i) {
+        const int c = c0 + ty + 4 * i, r = r0 + tx;
+        if (c < cols && r < rows) dst[base + (size_t)c * rows + r] = tile[tx][ty + 4 * i];
+    }
+}
+
+}  // namespace
+
+int launch_transpose(const void* src, void* dst, int batch, int rows, int cols, int esize, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const dim3 grid((cols + kTile - 1) / kTile, (rows + kTile - 1) / kTile, batch);
+    if (grid.y > 65535 || grid.z > 65535) return (int)hipErrorInvalidValue;
+    if (esize == 4)
+        hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(256), 0, st, static_cast<const uint32_t*>(src),
+                           static_cast<uint32_t*>(dst), rows, cols);
+    else
+        hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                           static_cast<uint16_t*>(dst), rows, cols);
+    return (int)hipGetLastError();
+}
+
+}  // namespace wtc

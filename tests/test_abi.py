@@ -39,7 +39,8 @@ FAKE = ctypes.c_void_p(16)   # never dereferenced: every case below fails valida
 @pytest.mark.parametrize("kw,status", [
     (dict(k=4), binding.WTC_EINVAL), (dict(k=0), binding.WTC_EINVAL), (dict(L=-1), binding.WTC_EINVAL),
     (dict(B=0), binding.WTC_EINVAL), (dict(H=0), binding.WTC_EINVAL), (dict(dtype=7), binding.WTC_EDTYPE),
-    (dict(layout=1), binding.WTC_EDTYPE), (dict(H=512, W=512), binding.WTC_EWORKSPACE),
+    (dict(layout=2), binding.WTC_EDTYPE), (dict(layout=1), binding.WTC_EWORKSPACE),
+    (dict(H=512, W=512), binding.WTC_EWORKSPACE),
     (dict(k=9), binding.WTC_ESHAPE),
 ])
 def test_forward_rejects(kw, status):
@@ -178,3 +179,20 @@ def test_large_planes_take_the_peeled_path():
         binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=1, direction=0)
     # limits that no path lifts
     assert binding.wtconv_forward_workspace(2, 3, 64, 64, 2, 9) == 0
+
+
+def test_channels_last_workspace_and_model():
+    """Channels-last tensors are transposed into NCHW copies at the front of
+    the workspace: forward two tensors, backward three, on top of the NCHW needs."""
+    B, C, H, W, L, k = 4, 6, 64, 64, 3, 5
+    t = B * C * H * W * 4
+    assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=1) == \
+        2 * t + binding.wtconv_forward_workspace(B, C, H, W, L, k)
+    assert binding.wtconv_backward_workspace(B, C, H, W, L, k, layout=1) == \
+        3 * t + binding.wtconv_backward_workspace(B, C, H, W, L, k)
+    assert binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16", layout=1) == \
+        3 * (t // 2) + binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16")
+    for direction, extra in ((0, 4), (1, 6)):
+        assert binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction, layout=1) == \
+            binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction) + extra * t
+    assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=2) == 0

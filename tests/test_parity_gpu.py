@@ -233,3 +233,36 @@ LARGE = [
 @pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", LARGE)
 def test_large_planes(B, C, H, W, L, k, seed, dtype):
     _case(B, C, H, W, L, k, seed, dtype)
+
+
+# Channels-last (NHWC) tensors: transposed into NCHW copies in the workspace by
+# the library, results transposed back; values identical to the NCHW call.
+CHANNELS_LAST = [
+    (2, 6, 64, 64, 3, 5, 90, "fp32"),
+    (2, 5, 32, 32, 3, 5, 91, "bf16"),
+    (3, 7, 14, 14, 2, 5, 92, "fp32"),
+    (5, 20, 7, 7, 1, 5, 93, "fp32"),       # register-resident small-plane kernel
+    (1, 3, 200, 150, 2, 5, 94, "fp32"),    # peeled plane
+]
+
+
+@pytest.mark.parametrize("impl", ["fused", "unfused"])
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", CHANNELS_LAST)
+def test_channels_last(impl, B, C, H, W, L, k, seed, dtype):
+    d = inputs(B, C, H, W, L, k, seed, dtype)
+    t = to_dev(d, dtype, L)
+    for key in ("x", "g"):
+        t[key] = t[key].contiguous(memory_format=torch.channels_last)
+    out, gr = run_fused(t, L, impl)
+    if C > 1 and H * W > 1:
+        assert not out.is_contiguous() and out.is_contiguous(memory_format=torch.channels_last)
+    ref_out, ref_gr = oracle_ref(d, L)
+    check_all(out, gr, ref_out, ref_gr, dtype, f"channels-last {impl} B{B} C{C} {H}x{W} L{L} {dtype}")
+
+
+def test_mixed_layouts_rejected():
+    d = inputs(1, 3, 16, 16, 1, 5, 95)
+    t = to_dev(d, "fp32", 1)
+    g_cl = t["g"].contiguous(memory_format=torch.channels_last)
+    with pytest.raises(ValueError):
+        binding.wtconv_backward(t["x"], g_cl, t["w0"], t["s0"], t["wl"], t["sl"], 1)
