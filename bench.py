@@ -246,7 +246,9 @@ def _oracle_task(args):
 
 def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
     """Time the float64 oracle (forward + backward) on a bounded sample of the
-    workload: whole batch entries, one per task, in a pool of host processes."""
+    workload: whole batch entries, one per task, in a pool of host processes,
+    about `budget_s` seconds of CPU work in total (the batch is cycled through
+    when one pass over it is shorter than that)."""
     from memory_bound_cnn_amd.inputs import workload_inputs
     try:
         ncpu = len(os.sched_getaffinity(0))
@@ -258,18 +260,19 @@ def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
     sl_ = d["sl"][:L] if L > 0 else None
     task = lambda b: (d["x"][b:b + 1], d["g"][b:b + 1], d["w0"], d["s0"], d["b0"], wl_, sl_, L)
     t1 = _oracle_task(task(0))                      # one entry, one core: sizes the sample
-    n_entries = int(min(wl.B, max(cores, budget_s * cores / max(t1, 1e-3))))
+    n_entries = int(max(cores, math.ceil(budget_s / max(t1, 1e-3))))
     ctx = mp.get_context("spawn")
     with ctx.Pool(cores) as pool:
         pool.map(_oracle_task, [task(0)] * cores)   # warm the workers (imports)
         t0 = time.perf_counter()
-        pool.map(_oracle_task, [task(b) for b in range(n_entries)], chunksize=1)
+        pool.map(_oracle_task, [task(b % wl.B) for b in range(n_entries)], chunksize=1)
         wall = time.perf_counter() - t0
     value = n_entries * bytes_per_batch_entry / wall / 1e9
     return dict(value=value, unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{n_entries} of {wl.B} batch entries of {wl.name} (L={L}): float64 NumPy oracle, "
-                       f"forward + backward, one batch entry per task on a pool of {cores} processes "
-                       f"(1 thread each); wall {wall:.2f} s; one entry on one core {t1:.3f} s",
+                sample=f"{n_entries} batch entries (the {wl.B} of {wl.name}, L={L}, cycled; about {budget_s:.0f} s "
+                       f"of CPU work): float64 NumPy oracle, forward + backward, one batch entry per task on a "
+                       f"pool of {cores} processes (1 thread each); wall {wall:.2f} s; one entry on one core "
+                       f"{t1:.3f} s",
                 wall_s=round(wall, 3), entries=n_entries)
 
 
