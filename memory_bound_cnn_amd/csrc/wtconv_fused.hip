@@ -28,10 +28,11 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
     const int c = blockIdx.x, tid = threadIdx.x, nthr = blockDim.x;
     const int KK = f.k * f.k;
     // records of channel c: workgroups whose plane range meets [c*B, (c+1)*B);
-    // segment 0 if the range starts in channel c, else segment 1.  Summed in a
-    // fixed order (deterministic).
+    // segment 0 if the range starts in channel c (w*ppw >= c*B), else segment 1.
+    // Summed in a fixed order (deterministic).
     const int w_lo = (int)(((long)c * f.B) / f.ppw);
     const int w_hi = (int)(((long)(c + 1) * f.B - 1) / f.ppw);
+    const long cB = (long)c * f.B;
     for (int e = tid; e < f.P; e += nthr) {
         float v = 0.f;
         if (f.chunks > 0) {
@@ -41,7 +42,7 @@ __global__ void __launch_bounds__(256) wtc_finalize_kernel(const FinalizeArgs f)
         } else {
 #pragma unroll 4
             for (int w = w_lo; w <= w_hi; ++w) {
-                const int seg = ((long)w * f.ppw) / f.B == c ? 0 : 1;
+                const int seg = (long)w * f.ppw >= cB ? 0 : 1;
                 v += f.partials[((size_t)w * 2 + seg) * f.P + e];
             }
         }
