@@ -839,7 +839,31 @@ wtc_fused_kernel(const FusedArgs a) {
             lds_barrier();
         }
 
-        // ---------------- phase 4a: levels 1 and 2, subband per lane ----------------
+        // ---------------- phase 4a: levels >= 3 flat, then levels 1 and 2 subband per lane ----------------
+        // The deep convolutions (their bands are complete after phase 2/3) come
+        // first, in the same phase as the band-per-lane stencils: their short
+        // chains of LDS reads overlap the stencils' arithmetic.
+        for (int i = 3; i <= Lm; ++i) {
+            const int hi = g.Hq() >> i, wi = g.Wq() >> i, Si = g.b_S(i), bs = g.b_bs(i);
+            const int pi4 = 4 * hi * wi;
+            const FastDiv dpi = make_div(pi4), dwi = make_div(wi);
+            for (int e = tid; e < g.NP() * pi4; e += nthr) {
+                const int s2 = fdiv(e, dpi), m = e - s2 * pi4;
+                if (bb + s2 >= b_end) continue;
+                float* Sl = lds + s2 * g.slot();
+                const int u = m & 3, j = m >> 2;
+                const int jy = fdiv(j, dwi), jx = j - jy * wi;
+                float w[KK];
+                load_w<K, BWD>(wts + ((i - 1) * 4 + u) * KK, w);
+                const float* win = Sl + g.b_off(i) + u * bs + jy * Si + jx;
+                float accv = 0.f;
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) accv = fmaf(w[ky * K + kx], win[ky * Si + kx], accv);
+                Sl[g.yd_off(i) + u * hi * wi + j] = accv;
+            }
+        }
         float y1[BPQ][4][4], y2[BPQ][2][2];
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
@@ -959,27 +983,9 @@ wtc_fused_kernel(const FusedArgs a) {
             }
         }
 
-        // ---------------- phase 4c: levels >= 3, flat ----------------
+        // ---------------- phase 4c: levels >= 3, flat (correlations) ----------------
         for (int i = 3; i <= Lm; ++i) {
             const int hi = g.Hq() >> i, wi = g.Wq() >> i, Si = g.b_S(i), bs = g.b_bs(i);
-            const int pi4 = 4 * hi * wi;
-            const FastDiv dpi = make_div(pi4), dwi = make_div(wi);
-            for (int e = tid; e < g.NP() * pi4; e += nthr) {
-                const int s2 = fdiv(e, dpi), m = e - s2 * pi4;
-                if (bb + s2 >= b_end) continue;
-                float* Sl = lds + s2 * g.slot();
-                const int u = m & 3, j = m >> 2;
-                const int jy = fdiv(j, dwi), jx = j - jy * wi;
-                float w[KK];
-                load_w<K, BWD>(wts + ((i - 1) * 4 + u) * KK, w);
-                const float* win = Sl + g.b_off(i) + u * bs + jy * Si + jx;
-                float accv = 0.f;
-#pragma unroll
-                for (int ky = 0; ky < K; ++ky)
-#pragma unroll
-                    for (int kx = 0; kx < K; ++kx) accv = fmaf(w[ky * K + kx], win[ky * Si + kx], accv);
-                Sl[g.yd_off(i) + u * hi * wi + j] = accv;
-            }
             if constexpr (BWD) {
                 // C_i^du[ky][kx] = sum_m X[m] G[m - (ky - R, kx - R)] (G with its zero
                 // halo): this role takes kernel row dky and its band rows; a chunk of
