@@ -522,9 +522,11 @@ wtc_fused_kernel(const FusedArgs a) {
     // offset within a plane group in device memory, and (packed) its plane
     // slot (bits 16+) and LDS offset (bits 0-15; slots fit in 64K floats);
     // -1 = no unit.  Single-pixel units decode on the fly (16 of them would
-    // take too many registers).
+    // take too many registers): each is decoded once, when its load is issued,
+    // and keeps its LDS destination until the commit.
     const int cplane = a.C * (int)plane_sz;   // < 2^31 / NP when prefetching
     int pf_goff[VEC ? PFU : 1], pf_lds[VEC ? PFU : 1];
+    int pf_dst[VEC ? 1 : PFU];
     if (VEC && pf_on) {
 #pragma unroll
         for (int k = 0; k < PFU; ++k) {
@@ -547,14 +549,18 @@ wtc_fused_kernel(const FusedArgs a) {
             for (int k = 0; k < PFU; ++k)
                 if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) load4(base + pf_goff[k], pf[k]);
         } else {
+            const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
 #pragma unroll
             for (int k = 0; k < PFU; ++k) {
                 const int e = tid + k * nthr;
+                pf_dst[k] = -1;
                 if (e < g.NP() * per) {
                     const int s2 = fdiv(e, dper), m = e - s2 * per;
-                    const int y = fdiv(m, dwv), xq = m - y * wv;
-                    if (bbn + s2 < b_end)
-                        pf[k][0] = to_f32(srcp[((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)y * a.W + xq]);
+                    if (bbn + s2 < b_end) {
+                        pf[k][0] = to_f32(base[s2 * cplane + m]);
+                        const int y = fdiv(m, dwv), xq = m - y * wv;
+                        pf_dst[k] = s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq;
+                    }
                 }
             }
         }
@@ -569,15 +575,10 @@ wtc_fused_kernel(const FusedArgs a) {
                     for (int i = 0; i < UW; ++i) d[i] = pf[k][i];
                 }
         } else {
+            (void)bbn;
 #pragma unroll
-            for (int k = 0; k < PFU; ++k) {
-                const int e = tid + k * nthr;
-                if (e < g.NP() * per) {
-                    const int s2 = fdiv(e, dper), m = e - s2 * per;
-                    const int y = fdiv(m, dwv), xq = m - y * wv;
-                    if (bbn + s2 < b_end) lds[s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq] = pf[k][0];
-                }
-            }
+            for (int k = 0; k < PFU; ++k)
+                if (pf_dst[k] >= 0) lds[pf_dst[k]] = pf[k][0];
         }
     };
     // Direct loads: rows [0, H) of the NP planes starting at batch index bbn go to
