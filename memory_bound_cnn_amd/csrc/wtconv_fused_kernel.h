@@ -78,6 +78,16 @@ __device__ __forceinline__ void load4(const bf16_t* p, float (&v)[4]) {
     v[2] = __uint_as_float(q.y << 16);
     v[3] = __uint_as_float(q.y & 0xFFFF0000u);
 }
+// Two consecutive pixels (the caller guarantees 2-pixel alignment).
+__device__ __forceinline__ void store2(float* p, float v0, float v1) {
+    *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
+}
+__device__ __forceinline__ void store2(bf16_t* p, float v0, float v1) {
+    bf16_t b0, b1;
+    from_f32(b0, v0);
+    from_f32(b1, v1);
+    *reinterpret_cast<uint32_t*>(p) = (uint32_t)b0.bits | ((uint32_t)b1.bits << 16);
+}
 __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
@@ -1115,6 +1125,14 @@ wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (py0 + i < a.H && px0 < a.W) store4(op + i * a.W, acc[s][i]);
+            } else if ((a.W & 1) == 0) {
+                // even width: pixel pairs
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p)
+                        if (py0 + i < a.H && px0 + 2 * p < a.W)
+                            store2(op + i * a.W + 2 * p, acc[s][i][2 * p], acc[s][i][2 * p + 1]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
