@@ -297,6 +297,7 @@ __device__ __forceinline__ float wave_sum(float v, int width_mask_from) {
 // ---------------------------------------------------------------------------
 struct RtGeom {
     static constexpr bool kDL = false;   // the runtime-geometry kernel stages planes through registers
+    static constexpr bool kFixed = false;
     static constexpr bool kNoLevels = false;
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
@@ -334,6 +335,7 @@ template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL
 struct CtGeom {
     static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, MODE, ESZ);
     static constexpr bool kDL = MODE == 1;
+    static constexpr bool kFixed = true;
     static constexpr bool kNoLevels = LM == 0;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
@@ -399,6 +401,29 @@ __device__ __forceinline__ void haar4(float a, float b, float c, float d, float 
     r[3] = d01 - d23;
 }
 
+// Value of v in lane L of this lane's quad (DPP quad permute: every lane of
+// the quad reads lane L).
+template <int L>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), L | (L << 2) | (L << 4) | (L << 6), 0xF, 0xF,
+                                                   false));
+}
+
+// Rows 2*JY and 2*JY + 1 of a quad's 8x8 block, from the four lanes' 4x4
+// blocks xk (lane 2*sy + sx holds rows 4*sy.., columns 4*sx..): r0/r1[h] are
+// columns 4*h .. 4*h + 3.
+template <int JY>
+__device__ __forceinline__ void quad_rows(const float (&xk)[4][4], float (&r0)[2][4], float (&r1)[2][4]) {
+    constexpr int ra = 2 * JY, rb = 2 * JY + 1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        r0[0][q] = quad_bcast<(ra >> 2) * 2>(xk[ra & 3][q]);
+        r0[1][q] = quad_bcast<(ra >> 2) * 2 + 1>(xk[ra & 3][q]);
+        r1[0][q] = quad_bcast<(rb >> 2) * 2>(xk[rb & 3][q]);
+        r1[1][q] = quad_bcast<(rb >> 2) * 2 + 1>(xk[rb & 3][q]);
+    }
+}
+
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(BWD, BPQ, G::kNoLevels))))
 wtc_fused_kernel(const FusedArgs a) {
@@ -409,6 +434,9 @@ wtc_fused_kernel(const FusedArgs a) {
     static_assert(!DL || (VEC && BPQ == 1), "direct loads: 4-pixel rows, one block per quad");
     constexpr bool SDL = DL && sizeof(ST) == 2;           // bf16: raw plane staged, widened per plane
     constexpr bool XDL = DL && BWD && sizeof(ST) == 4;    // fp32 backward: x plane in LDS too
+    // x block of phase 2 reused in phase 4a (fixed geometry only: the
+    // runtime-geometry kernel has no registers to spare)
+    constexpr bool XQB = BWD && !XDL && BPQ == 1 && G::kFixed;
     constexpr int PFF = pf_capacity(BWD, BPQ);  // prefetch capacity, floats per thread
     constexpr int PFU = DL ? 1 : (VEC ? PFF / 4 : PFF);   // prefetch units (4-pixel groups or pixels)
     constexpr int UW = VEC ? 4 : 1;
@@ -714,6 +742,9 @@ wtc_fused_kernel(const FusedArgs a) {
 
         // ---------------- phase 2: base conv; analysis of levels 1..3 ----------------
         float acc[BPQ][4][4];
+        // backward without an LDS copy of x, one block per quad: this lane's 4x4
+        // block of x, kept for phase 4a (the quad's 8x8 block by quad broadcasts)
+        float xkeep[XQB ? 4 : 1][4];
         // raw bands of this lane's block: level 1 at its 2x2 positions [jy][jx][u],
         // level 2 at its position [u], level 3 (band t) at the quad's position
         float hv1[BPQ][2][2][4], hv2[BPQ][4], hv3[BPQ];
@@ -761,6 +792,12 @@ wtc_fused_kernel(const FusedArgs a) {
                 const ST* xp = auxp + poff + opaque(py0 * a.W + px0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ld_row4<VEC>(xp + i * a.W, py0 + i < a.H, px0, a.W, xo[i]);
+                if constexpr (XQB) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) xkeep[i][j] = xo[i][j];
+                }
             }
             const float* win = S + g.a0_off() + py0 * g.a0_S() + px0;
             stencil<K, 4, 4, 4, BWD>(win, g.a0_S(), w, acc[s], xo, corr0);
@@ -896,6 +933,11 @@ wtc_fused_kernel(const FusedArgs a) {
                         lds_row<4, 4>(xr + 4, r0[1]);
                         lds_row<4, 4>(xr + g.xp_S(), r1[0]);
                         lds_row<4, 4>(xr + g.xp_S() + 4, r1[1]);
+                    } else if constexpr (XQB) {
+                        if (jy == 0) quad_rows<0>(xkeep, r0, r1);
+                        if (jy == 1) quad_rows<1>(xkeep, r0, r1);
+                        if (jy == 2) quad_rows<2>(xkeep, r0, r1);
+                        if (jy == 3) quad_rows<3>(xkeep, r0, r1);
                     } else {
                     const ST* p0r = xp + (2 * jy) * a.W;
                     ld_row4<VEC>(p0r, y0 < a.H, 8 * qx, a.W, r0[0]);
