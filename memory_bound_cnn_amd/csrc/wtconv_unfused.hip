@@ -144,12 +144,22 @@ __device__ void stage(float* lds, const T* __restrict__ src, int p0, int pstride
     const int total = t.NPB * RH * SW;
     const uint32_t hw = (uint32_t)t.h * t.w;
     Walk3 it(threadIdx.x, kThreads, SW, RH);
-    for (int f = threadIdx.x; f < total; f += kThreads, it.next()) {
-        const int y = ty0 + it.i1 - halo, x = tx0 + it.i0 - halo;
-        float v = 0.f;
-        if (it.i2 < np_valid && y >= 0 && y < t.h && x >= 0 && x < t.w)
-            v = ldv(src, (uint32_t)(p0 + it.i2 * pstride) * hw + (uint32_t)(y * t.w + x));
-        lds[f] = v;
+    // four elements per thread in flight: their loads are issued before any of
+    // their LDS writes, so one wait covers four loads
+    constexpr int U = 4;
+    for (int f0 = threadIdx.x; f0 < total; f0 += U * kThreads) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int y = ty0 + it.i1 - halo, x = tx0 + it.i0 - halo;
+            v[u] = 0.f;
+            if (f0 + u * kThreads < total && it.i2 < np_valid && y >= 0 && y < t.h && x >= 0 && x < t.w)
+                v[u] = ldv(src, (uint32_t)(p0 + it.i2 * pstride) * hw + (uint32_t)(y * t.w + x));
+            it.next();
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (f0 + u * kThreads < total) lds[f0 + u * kThreads] = v[u];
     }
 }
 
