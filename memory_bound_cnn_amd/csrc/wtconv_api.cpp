@@ -161,7 +161,9 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.NP = NP;
     {
         // prefetch when every thread's share of a plane group fits its capacity
-        const int units = cdiv(NP * per_units, nthr);
+        // (single-pixel units: counted per plane, NP * ceil(H W / threads), the
+        // mapping of the fixed-geometry kernels)
+        const int units = a.vec ? cdiv(NP * per_units, nthr) : NP * cdiv(per_units, nthr);
         a.pf_on = (!a.lay.dl && units * (a.vec ? 4 : 1) <= pf_capacity(bwd, bpq)) ? 1 : 0;
         // the kernel keeps unit offsets within a plane group in 32 bits
         if ((long)NP * d->C * d->H * d->W >= (1L << 31)) a.pf_on = 0;

@@ -586,6 +586,28 @@ wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
             for (int k = 0; k < PFU; ++k)
                 if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) load4(base + pf_goff[k], pf[k]);
+        } else if constexpr (G::kFixed) {
+            // unit k: plane k % NP, in-plane pixel tid + (k / NP) * nthr, so one
+            // row/column decode serves the NP planes (NP is a constant here; the
+            // planner prefetches only when NP * ceil(H W / nthr) units fit)
+            constexpr int NPc = G::NP(), NJ = (PFU + NPc - 1) / NPc;
+            const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
+#pragma unroll
+            for (int jj = 0; jj < NJ; ++jj) {
+                const int m = tid + jj * nthr;
+                const int y = fdiv(m, dwv), xq = m - y * wv;
+                const int dst0 = g.a0_off() + (y + R) * g.a0_S() + R + xq;
+#pragma unroll
+                for (int s2 = 0; s2 < NPc; ++s2) {
+                    const int k = jj * NPc + s2;
+                    if (k >= PFU) continue;
+                    pf_dst[k] = -1;
+                    if (m < per && bbn + s2 < b_end) {
+                        pf[k][0] = to_f32(base[s2 * cplane + m]);
+                        pf_dst[k] = s2 * g.slot() + dst0;
+                    }
+                }
+            }
         } else {
             const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
 #pragma unroll
