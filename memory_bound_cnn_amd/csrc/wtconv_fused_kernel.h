@@ -43,6 +43,8 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "wtc_internal.h"
 
 namespace wtc {
@@ -647,7 +649,33 @@ wtc_fused_kernel(const FusedArgs a) {
     // is the chunk start + 4 l bytes, so lanes past the row end are masked off.
     // Cells outside the interior are never written (zeroed once per segment).
     auto dl_issue = [&](const ST* base, int roff, int rS, int rr, int rc, int bbn) {
-        if constexpr (DL && !SDL) {
+        if constexpr (DL && !SDL && G::kFixed) {
+            // fixed geometry: the row loop is unrolled (no branches between the
+            // copies); rows of a plane are dealt to the waves round-robin
+            static_assert(G::Wq() <= 64, "direct loads: one 64-lane row chunk");
+            constexpr int NW = G::nthr() / 64, NPc = G::NP(), JT = NPc * G::Hq();
+            constexpr int NJ = (JT + NW - 1) / NW;
+            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
+            auto rows = [&](auto full) {
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) {
+                    const int j = wave + jj * NW;
+                    const int s2 = NPc == 1 ? 0 : j / G::Hq();
+                    const int r = j - s2 * G::Hq();
+                    if (JT % NW != 0 && j >= JT) continue;
+                    if (!decltype(full)::value && r >= a.H) continue;
+                    if (NPc > 1 && bbn + s2 >= b_end) continue;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(base + ((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)r * a.W + lane),
+                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc),
+                        4, 0, 0);
+                }
+            };
+            if (lane < a.W) {
+                if (a.H == G::Hq()) rows(std::true_type{});
+                else rows(std::false_type{});
+            }
+        } else if constexpr (DL && !SDL) {
             constexpr int CPR = (G::Wq() + 63) / 64;
             const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
             const int nw = nthr >> 6;
@@ -670,7 +698,31 @@ wtc_fused_kernel(const FusedArgs a) {
     // bf16: the raw planes (H*W 16-bit pixels, contiguous) are copied word by
     // word into the staging area, 64 words per wave instruction
     auto stage_issue = [&](int bbn) {
-        if constexpr (SDL) {
+        if constexpr (SDL && G::kFixed) {
+            // fixed geometry: unrolled over the plane's 64-word chunks
+            constexpr int NW = G::nthr() / 64, NPc = G::NP();
+            constexpr int CH = (G::Hq() * G::Wq() / 2 + 63) / 64, JT = NPc * CH;
+            constexpr int NJ = (JT + NW - 1) / NW;
+            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
+            const int words = (a.H * a.W) >> 1;
+            auto chunks = [&](auto full) {
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) {
+                    const int j = wave + jj * NW;
+                    const int s2 = NPc == 1 ? 0 : j / CH, ch = j - s2 * CH;
+                    if (JT % NW != 0 && j >= JT) continue;
+                    if (NPc > 1 && bbn + s2 >= b_end) continue;
+                    const int i = ch * 64 + lane;
+                    if (!decltype(full)::value && i >= words) continue;
+                    __builtin_amdgcn_global_load_lds(
+                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + c) * plane_sz) +
+                                      i),
+                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + ch * 64), 4, 0, 0);
+                }
+            };
+            if (words == G::Hq() * G::Wq() / 2 && words % 64 == 0) chunks(std::true_type{});
+            else chunks(std::false_type{});
+        } else if constexpr (SDL) {
             const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
             const int nw = nthr >> 6;
             const int words = (a.H * a.W) >> 1, chunks = (words + 63) >> 6;
