@@ -48,6 +48,13 @@ constexpr int lay_round_up(int v, int m) { return (v + m - 1) / m * m; }
 
 // The one definition of the slot layout, evaluated on the host for the
 // runtime-geometry kernel and at compile time for the fixed-geometry ones.
+// Floats of the backward reduction scratch: per 16-lane row of the workgroup
+// C_0 (k^2), C_1 and C_2 (4 k^2 each), sum g and the tail term; then the deep
+// levels' output-stationary partials (levels 3..Lm, 4 k dsub roles of k).
+constexpr int red_len(int nthr, int k, int Lm, int dsub) {
+    return (nthr / 16) * (9 * k * k + 2) + (Lm > 2 ? Lm - 2 : 0) * 4 * k * dsub * k;
+}
+
 constexpr Layout make_layout(int k, int Hq, int Wq, int Lm, int early_req, bool bwd, int bovl, int mode = 0,
                              int esize = 4) {
     Layout L{};

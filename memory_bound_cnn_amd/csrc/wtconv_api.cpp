@@ -107,7 +107,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     best.score = -1;
     auto consider = [&](const Layout& lay, int NP, int nthr, int bpq) {
         const int dsub = std::max(1, nthr / (4 * k));
-        const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * k * dsub * k;
+        const int red_n = red_len(nthr, k, a.Lm, dsub);
         const size_t lds = (size_t)std::max(NP * lay.slot + wts_n, bwd ? red_n : 0) * 4;
         if (lds > kLdsLimit || NP * per_units >= 65536) return;   // fast in-kernel division range
         // plain depthwise conv (no levels) on a plane class with fixed-geometry
@@ -173,7 +173,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.P = partial_len(k, a.Lm);
     // reduction scratch reuses the plane slots after the last plane
     a.red_off = 0;
-    const int red_n = (nthr / 64) * (9 * KK + 2) + std::max(0, a.Lm - 2) * 4 * k * a.dsub * k;
+    const int red_n = red_len(nthr, k, a.Lm, a.dsub);
     size_t lds_floats = (size_t)std::max(NP * slot + wts_n, bwd ? red_n : 0);
     p->lds = lds_floats * 4;
     if (p->lds > kLdsLimit) return WTC_ESHAPE;

@@ -285,10 +285,23 @@ __device__ __forceinline__ int opaque(int v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v, int width_mask_from) {
-    // xor-butterfly over lane bits >= log2(width_mask_from)
-    for (int m = width_mask_from; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-    return v;
+// Value of v in lane l - N of the same 16-lane row (0 for the row's first N
+// lanes): a DPP row shift, plain VALU with no LDS round trip.
+template <int N>
+__device__ __forceinline__ float row_shr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 | N, 0xF, 0xF, true));
+}
+// Lanes 12..15 of every 16-lane row: the sum of v over the row's four lanes
+// with the same lane index mod 4 (lane 12 + r holds residue r).
+__device__ __forceinline__ float row_sum_by_residue(float v) {
+    v += row_shr<4>(v);
+    return v + row_shr<8>(v);
+}
+// Lane 15 of every 16-lane row: the sum of v over the row.
+__device__ __forceinline__ float row_sum(float v) {
+    v = row_sum_by_residue(v);
+    v += row_shr<1>(v);
+    return v + row_shr<2>(v);
 }
 
 // ---------------------------------------------------------------------------
@@ -1260,31 +1273,42 @@ wtc_fused_kernel(const FusedArgs a) {
     }
     if constexpr (BWD) {
         // ---------------- reduction of the correlation accumulators ----------------
+        // Row sums by DPP (four steps per accumulator, all independent), then
+        // one partial per 16-lane row in LDS, summed in a fixed order.
         lds_barrier();
         float* red = lds + g.red_off();
-        const int nw = nthr >> 6, wave = tid >> 6, lane = tid & 63;
-        // per-wave record: [C_0 (KK)][C_1 u=0..3 (KK each)][C_2 u=0..3][sumg][tail]
-        const int WR = KK * 9 + 2;
+        const int nw = nthr >> 6, lane = tid & 63;
+        const int NR = nw * 4, row = (tid >> 6) * 4 + ((lane >> 4) & 3);
+        // [C_0: NR x KK][C_1: NR x 4 x KK][C_2: NR x 4 x KK][sum g: NR][tail: NR][deep]
+        float* r0 = red;
+        float* r1 = r0 + NR * KK;
+        float* r2 = r1 + NR * 4 * KK;
+        float* rs = r2 + NR * 4 * KK;
+        float* rt = rs + NR;
+        float* dred = rt + NR;   // deep: [q][role]
 #pragma unroll
         for (int q = 0; q < KK; ++q) {
-            const float v0 = wave_sum(corr0[q], 1);
-            const float v1 = wave_sum(corr1[q], 4);
-            const float v2 = wave_sum(corr2[q], 4);
-            // un-rotate: accumulator q holds tap KK-1-q
-            if (lane == 0) red[wave * WR + (KK - 1 - q)] = v0;
-            if (lane < 4) {
-                red[wave * WR + KK + lane * KK + (KK - 1 - q)] = v1;
-                red[wave * WR + 5 * KK + lane * KK + (KK - 1 - q)] = v2;
+            corr0[q] = row_sum(corr0[q]);
+            corr1[q] = row_sum_by_residue(corr1[q]);
+            corr2[q] = row_sum_by_residue(corr2[q]);
+        }
+        sumg = row_sum(sumg);
+        tailc = row_sum(tailc);
+        // un-rotate: accumulator q holds tap KK-1-q; band u = lane mod 4
+        if ((lane & 15) >= 12) {
+            const int u = lane & 3;
+#pragma unroll
+            for (int q = 0; q < KK; ++q) {
+                r1[(row * 4 + u) * KK + (KK - 1 - q)] = corr1[q];
+                r2[(row * 4 + u) * KK + (KK - 1 - q)] = corr2[q];
+            }
+            if (u == 3) {
+#pragma unroll
+                for (int q = 0; q < KK; ++q) r0[row * KK + (KK - 1 - q)] = corr0[q];
+                rs[row] = sumg;
+                rt[row] = tailc;
             }
         }
-        {
-            const float vs = wave_sum(sumg, 1), vt = wave_sum(tailc, 1);
-            if (lane == 0) {
-                red[wave * WR + 9 * KK] = vs;
-                red[wave * WR + 9 * KK + 1] = vt;
-            }
-        }
-        float* dred = red + nw * WR;   // deep: [q][role]
         if (dactive) {
 #pragma unroll
             for (int q = 0; q < kMaxLm - 2; ++q)
@@ -1297,22 +1321,23 @@ wtc_fused_kernel(const FusedArgs a) {
         for (int e = tid; e < g.P(); e += nthr) {
             float v = 0.f;
             if (e < KK) {
-                for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + e];
+                for (int i = 0; i < NR; ++i) v += r0[i * KK + e];
             } else if (e < KK + 4 * KK * Lm) {
                 const int lvl = (e - KK) / (4 * KK) + 1;
                 const int rem = (e - KK) - (lvl - 1) * 4 * KK;
                 if (lvl <= 2) {
-                    const int base = (lvl == 1) ? KK : 5 * KK;
-                    for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + base + rem];
+                    const float* rl = lvl == 1 ? r1 : r2;
+                    const int u = rem / KK, tap = rem - u * KK;
+                    for (int i = 0; i < NR; ++i) v += rl[(i * 4 + u) * KK + tap];
                 } else {
                     const int u = rem / KK, tap = rem - u * KK, ky = tap / K, kx = tap - ky * K;
                     for (int sb = 0; sb < g.dsub(); ++sb)
                         v += dred[((lvl - 3) * droles + (sb * K + ky) * 4 + u) * K + kx];
                 }
             } else if (e == g.P() - 2) {
-                for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + 9 * KK];
+                for (int i = 0; i < NR; ++i) v += rs[i];
             } else {
-                for (int wv = 0; wv < nw; ++wv) v += red[wv * WR + 9 * KK + 1];
+                for (int i = 0; i < NR; ++i) v += rt[i];
             }
             rec[e] = v;
         }
