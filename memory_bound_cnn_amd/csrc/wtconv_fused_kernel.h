@@ -509,57 +509,6 @@ wtc_fused_kernel(const FusedArgs a) {
     const int b_begin = (int)(qs - (long)c * a.B);
     const int b_end = (int)(qe - (long)c * a.B);
     lds_barrier();  // the previous segment is done with the weights and the slots
-    // ---- zero the halo rings: per segment (the backward reduction reuses the
-    // slots), and per plane where regions overlap ----
-    for (int s2 = 0; s2 < g.NP(); ++s2) {
-        float* S = lds + s2 * g.slot();
-        zero_ring(S + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
-        for (int i = 1; i <= Lm; ++i)
-            for (int u = 0; u < 4; ++u)
-                zero_ring(S + g.b_off(i) + u * g.b_bs(i), g.b_rows(i), g.b_S(i), R, g.Hq() >> i, R,
-                          g.Wq() >> i, tid, nthr);
-    }
-    // ---- fold scales and Haar normalisations into the level weights ----
-    // W'_i = 4^-i s_i W_i (LDS, per workgroup).  The base weights stay unfolded;
-    // s0 is applied once per output pixel, fused with the synthesis add.
-    // Every parameter is read from device memory here, once per workgroup: no
-    // vector-memory load may sit behind the next planes' prefetch in the plane
-    // loop (vector-memory completions are counted in order).
-    float* wts = lds + g.wts_off();
-    float* wbase = wts + 4 * a.L * KK;          // unfolded base weights W0[c]
-    for (int e = tid; e < 4 * a.L * KK; e += nthr) {
-        const int i = e / (4 * KK), rem = e - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
-        const float sc = ldexpf(a.sl[((size_t)i * a.C + c) * 4 + u], -2 * (i + 1));
-        wts[e] = sc * a.wl[(((size_t)i * a.C + c) * 4 + u) * KK + tap];
-    }
-    for (int e = tid; e < KK; e += nthr) wbase[e] = a.w0[(size_t)c * KK + e];
-    if (tid == 0) {
-        wbase[KK] = BWD ? 0.f : a.b0[c];
-        wbase[KK + 1] = a.s0[c];
-    }
-
-    lds_barrier();
-    // tail levels (1x1 grids): kappa = sum of their folded centre taps
-    float kappa = 0.f;
-    for (int i = Lm; i < a.L; ++i)
-        for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KK + (KK >> 1)];
-
-    // ---- persistent backward accumulators ----
-    float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm - 2][K];
-#pragma unroll
-    for (int i = 0; i < KK; ++i) corr0[i] = corr1[i] = corr2[i] = 0.f;
-#pragma unroll
-    for (int q = 0; q < kMaxLm - 2; ++q)
-#pragma unroll
-        for (int kx = 0; kx < K; ++kx) cdeep[q][kx] = 0.f;
-    float sumg = 0.f, tailc = 0.f;
-    // deep-level (>= 3) correlation role: subband du, kernel row dky, band rows
-    // dsb, dsb + dsub, ...; one accumulator per kernel column
-    const int drole = tid;
-    const int droles = 4 * K * g.dsub();
-    const bool dactive = BWD && drole < droles;
-    const int du = drole & 3, dky = (drole >> 2) % K, dsb = (drole >> 2) / K;
-
     const ST* srcp = reinterpret_cast<const ST*>(a.src);
     const ST* auxp = reinterpret_cast<const ST*>(a.aux);
     ST* dstp = reinterpret_cast<ST*>(a.dst);
@@ -751,6 +700,8 @@ wtc_fused_kernel(const FusedArgs a) {
             }
         }
     };
+    // the first planes' copies are issued before the set-up below, which they
+    // do not touch (interiors of the staging areas vs rings and weights)
     if (pf_on) pf_issue(b_begin);
     if constexpr (XDL) {
         for (int s2 = 0; s2 < g.NP(); ++s2)
@@ -759,6 +710,57 @@ wtc_fused_kernel(const FusedArgs a) {
     }
     if constexpr (DL && !SDL) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, b_begin);
     if constexpr (SDL) stage_issue(b_begin);
+
+    // ---- zero the halo rings: per segment (the backward reduction reuses the
+    // slots), and per plane where regions overlap ----
+    for (int s2 = 0; s2 < g.NP(); ++s2) {
+        float* S = lds + s2 * g.slot();
+        zero_ring(S + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
+        for (int i = 1; i <= Lm; ++i)
+            for (int u = 0; u < 4; ++u)
+                zero_ring(S + g.b_off(i) + u * g.b_bs(i), g.b_rows(i), g.b_S(i), R, g.Hq() >> i, R,
+                          g.Wq() >> i, tid, nthr);
+    }
+    // ---- fold scales and Haar normalisations into the level weights ----
+    // W'_i = 4^-i s_i W_i (LDS, per workgroup).  The base weights stay unfolded;
+    // s0 is applied once per output pixel, fused with the synthesis add.
+    // Every parameter is read from device memory here, once per workgroup: no
+    // vector-memory load may sit behind the next planes' prefetch in the plane
+    // loop (vector-memory completions are counted in order).
+    float* wts = lds + g.wts_off();
+    float* wbase = wts + 4 * a.L * KK;          // unfolded base weights W0[c]
+    for (int e = tid; e < 4 * a.L * KK; e += nthr) {
+        const int i = e / (4 * KK), rem = e - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
+        const float sc = ldexpf(a.sl[((size_t)i * a.C + c) * 4 + u], -2 * (i + 1));
+        wts[e] = sc * a.wl[(((size_t)i * a.C + c) * 4 + u) * KK + tap];
+    }
+    for (int e = tid; e < KK; e += nthr) wbase[e] = a.w0[(size_t)c * KK + e];
+    if (tid == 0) {
+        wbase[KK] = BWD ? 0.f : a.b0[c];
+        wbase[KK + 1] = a.s0[c];
+    }
+
+    lds_barrier();
+    // tail levels (1x1 grids): kappa = sum of their folded centre taps
+    float kappa = 0.f;
+    for (int i = Lm; i < a.L; ++i)
+        for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KK + (KK >> 1)];
+
+    // ---- persistent backward accumulators ----
+    float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm - 2][K];
+#pragma unroll
+    for (int i = 0; i < KK; ++i) corr0[i] = corr1[i] = corr2[i] = 0.f;
+#pragma unroll
+    for (int q = 0; q < kMaxLm - 2; ++q)
+#pragma unroll
+        for (int kx = 0; kx < K; ++kx) cdeep[q][kx] = 0.f;
+    float sumg = 0.f, tailc = 0.f;
+    // deep-level (>= 3) correlation role: subband du, kernel row dky, band rows
+    // dsb, dsb + dsub, ...; one accumulator per kernel column
+    const int drole = tid;
+    const int droles = 4 * K * g.dsub();
+    const bool dactive = BWD && drole < droles;
+    const int du = drole & 3, dky = (drole >> 2) % K, dsb = (drole >> 2) / K;
 
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
