@@ -312,6 +312,7 @@ __device__ __forceinline__ float row_sum(float v) {
 // ---------------------------------------------------------------------------
 struct RtGeom {
     static constexpr bool kDL = false;   // the runtime-geometry kernel stages planes through registers
+    static constexpr bool kXSeg = false;
     static constexpr bool kFixed = false;
     static constexpr bool kNoLevels = false;
     const FusedArgs& a;
@@ -350,6 +351,10 @@ template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL
 struct CtGeom {
     static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, MODE, ESZ);
     static constexpr bool kDL = MODE == 1;
+    // direct loads may run ahead into the next channel segment: the backward
+    // reduction scratch (from offset 0) ends before the first copy target
+    static constexpr bool kXSeg =
+        MODE == 1 && (!BWDL || red_len(NTHR, K, LM, NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1) <= lay.a0_off);
     static constexpr bool kFixed = true;
     static constexpr bool kNoLevels = LM == 0;
     const FusedArgs& a;
@@ -610,7 +615,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // one 64-pixel row chunk per wave instruction; the LDS destination of lane l
     // is the chunk start + 4 l bytes, so lanes past the row end are masked off.
     // Cells outside the interior are never written (zeroed once per segment).
-    auto dl_issue = [&](const ST* base, int roff, int rS, int rr, int rc, int bbn) {
+    auto dl_issue = [&](const ST* base, int roff, int rS, int rr, int rc, int bbn, int ch, int bend) {
         if constexpr (DL && !SDL && G::kFixed) {
             // fixed geometry: the row loop is unrolled (no branches between the
             // copies); rows of a plane are dealt to the waves round-robin
@@ -626,9 +631,9 @@ wtc_fused_kernel(const FusedArgs a) {
                     const int r = j - s2 * G::Hq();
                     if (JT % NW != 0 && j >= JT) continue;
                     if (!decltype(full)::value && r >= a.H) continue;
-                    if (NPc > 1 && bbn + s2 >= b_end) continue;
+                    if (NPc > 1 && bbn + s2 >= bend) continue;
                     __builtin_amdgcn_global_load_lds(
-                        (const void*)(base + ((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)r * a.W + lane),
+                        (const void*)(base + ((size_t)(bbn + s2) * a.C + ch) * plane_sz + (size_t)r * a.W + lane),
                         (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc),
                         4, 0, 0);
                 }
@@ -645,21 +650,21 @@ wtc_fused_kernel(const FusedArgs a) {
             for (int j = wave; j < g.NP() * per_plane; j += nw) {
                 const int s2 = g.NP() == 1 ? 0 : j / per_plane;
                 const int m = j - s2 * per_plane;
-                const int r = CPR == 1 ? m : m / CPR, ch = m - r * CPR;
-                if (bbn + s2 >= b_end) continue;
-                const int col = ch * 64 + lane;
+                const int r = CPR == 1 ? m : m / CPR, cc = m - r * CPR;
+                if (bbn + s2 >= bend) continue;
+                const int col = cc * 64 + lane;
                 if (col < a.W)
                     __builtin_amdgcn_global_load_lds(
-                        (const void*)(base + ((size_t)(bbn + s2) * a.C + c) * plane_sz + (size_t)r * a.W + col),
+                        (const void*)(base + ((size_t)(bbn + s2) * a.C + ch) * plane_sz + (size_t)r * a.W + col),
                         (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc +
-                                                                   ch * 64),
+                                                                   cc * 64),
                         4, 0, 0);
             }
         }
     };
     // bf16: the raw planes (H*W 16-bit pixels, contiguous) are copied word by
     // word into the staging area, 64 words per wave instruction
-    auto stage_issue = [&](int bbn) {
+    auto stage_issue = [&](int bbn, int ch, int bend) {
         if constexpr (SDL && G::kFixed) {
             // fixed geometry: unrolled over the plane's 64-word chunks
             constexpr int NW = G::nthr() / 64, NPc = G::NP();
@@ -671,15 +676,15 @@ wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj) {
                     const int j = wave + jj * NW;
-                    const int s2 = NPc == 1 ? 0 : j / CH, ch = j - s2 * CH;
+                    const int s2 = NPc == 1 ? 0 : j / CH, k = j - s2 * CH;
                     if (JT % NW != 0 && j >= JT) continue;
-                    if (NPc > 1 && bbn + s2 >= b_end) continue;
-                    const int i = ch * 64 + lane;
+                    if (NPc > 1 && bbn + s2 >= bend) continue;
+                    const int i = k * 64 + lane;
                     if (!decltype(full)::value && i >= words) continue;
                     __builtin_amdgcn_global_load_lds(
-                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + c) * plane_sz) +
+                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + ch) * plane_sz) +
                                       i),
-                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + ch * 64), 4, 0, 0);
+                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + k * 64), 4, 0, 0);
                 }
             };
             if (words == G::Hq() * G::Wq() / 2 && words % 64 == 0) chunks(std::true_type{});
@@ -689,27 +694,35 @@ wtc_fused_kernel(const FusedArgs a) {
             const int nw = nthr >> 6;
             const int words = (a.H * a.W) >> 1, chunks = (words + 63) >> 6;
             for (int j = wave; j < g.NP() * chunks; j += nw) {
-                const int s2 = g.NP() == 1 ? 0 : j / chunks, ch = j - s2 * chunks;
-                if (bbn + s2 >= b_end) continue;
-                const int i = ch * 64 + lane;
+                const int s2 = g.NP() == 1 ? 0 : j / chunks, k = j - s2 * chunks;
+                if (bbn + s2 >= bend) continue;
+                const int i = k * 64 + lane;
                 if (i < words)
                     __builtin_amdgcn_global_load_lds(
-                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + c) * plane_sz) +
+                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + ch) * plane_sz) +
                                       i),
-                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + ch * 64), 4, 0, 0);
+                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + k * 64), 4, 0, 0);
             }
         }
     };
     // the first planes' copies are issued before the set-up below, which they
     // do not touch (interiors of the staging areas vs rings and weights)
+    // (a second channel segment's first copies were issued at the end of the
+    // first segment, where the layout allows it)
+    constexpr bool XSEG = DL && G::kXSeg;
+    const bool pre = XSEG && seg == 1;
     if (pf_on) pf_issue(b_begin);
     if constexpr (XDL) {
         for (int s2 = 0; s2 < g.NP(); ++s2)
             zero_ring(lds + s2 * g.slot() + g.xp_off(), g.Hq(), g.xp_S(), 0, a.H, 0, a.W, tid, nthr);
-        dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, b_begin);
+        if (!pre) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, b_begin, c, b_end);
     }
-    if constexpr (DL && !SDL) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, b_begin);
-    if constexpr (SDL) stage_issue(b_begin);
+    if constexpr (DL && !SDL) {
+        if (!pre) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, b_begin, c, b_end);
+    }
+    if constexpr (SDL) {
+        if (!pre) stage_issue(b_begin, c, b_end);
+    }
 
     // ---- zero the halo rings: per segment (the backward reduction reuses the
     // slots), and per plane where regions overlap ----
@@ -793,7 +806,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 // the staging area is free: the next planes' copies land meanwhile
                 // (backward: after this plane's last x load, whose wait would
                 // otherwise also wait for the copy, vector-memory counts being in order)
-                if (!BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP());
+                if (!BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP(), c, b_end);
             }
         } else {
         lds_barrier();  // the previous plane is fully consumed
@@ -951,7 +964,7 @@ wtc_fused_kernel(const FusedArgs a) {
         }
         lds_barrier();
         // the level-0 plane is dead: the next planes' copies land during the rest
-        if (DL && !SDL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP());
+        if (DL && !SDL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP(), c, b_end);
 
         // ---------------- phase 3: analysis of levels early_lv+1..Lm ----------------
         for (int i = g.early() + 1; i <= Lm; ++i) {
@@ -1091,14 +1104,14 @@ wtc_fused_kernel(const FusedArgs a) {
             if (tail && qpb[s] == 0 && t == 0) S[g.tail_off()] = S[g.b_off(Lm) + R * g.b_S(Lm) + R] * kappa;
         }
 
-        if (SDL && BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP());
+        if (SDL && BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP(), c, b_end);
 
         // ---------------- phase 4b: x bands of levels >= 4 (backward) ----------------
         if constexpr (BWD) {
             if (Lm >= 3) {
                 lds_barrier();  // band 0 of level 3 (x) written in phase 4a
                 // every wave is done with the x plane: the next one lands meanwhile
-                if (XDL && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
+                if (XDL && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP(), c, b_end);
                 for (int i = 4; i <= Lm; ++i) {
                     const int hi = g.Hq() >> i, wi = g.Wq() >> i, wp = g.Wq() >> (i - 1);
                     const int pi = hi * wi;
@@ -1166,7 +1179,7 @@ wtc_fused_kernel(const FusedArgs a) {
             }
         }
         lds_barrier();
-        if (XDL && Lm < 3 && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP());
+        if (XDL && Lm < 3 && bb + g.NP() < b_end) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, bb + g.NP(), c, b_end);
 
         // ---------------- phase 4d: levels 1, 2 results in place ----------------
 #pragma unroll
@@ -1271,6 +1284,17 @@ wtc_fused_kernel(const FusedArgs a) {
                     for (int j = 0; j < 4; ++j)
                         if (py0 + i < a.H && px0 + j < a.W) from_f32(op[i * a.W + j], acc[s][i][j]);
             }
+        }
+    }
+    if constexpr (XSEG) {
+        // every wave is past this segment's last phase 2 and 4b, so the copy
+        // targets are free: the next segment's first planes land during the
+        // reduction and set-up
+        if (seg == 0 && q1 > (long)(c + 1) * a.B) {
+            const int bend_next = (int)(min(q1, (long)(c + 2) * a.B) - (long)(c + 1) * a.B);
+            if constexpr (XDL) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, 0, c + 1, bend_next);
+            if constexpr (!SDL) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, 0, c + 1, bend_next);
+            if constexpr (SDL) stage_issue(0, c + 1, bend_next);
         }
     }
     if constexpr (BWD) {
