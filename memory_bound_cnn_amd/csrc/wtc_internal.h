@@ -245,7 +245,7 @@ struct UnfusedPlan {
 };
 
 // workgroups per channel of the baseline's weight-gradient correlation
-int unfused_corr_blocks(int nb, int nch);
+int unfused_corr_blocks(int nb, int nch, int h, int w);
 int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p);
 // stage 0: the whole pipeline; 1: only the analysis cascades (into the
 // workspace); 2: everything after them, with `zext` (may be null) added to the

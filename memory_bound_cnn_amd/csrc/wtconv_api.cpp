@@ -491,9 +491,9 @@ double io_unfused(const wtc_desc* d, int dir) {
     // partials written and read back; parameters read twice, gradients written
     for (int i = 1; i <= d->L; ++i) {
         t += 8.0 * band(i);
-        t += 2.0 * f4 * unfused_corr_blocks(d->B, 4 * d->C) * 4.0 * d->C * kk1;
+        t += 2.0 * f4 * unfused_corr_blocks(d->B, 4 * d->C, p.h[i], p.w[i]) * 4.0 * d->C * kk1;
     }
-    t += 2.0 * N * e + 2.0 * f4 * unfused_corr_blocks(d->B, d->C) * (double)d->C * kk1;
+    t += 2.0 * N * e + 2.0 * f4 * unfused_corr_blocks(d->B, d->C, d->H, d->W) * (double)d->C * kk1;
     return t + 3.0 * params;
 }
 

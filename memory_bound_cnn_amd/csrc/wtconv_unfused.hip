@@ -331,6 +331,191 @@ __global__ void __launch_bounds__(kThreads) k_tcorr(const TA* __restrict__ A, co
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large planes (both sides >= kBigSide): 64 x 64 tiles, each thread a 4 x 4
+// block with a register-blocked window (two window rows live, read as 16-byte
+// LDS rows), so a window row of X serves 4 x K multiply-adds per value.
+// ---------------------------------------------------------------------------
+constexpr int kBigTile = 64;
+constexpr int kBigSide = 48;
+
+__host__ __device__ constexpr int big_xs_stride(int R) { return (kBigTile + 2 * R + 3) & ~3; }
+
+bool big_planes(int h, int w) { return h >= kBigSide && w >= kBigSide; }
+
+// Stage rows [y0, y0 + rows) x columns [x0, x0 + cols) of plane `src` (h x w,
+// zero outside) into lds[r * stride + c]; cols <= 64 + 2 * kMaxK.  Wave v takes
+// rows v, v + 4, ...; lane l column l (and l + 64 where cols > 64).  All loads
+// of a thread are issued before its LDS writes.
+template <int ROWS, int COLS, typename T>
+__device__ __forceinline__ void stage_rows(float* lds, int stride, const T* __restrict__ src, int h, int w, int y0,
+                                           int x0) {
+    constexpr int NW = kThreads / 64, RPW = (ROWS + NW - 1) / NW, CPL = (COLS + 63) / 64;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float v[RPW][CPL];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int r = wave + k * NW, c = lane + cc * 64;
+            const int y = y0 + r, x = x0 + c;
+            v[k][cc] = (r < ROWS && c < COLS && y >= 0 && y < h && x >= 0 && x < w) ? ldv(src, (uint32_t)(y * w + x)) : 0.f;
+        }
+#pragma unroll
+    for (int k = 0; k < RPW; ++k)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const int r = wave + k * NW, c = lane + cc * 64;
+            if (r < ROWS && c < COLS) lds[r * stride + c] = v[k][cc];
+        }
+}
+
+// Read WW consecutive floats of a 16-byte aligned LDS row.
+template <int WW>
+__device__ __forceinline__ void lds_row4(const float* p, float (&row)[WW]) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int q = 0; q + 4 <= WW; q += 4) {
+        const f4 v = *reinterpret_cast<const f4*>(p + q);
+        row[q] = v.x; row[q + 1] = v.y; row[q + 2] = v.z; row[q + 3] = v.w;
+    }
+    constexpr int done = (WW / 4) * 4;
+    if constexpr (WW - done >= 2) {
+        const f2 v = *reinterpret_cast<const f2*>(p + done);
+        row[done] = v.x; row[done + 1] = v.y;
+    }
+    if constexpr ((WW - done) % 2 == 1) row[WW - 1] = p[WW - 1];
+}
+
+// Same contract as k_tcorr, for large planes: the units of channel ch are
+// (batch entry, 64 x 64 tile) pairs, nb * ntile of them, split evenly over the
+// nblk workgroups of the channel (grid nch x nblk).
+template <int K, typename TA, typename TX>
+__global__ void __launch_bounds__(kThreads) k_tcorr_big(const TA* __restrict__ A, const TX* __restrict__ X, int nb,
+                                                        int nch, int h, int w, int ntx, int nty, int nblk,
+                                                        float* __restrict__ part) {
+    constexpr int R = K / 2, KK = K * K, WW = 4 + 2 * R, NW = kThreads / 64;
+    constexpr int SA = kBigTile + 4, SX = big_xs_stride(R);
+    __shared__ __align__(16) float as[kBigTile * SA];
+    __shared__ __align__(16) float xs[(kBigTile + 2 * R) * SX];
+    __shared__ float red[NW][KK + 1];
+    const int ch = blockIdx.x, blk = blockIdx.y;
+    const int ntile = ntx * nty, units = nb * ntile;
+    const int u0 = (int)((long)units * blk / nblk), u1 = (int)((long)units * (blk + 1) / nblk);
+    const uint32_t hw = (uint32_t)h * w;
+    const int qy = threadIdx.x >> 4, qx = threadIdx.x & 15;
+    float acc[KK + 1];
+#pragma unroll
+    for (int d = 0; d <= KK; ++d) acc[d] = 0.f;
+    for (int u = u0; u < u1; ++u) {
+        const int b = u / ntile, tile = u - b * ntile;
+        const int ty0 = (tile / ntx) * kBigTile, tx0 = (tile % ntx) * kBigTile;
+        const uint32_t pbase = (uint32_t)(b * nch + ch) * hw;
+        __syncthreads();   // the previous unit's reads are done
+        stage_rows<kBigTile, kBigTile>(as, SA, A + pbase, h, w, ty0, tx0);
+        stage_rows<kBigTile + 2 * R, kBigTile + 2 * R>(xs, SX, X + pbase, h, w, ty0 - R, tx0 - R);
+        __syncthreads();
+        float a[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lds_row4<4>(as + (4 * qy + i) * SA + 4 * qx, a[i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[KK] += (a[i][0] + a[i][1]) + (a[i][2] + a[i][3]);
+        const float* xb = xs + (4 * qy) * SX + 4 * qx;
+        float rows[2][WW];
+        lds_row4<WW>(xb, rows[0]);
+#pragma unroll
+        for (int wy = 0; wy < 4 + 2 * R; ++wy) {
+            float (&row)[WW] = rows[wy & 1];
+            if (wy + 1 < 4 + 2 * R) lds_row4<WW>(xb + (wy + 1) * SX, rows[(wy + 1) & 1]);
+#pragma unroll
+            for (int oy = 0; oy < 4; ++oy) {
+                const int ky = wy - oy;
+                if (ky < 0 || ky >= K) continue;
+#pragma unroll
+                for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                    for (int ox = 0; ox < 4; ++ox) acc[ky * K + kx] = fmaf(a[oy][ox], row[ox + kx], acc[ky * K + kx]);
+            }
+        }
+    }
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 0; d <= KK; ++d) {
+        float v = acc[d];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) red[wv][d] = v;
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d <= KK; d += kThreads) {
+        float s = 0.f;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) s += red[q][d];
+        part[((uint32_t)blk * nch + ch) * (KK + 1) + d] = s;
+    }
+}
+
+// Same contract as k_tconv, for large planes: one workgroup per (plane,
+// 64 x 64 tile), grid P * ntile.
+template <int K, bool ROT, typename TI, typename TO>
+__global__ void __launch_bounds__(kThreads) k_tconv_big(const TI* __restrict__ in, int nch, int h, int w, int ntx,
+                                                        int nty, const float* __restrict__ wt,
+                                                        const float* __restrict__ scale,
+                                                        const float* __restrict__ bias, const float* __restrict__ Z,
+                                                        TO* __restrict__ out) {
+    constexpr int R = K / 2, KK = K * K, WW = 4 + 2 * R, SX = big_xs_stride(R);
+    __shared__ __align__(16) float xs[(kBigTile + 2 * R) * SX];
+    const int ntile = ntx * nty;
+    const int p = blockIdx.x / ntile, tile = blockIdx.x - p * ntile;
+    const int ty0 = (tile / ntx) * kBigTile, tx0 = (tile % ntx) * kBigTile;
+    const int ch = p % nch;
+    const uint32_t hw = (uint32_t)h * w, pbase = (uint32_t)p * hw;
+    stage_rows<kBigTile + 2 * R, kBigTile + 2 * R>(xs, SX, in + pbase, h, w, ty0 - R, tx0 - R);
+    float wk[KK];
+#pragma unroll
+    for (int q = 0; q < KK; ++q) wk[q] = wt[ch * KK + (ROT ? KK - 1 - q : q)];
+    const float sc = scale[ch], bi = bias ? bias[ch] : 0.f;
+    __syncthreads();
+    const int qy = threadIdx.x >> 4, qx = threadIdx.x & 15;
+    float acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    const float* xb = xs + (4 * qy) * SX + 4 * qx;
+    float rows[2][WW];
+    lds_row4<WW>(xb, rows[0]);
+#pragma unroll
+    for (int wy = 0; wy < 4 + 2 * R; ++wy) {
+        float (&row)[WW] = rows[wy & 1];
+        if (wy + 1 < 4 + 2 * R) lds_row4<WW>(xb + (wy + 1) * SX, rows[(wy + 1) & 1]);
+#pragma unroll
+        for (int oy = 0; oy < 4; ++oy) {
+            const int ky = wy - oy;
+            if (ky < 0 || ky >= K) continue;
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                for (int ox = 0; ox < 4; ++ox) acc[oy][ox] = fmaf(wk[ky * K + kx], row[ox + kx], acc[oy][ox]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int y = ty0 + 4 * qy + i;
+        if (y >= h) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int x = tx0 + 4 * qx + j;
+            if (x >= w) continue;
+            const uint32_t o = pbase + (uint32_t)(y * w + x);
+            float v = fmaf(sc, acc[i][j], bi);
+            if (Z) v += Z[o];
+            stv(out, o, v);
+        }
+    }
+}
+
 // dW = s * C, ds = sum_d W * C, and (base level) db = sum g, from the partials.
 // One workgroup of 64 lanes per channel, lane d < K*K+1 sums slot d over the
 // partial blocks in a fixed order.
@@ -376,6 +561,17 @@ void launch_synthesis(const float* Y, const float* Zd, int P, int h, int w, floa
 template <int K, typename TI, typename TO>
 void launch_conv(bool rot, const TI* in, int P, int nch, int h, int w, const float* wt, const float* scale,
                  const float* bias, const float* Z, TO* out, hipStream_t st) {
+    if (big_planes(h, w)) {
+        const int ntx = (w + kBigTile - 1) / kBigTile, nty = (h + kBigTile - 1) / kBigTile;
+        const uint32_t grid = (uint32_t)P * ntx * nty;
+        if (rot)
+            hipLaunchKernelGGL((k_tconv_big<K, true, TI, TO>), dim3(grid), dim3(kThreads), 0, st, in, nch, h, w, ntx,
+                               nty, wt, scale, bias, Z, out);
+        else
+            hipLaunchKernelGGL((k_tconv_big<K, false, TI, TO>), dim3(grid), dim3(kThreads), 0, st, in, nch, h, w, ntx,
+                               nty, wt, scale, bias, Z, out);
+        return;
+    }
     const Tile t = make_tile(h, w, K, false);
     const uint32_t grid = (uint32_t)((P + t.NPB - 1) / t.NPB) * (uint32_t)(t.ntx * t.nty);
     const size_t lds = tile_lds_floats(t, K, false) * sizeof(float);
@@ -389,8 +585,10 @@ void launch_conv(bool rot, const TI* in, int P, int nch, int h, int w, const flo
 
 }  // namespace
 
-int unfused_corr_blocks(int nb, int nch) {
-    return std::max(1, std::min(nb, (kCorrTarget + nch - 1) / nch));
+int unfused_corr_blocks(int nb, int nch, int h, int w) {
+    // large planes: units are (batch entry, tile) pairs
+    const int units = big_planes(h, w) ? nb * ((h + kBigTile - 1) / kBigTile) * ((w + kBigTile - 1) / kBigTile) : nb;
+    return std::max(1, std::min(units, (kCorrTarget + nch - 1) / nch));
 }
 
 namespace {
@@ -399,11 +597,17 @@ namespace {
 template <int K, typename TA, typename TX>
 void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const float* wt, const float* scale,
                  float* dw, float* ds, float* db, float* part, hipStream_t st) {
-    const int nblk = unfused_corr_blocks(nb, nch);
-    const Tile t = make_tile(h, w, K, true);
-    const size_t lds = tile_lds_floats(t, K, true) * sizeof(float);
-    hipLaunchKernelGGL((k_tcorr<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, nblk,
-                       part);
+    const int nblk = unfused_corr_blocks(nb, nch, h, w);
+    if (big_planes(h, w)) {
+        const int ntx = (w + kBigTile - 1) / kBigTile, nty = (h + kBigTile - 1) / kBigTile;
+        hipLaunchKernelGGL((k_tcorr_big<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), 0, st, A, X, nb, nch, h, w,
+                           ntx, nty, nblk, part);
+    } else {
+        const Tile t = make_tile(h, w, K, true);
+        const size_t lds = tile_lds_floats(t, K, true) * sizeof(float);
+        hipLaunchKernelGGL((k_tcorr<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, nblk,
+                           part);
+    }
     hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, K, wt, scale, dw,
                        ds, db);
 }
@@ -516,8 +720,9 @@ int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p) {
     p->part_off = off;
     if (bwd) {
         const int kk1 = d->k * d->k + 1;
-        size_t np = (size_t)unfused_corr_blocks(d->B, d->C) * d->C * kk1;
-        if (d->L > 0) np = std::max(np, (size_t)unfused_corr_blocks(d->B, 4 * d->C) * 4 * d->C * kk1);
+        size_t np = (size_t)unfused_corr_blocks(d->B, d->C, d->H, d->W) * d->C * kk1;
+        for (int i = 1; i <= d->L; ++i)
+            np = std::max(np, (size_t)unfused_corr_blocks(d->B, 4 * d->C, p->h[i], p->w[i]) * 4 * d->C * kk1);
         off += align256_host(np * sizeof(float));
     }
     p->total = off;

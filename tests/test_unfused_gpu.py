@@ -24,6 +24,13 @@ CASES = [
     (1, 2, 9, 17, 2, 7, 109, "fp32"),      # k = 7
     (2, 4, 24, 24, 2, 1, 110, "fp32"),     # k = 1
     (1, 1, 200, 72, 2, 5, 111, "fp32"),    # larger than the fused path's LDS plane limit in one side
+    # planes with both sides >= 48 take the 64 x 64 tiled stencil kernels
+    # (level 0 here, and level 1 too for the 100-wide one): every kernel size,
+    # ragged tiles, bf16 storage
+    (1, 2, 96, 100, 1, 7, 112, "fp32"),
+    (1, 2, 70, 66, 1, 1, 113, "fp32"),
+    (2, 2, 80, 72, 2, 3, 114, "bf16"),
+    (1, 3, 130, 97, 2, 5, 115, "fp32"),
 ]
 
 
