@@ -33,6 +33,20 @@ __device__ __forceinline__ float ldv(const uint16_t* p, uint32_t i) {
     return __uint_as_float(((uint32_t)p[i]) << 16);
 }
 __device__ __forceinline__ void stv(float* p, uint32_t i, float v) { p[i] = v; }
+// four consecutive values at a 4-element aligned index
+__device__ __forceinline__ void st4(float* p, uint32_t i, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t bf16_bits(float v) {
+    // round to nearest even (finite values)
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ void st4(uint16_t* p, uint32_t i, const float (&v)[4]) {
+    *reinterpret_cast<uint2*>(p + i) = make_uint2(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
+                                                  bf16_bits(v[2]) | (bf16_bits(v[3]) << 16));
+}
 __device__ __forceinline__ void stv(uint16_t* p, uint32_t i, float v) {
     // round to nearest even (finite values)
     uint32_t u = __float_as_uint(v);
@@ -500,18 +514,31 @@ __global__ void __launch_bounds__(kThreads) k_tconv_big(const TI* __restrict__ i
                 for (int ox = 0; ox < 4; ++ox) acc[oy][ox] = fmaf(wk[ky * K + kx], row[ox + kx], acc[oy][ox]);
         }
     }
+    const int x0 = tx0 + 4 * qx;
+    // whole 4-pixel rows as one 16-byte (8-byte for bf16) access where aligned
+    const bool vec = (w & 3) == 0 && x0 + 4 <= w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int y = ty0 + 4 * qy + i;
         if (y >= h) continue;
+        const uint32_t o = pbase + (uint32_t)(y * w + x0);
+        float v[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int x = tx0 + 4 * qx + j;
-            if (x >= w) continue;
-            const uint32_t o = pbase + (uint32_t)(y * w + x);
-            float v = fmaf(sc, acc[i][j], bi);
-            if (Z) v += Z[o];
-            stv(out, o, v);
+        for (int j = 0; j < 4; ++j) v[j] = fmaf(sc, acc[i][j], bi);
+        if (vec) {
+            if (Z) {
+                const float4 z = *reinterpret_cast<const float4*>(Z + o);
+                v[0] += z.x; v[1] += z.y; v[2] += z.z; v[3] += z.w;
+            }
+            st4(out, o, v);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (x0 + j >= w) continue;
+                float u = v[j];
+                if (Z) u += Z[o + j];
+                stv(out, o + j, u);
+            }
         }
     }
 }
