@@ -246,6 +246,12 @@ struct UnfusedPlan {
 
 // workgroups per channel of the baseline's weight-gradient correlation
 int unfused_corr_blocks(int nb, int nch, int h, int w);
+
+// Peeled planes: the top level (level 1 and the base conv, fused over 64 x 64
+// tiles) and the normalised level-1 LL band feeding the sub-problem.
+int top_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
+                const float* wl, const float* sl, const float* zext, void* out, void* stream);
+int top_ll(const wtc_desc* d, const void* x, float* ll, void* stream);
 int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p);
 // stage 0: the whole pipeline; 1: only the analysis cascades (into the
 // workspace); 2: everything after them, with `zext` (may be null) added to the

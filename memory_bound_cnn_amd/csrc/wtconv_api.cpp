@@ -292,16 +292,15 @@ int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float
     st = peel_plan(d, false, depth, &pp);
     if (st != WTC_OK) return st;
     if (pp.total > 0 && (!ws || wsb < pp.total)) return WTC_EWORKSPACE;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    st = unfused_forward(&pp.d1, pp.u, x, w0, s0, b0, wl, sl, out, ws, stream, 1, nullptr);
-    if (st != WTC_OK) return st;
+    // L = 0: the plain depthwise conv
+    if (d->L == 0) return unfused_forward(&pp.d1, pp.u, x, w0, s0, b0, wl, sl, out, ws, stream, 0, nullptr);
     const float* zext = nullptr;
     if (d->L >= 2) {
         float* ll = reinterpret_cast<float*>(ws + pp.a_off);
         float* z2 = reinterpret_cast<float*>(ws + pp.b_off);
         float* zero = reinterpret_cast<float*>(ws + pp.par_off);
         const size_t lvl = (size_t)4 * d->C * d->k * d->k;
-        if ((st = copy_ll(ll, reinterpret_cast<const float*>(ws + pp.u.s_off[1]), pp, hs)) != WTC_OK) return st;
+        if ((st = top_ll(d, x, ll, stream)) != WTC_OK) return st;
         if (launch_fill_zero(zero, 2 * d->C, stream) != 0) return WTC_EHIP;
         // Z_2 = WTConv of LL_1 with levels 2..L; scale and bias 0 remove its base conv
         st = fused_fwd_run(&pp.sub, ll, w0, zero, zero + d->C, wl + lvl, sl + 4 * d->C, z2, ws + pp.sub_off,
@@ -309,7 +308,8 @@ int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float
         if (st != WTC_OK) return st;
         zext = z2;
     }
-    return unfused_forward(&pp.d1, pp.u, x, w0, s0, b0, wl, sl, out, ws, stream, 2, zext);
+    // level 1 and the base conv, fused over tiles
+    return top_forward(d, x, w0, s0, b0, wl, sl, zext, out, stream);
 }
 
 int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
