@@ -252,6 +252,16 @@ int unfused_corr_blocks(int nb, int nch, int h, int w);
 int top_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
                 const float* wl, const float* sl, const float* zext, void* out, void* stream);
 int top_ll(const wtc_desc* d, const void* x, float* ll, void* stream);
+// Backward of the top level: dx, and per (batch entry, tile) partial
+// correlation records of the base (part0: [B ntile][C][k^2 + 1], slot k^2 = sum g)
+// and of level 1 (part1: [B ntile][4C][k^2 + 1]); top_records() floats of each.
+size_t top_records(const wtc_desc* d);
+int top_backward(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0, const float* wl,
+                 const float* sl, const float* dll, void* dx, float* part0, float* part1, void* stream);
+// Chain rule of one level from correlation partials [nblk][nch][k^2 + 1]:
+// dw = scale C, ds = sum W C, db = slot k^2 (if db)
+int launch_corr_finalize(const float* part, int nch, int nblk, int k, const float* wt, const float* scale, float* dw,
+                         float* ds, float* db, void* stream);
 int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p);
 // stage 0: the whole pipeline; 1: only the analysis cascades (into the
 // workspace); 2: everything after them, with `zext` (may be null) added to the

@@ -265,13 +265,6 @@ size_t fused_bwd_ws(const wtc_desc* d, int depth, int* st) {
     return *st == WTC_OK ? pp.total : 0;
 }
 
-// LL band (band 0) of level-1 bands [B*C][4][h1*w1] -> contiguous [B*C][h1*w1]
-int copy_ll(float* dst, const float* bands, const PeelPlan& pp, hipStream_t st) {
-    const size_t plane = pp.n1 / ((size_t)pp.sub.B * pp.sub.C) * sizeof(float);
-    return hipMemcpy2DAsync(dst, plane, bands, 4 * plane, plane, (size_t)pp.sub.B * pp.sub.C,
-                            hipMemcpyDeviceToDevice, st) == hipSuccess ? WTC_OK : WTC_EHIP;
-}
-
 int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
                   const float* wl, const float* sl, void* out, char* ws, size_t wsb, void* stream, int depth) {
     FusedPlan p;
@@ -343,9 +336,10 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
     st = peel_plan(d, true, depth, &pp);
     if (st != WTC_OK) return st;
     if (!ws || wsb < pp.total) return WTC_EWORKSPACE;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    st = unfused_backward(&pp.d1, pp.u, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream, 1, nullptr);
-    if (st != WTC_OK) return st;
+    // L = 0: the plain depthwise conv and its correlation
+    if (d->L == 0)
+        return unfused_backward(&pp.d1, pp.u, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream, 0,
+                                nullptr);
     const float* zext = nullptr;
     if (d->L >= 2) {
         float* xll = reinterpret_cast<float*>(ws + pp.a_off);
@@ -355,8 +349,8 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
         float* scratch = zero + 2 * d->C;   // the sub-problem's base gradients (unused)
         const int KK = d->k * d->k;
         const size_t lvl = (size_t)4 * d->C * KK;
-        if ((st = copy_ll(xll, reinterpret_cast<const float*>(ws + pp.u.s_off[1]), pp, hs)) != WTC_OK) return st;
-        if ((st = copy_ll(gll, reinterpret_cast<const float*>(ws + pp.u.dt_off[1]), pp, hs)) != WTC_OK) return st;
+        if ((st = top_ll(d, x, xll, stream)) != WTC_OK) return st;
+        if ((st = top_ll(d, g, gll, stream)) != WTC_OK) return st;
         if (launch_fill_zero(zero, 2 * d->C, stream) != 0) return WTC_EHIP;
         // levels 2..L: the backward of WTConv(LL_1) with upstream gradient LL_1(g)
         // (the level-1 synthesis adjoint); scale 0 removes its base conv from dLL_1
@@ -366,7 +360,17 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
         if (st != WTC_OK) return st;
         zext = dll;
     }
-    return unfused_backward(&pp.d1, pp.u, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, stream, 2, zext);
+    // level 1 and the base conv fused over tiles; the tiles' correlation
+    // records go where the level-by-level intermediates would (unused here)
+    const size_t nrec = top_records(d);
+    const size_t rec1_off = al256(nrec * sizeof(float));
+    if (rec1_off + 4 * nrec * sizeof(float) > pp.u.total) return WTC_EWORKSPACE;
+    float* part0 = reinterpret_cast<float*>(ws);
+    float* part1 = reinterpret_cast<float*>(ws + rec1_off);
+    if ((st = top_backward(d, x, g, w0, s0, wl, sl, zext, dx, part0, part1, stream)) != WTC_OK) return st;
+    const int nblk = (int)(nrec / ((size_t)d->C * (d->k * d->k + 1)));
+    if ((st = launch_corr_finalize(part0, d->C, nblk, d->k, w0, s0, dw0, ds0, db0, stream)) != WTC_OK) return st;
+    return launch_corr_finalize(part1, 4 * d->C, nblk, d->k, wl, sl, dwl, dsl, nullptr, stream);
 }
 
 int unf_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,

@@ -1,4 +1,4 @@
-// Top level of a peeled plane (planes beyond the on-chip pipeline), forward.
+// Top level of a peeled plane (planes beyond the on-chip pipeline).
 //
 // The levels >= 2 of WTConv are WTConv itself applied to the level-1 LL band,
 // so a large plane runs its deeper levels as a sub-problem on that band and
@@ -81,6 +81,47 @@ __device__ __forceinline__ void tstencil(const float* win, int S, const float (&
                 for (int ox = 0; ox < 4; ++ox) acc[oy][ox] = fmaf(w[ky * K + kx], row[ox + kx], acc[oy][ox]);
         }
     }
+}
+
+// tstencil plus the correlation of the window with a 4 x 4 block xv:
+//   corr[ky K + kx] += xv[oy][ox] win[oy + ky][ox + kx]
+template <int K>
+__device__ __forceinline__ void tstencil_corr(const float* win, int S, const float (&w)[K * K], float (&acc)[4][4],
+                                              const float (&xv)[4][4], float (&corr)[K * K]) {
+    constexpr int R = K / 2, WW = 4 + 2 * R, WH = 4 + 2 * R;
+    float rows[2][WW];
+    trow<WW>(win, rows[0]);
+#pragma unroll
+    for (int wy = 0; wy < WH; ++wy) {
+        float (&row)[WW] = rows[wy & 1];
+        if (wy + 1 < WH) trow<WW>(win + (wy + 1) * S, rows[(wy + 1) & 1]);
+#pragma unroll
+        for (int oy = 0; oy < 4; ++oy) {
+            const int ky = wy - oy;
+            if (ky < 0 || ky >= K) continue;
+#pragma unroll
+            for (int kx = 0; kx < K; ++kx)
+#pragma unroll
+                for (int ox = 0; ox < 4; ++ox) {
+                    acc[oy][ox] = fmaf(w[ky * K + kx], row[ox + kx], acc[oy][ox]);
+                    corr[ky * K + kx] = fmaf(xv[oy][ox], row[ox + kx], corr[ky * K + kx]);
+                }
+        }
+    }
+}
+
+// Value of v in lane l - N of the same 16-lane row (0 for the row's first N
+// lanes): DPP row shift.
+template <int N>
+__device__ __forceinline__ float trow_shr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 | N, 0xF, 0xF, true));
+}
+// Lane 15 of every 16-lane row: the sum of v over the row.
+__device__ __forceinline__ float trow_sum(float v) {
+    v += trow_shr<1>(v);
+    v += trow_shr<2>(v);
+    v += trow_shr<4>(v);
+    return v + trow_shr<8>(v);
 }
 
 // Geometry of the staged x tile and of the level-1 band tile (compile time).
@@ -244,6 +285,227 @@ __global__ void __launch_bounds__(kTopThreads) k_top_fwd(const T* __restrict__ x
     }
 }
 
+// Backward of the top level over one 64 x 64 tile of plane p = b C + c:
+//   dx = s0 (rot W0 * g) + synthesis(dS1),  dS1_u = s1_u (rot W1_u * G1_u) (+ dLL, band 0)
+// with G1 = level-1 analysis of g (recomputed from the staged g tile), and the
+// tile's correlations C0[d] = sum g[p] x[p + d], sum g, C1_u[d] = sum G1_u[j] X1_u[j + d]
+// (X1 from this thread's own 4 x 4 block of x, which is exactly its 2 x 2
+// level-1 positions).  Each window of g (G1) serves the rotated conv and the
+// correlation with the x (X1) block, which yields C[-d]: stored un-rotated.
+// Records: part0[(b ntile + tile) C + c][k^2 + 1] (slot k^2: sum g), part1[(b
+// ntile + tile) 4C + 4c + u][k^2 + 1] (slot k^2: 0), for the per-level finalize.
+template <int K, typename T>
+__global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x, const T* __restrict__ g, int C,
+                                                         int H, int W, int ntx, int nty, const float* __restrict__ w0,
+                                                         const float* __restrict__ s0, const float* __restrict__ wl,
+                                                         const float* __restrict__ sl, const float* __restrict__ dll,
+                                                         T* __restrict__ dx, float* __restrict__ part0,
+                                                         float* __restrict__ part1) {
+    using G = TopGeom<K>;
+    constexpr int R = G::R, KK = K * K;
+    __shared__ __align__(16) float gs[G::XN];       // g tile; then X1; then the level-1 results
+    __shared__ __align__(16) float bs[4 * G::BSZ];  // the four level-1 bands of g; then the reductions
+    const int ntile = ntx * nty;
+    const int p = blockIdx.x / ntile, tile = blockIdx.x - p * ntile;
+    const int ty0 = (tile / ntx) * kTop, tx0 = (tile % ntx) * kTop;
+    const int c = p % C, bb = p / C;
+    const int h1 = (H + 1) >> 1, w1 = (W + 1) >> 1;
+    const uint32_t hw = (uint32_t)H * W;
+    const T* gp = g + (size_t)p * hw;
+    const T* xp = x + (size_t)p * hw;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int qy = tid >> 4, qx = tid & 15;
+    const int x0 = tx0 + 4 * qx;
+
+    // ---- stage the g tile (as the forward's x tile); this thread's 4 x 4 block
+    // of x and the sub-problem's gradient at its 2 x 2 level-1 positions into
+    // registers; every load issued before any use
+    float xb[4][4], zq[2][2];
+    {
+        constexpr int NW = kTopThreads / 64, RPW = (G::XR + NW - 1) / NW, CPL = (G::XS + 63) / 64;
+        float v[RPW][CPL];
+#pragma unroll
+        for (int k = 0; k < RPW; ++k)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int r = wave + k * NW, col = lane + cc * 64;
+                const int y = ty0 - 2 * R + r, xg = tx0 - G::CO + col;
+                v[k][cc] = (r < G::XR && col < G::XS && y >= 0 && y < H && xg >= 0 && xg < W)
+                               ? tld(gp, (uint32_t)(y * W + xg)) : 0.f;
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int y = ty0 + 4 * qy + i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                xb[i][j] = (y < H && x0 + j < W) ? tld(xp, (uint32_t)(y * W + x0 + j)) : 0.f;
+        }
+        const float* zp = dll ? dll + (size_t)p * h1 * w1 : nullptr;
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+            for (int b2 = 0; b2 < 2; ++b2) {
+                const int gy = (ty0 >> 1) + 2 * qy + a2, gx = (tx0 >> 1) + 2 * qx + b2;
+                zq[a2][b2] = (zp && gy < h1 && gx < w1) ? zp[gy * w1 + gx] : 0.f;
+            }
+#pragma unroll
+        for (int k = 0; k < RPW; ++k)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const int r = wave + k * NW, col = lane + cc * 64;
+                if (r < G::XR && col < G::XS) gs[r * G::XS + col] = v[k][cc];
+            }
+    }
+    __syncthreads();
+
+    // ---- base: rotated conv of g, correlation of g with the x block, sum of g
+    float acc[4][4], corr0[KK], sumg = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+#pragma unroll
+    for (int q = 0; q < KK; ++q) corr0[q] = 0.f;
+    {
+        float w[KK];
+#pragma unroll
+        for (int t = 0; t < KK; ++t) w[t] = w0[c * KK + (KK - 1 - t)];
+        tstencil_corr<K>(gs + (4 * qy + R) * G::XS + (4 * qx + G::CO - R), G::XS, w, acc, xb, corr0);
+        const float* gc = gs + (4 * qy + 2 * R) * G::XS + (4 * qx + G::CO);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float r4[4];
+            trow<4>(gc + i * G::XS, r4);
+            sumg += (r4[0] + r4[1]) + (r4[2] + r4[3]);
+        }
+    }
+    // ---- level-1 bands of g (positions -R .. 32 + R) into LDS
+    for (int e = tid; e < G::BR * G::BR; e += kTopThreads) {
+        const int jy = e / G::BR, jx = e - jy * G::BR;
+        const float* q = gs + (2 * jy) * G::XS + (G::CO - 2 * R + 2 * jx);
+        const float a = q[0], b = q[1], cc = q[G::XS], d = q[G::XS + 1];
+        const float s01 = a + b, d01 = a - b, s23 = cc + d, d23 = cc - d;
+        float* o = bs + jy * G::BS + jx;
+        o[0] = 0.5f * (s01 + s23);
+        o[G::BSZ] = 0.5f * (d01 + d23);
+        o[2 * G::BSZ] = 0.5f * (s01 - s23);
+        o[3 * G::BSZ] = 0.5f * (d01 - d23);
+    }
+    __syncthreads();   // g tile no longer read
+
+    // ---- X1 of this thread's block (its 2 x 2 level-1 positions) over the g tile
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            const float a = xb[2 * a2][2 * b2], b = xb[2 * a2][2 * b2 + 1];
+            const float cc = xb[2 * a2 + 1][2 * b2], d = xb[2 * a2 + 1][2 * b2 + 1];
+            const float s01 = a + b, d01 = a - b, s23 = cc + d, d23 = cc - d;
+            float* o = gs + (2 * qy + a2) * G::YS + 2 * qx + b2;
+            o[0] = 0.5f * (s01 + s23);
+            o[G::YSZ] = 0.5f * (d01 + d23);
+            o[2 * G::YSZ] = 0.5f * (s01 - s23);
+            o[3 * G::YSZ] = 0.5f * (d01 - d23);
+        }
+    __syncthreads();
+
+    // ---- level 1: wave u takes band u, lane l the 4 x 4 block (l / 8, l % 8)
+    float y1[4][4], corr1[KK];
+    const int u = wave, by = lane >> 3, bx = lane & 7;
+    const size_t pu = (size_t)c * 4 + u;
+    const float su = sl[pu];
+    {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y1[i][j] = 0.f;
+#pragma unroll
+        for (int q = 0; q < KK; ++q) corr1[q] = 0.f;
+        float w[KK];
+#pragma unroll
+        for (int t = 0; t < KK; ++t) w[t] = wl[pu * KK + (KK - 1 - t)];
+        float xv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) trow<4>(gs + u * G::YSZ + (4 * by + i) * G::YS + 4 * bx, xv[i]);
+        tstencil_corr<K>(bs + u * G::BSZ + (4 * by) * G::BS + 4 * bx, G::BS, w, y1, xv, corr1);
+    }
+    __syncthreads();   // X1 and G1 no longer read
+    {
+        float* yo = gs + u * G::YSZ + (4 * by) * G::YS + 4 * bx;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<tf4*>(yo + i * G::YS) = tf4{su * y1[i][0], su * y1[i][1], su * y1[i][2], su * y1[i][3]};
+    }
+    // ---- reductions: DPP row sums, one partial per 16-lane row in LDS (over the bands)
+    const int row = tid >> 4;   // 16 rows of 16 lanes
+    float* r0 = bs;                       // [16][KK + 1]
+    float* r1 = bs + 16 * (KK + 1);       // [16][KK]: rows 4u .. 4u + 3 belong to band u
+#pragma unroll
+    for (int q = 0; q < KK; ++q) {
+        corr0[q] = trow_sum(corr0[q]);
+        corr1[q] = trow_sum(corr1[q]);
+    }
+    sumg = trow_sum(sumg);
+    if ((lane & 15) == 15) {
+#pragma unroll
+        for (int q = 0; q < KK; ++q) {
+            r0[row * (KK + 1) + q] = corr0[q];
+            r1[row * KK + q] = corr1[q];
+        }
+        r0[row * (KK + 1) + KK] = sumg;
+    }
+    __syncthreads();
+
+    // ---- level-1 synthesis (+ the sub-problem's gradient on the LL band) and dx
+    const float sc = s0[c];
+    float o[4][4];
+#pragma unroll
+    for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+            const float* yp = gs + (2 * qy + a2) * G::YS + 2 * qx + b2;
+            const float t0 = yp[0] + zq[a2][b2];
+            const float t1 = yp[G::YSZ], t2 = yp[2 * G::YSZ], t3 = yp[3 * G::YSZ];
+            const float pa = t0 + t1, pb = t0 - t1, pc = t2 + t3, pd = t2 - t3;
+            o[2 * a2][2 * b2] = fmaf(sc, acc[2 * a2][2 * b2], 0.5f * (pa + pc));
+            o[2 * a2][2 * b2 + 1] = fmaf(sc, acc[2 * a2][2 * b2 + 1], 0.5f * (pb + pd));
+            o[2 * a2 + 1][2 * b2] = fmaf(sc, acc[2 * a2 + 1][2 * b2], 0.5f * (pa - pc));
+            o[2 * a2 + 1][2 * b2 + 1] = fmaf(sc, acc[2 * a2 + 1][2 * b2 + 1], 0.5f * (pb - pd));
+        }
+    const bool vec = (W & 3) == 0 && x0 + 4 <= W;
+    T* op = dx + (size_t)p * hw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int y = ty0 + 4 * qy + i;
+        if (y >= H) continue;
+        if (vec) {
+            tst4(op, (uint32_t)(y * W + x0), o[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (x0 + j < W) tst(op, (uint32_t)(y * W + x0 + j), o[i][j]);
+        }
+    }
+    // ---- the tile's records (fixed summation order)
+    const size_t blk = (size_t)bb * ntile + tile;
+    for (int e = tid; e < (KK + 1) + 4 * (KK + 1); e += kTopThreads) {
+        if (e < KK + 1) {
+            float v = 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) v += r0[rr * (KK + 1) + (e < KK ? KK - 1 - e : KK)];
+            part0[(blk * C + c) * (KK + 1) + e] = v;
+        } else {
+            const int f = e - (KK + 1), ub = f / (KK + 1), d = f - ub * (KK + 1);
+            float v = 0.f;
+            if (d < KK) {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) v += r1[(4 * ub + rr) * KK + (KK - 1 - d)];
+            }
+            part1[(blk * 4 * C + (size_t)c * 4 + ub) * (KK + 1) + d] = v;
+        }
+    }
+}
+
 // Normalised LL band of level 1 (the sub-problem's input), one thread per
 // level-1 position: ll[p][j] = (a + b + c + d) / 2 of the 2 x 2 block (zero
 // beyond the plane).
@@ -287,7 +549,42 @@ int top_fwd_t(const wtc_desc* d, const void* x, const float* w0, const float* s0
     }
 }
 
+template <int K, typename T>
+int top_bwd_k(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0, const float* wl,
+              const float* sl, const float* dll, void* dx, float* part0, float* part1, hipStream_t st) {
+    const int ntx = (d->W + kTop - 1) / kTop, nty = (d->H + kTop - 1) / kTop;
+    const uint32_t grid = (uint32_t)d->B * d->C * ntx * nty;
+    hipLaunchKernelGGL((k_top_bwd<K, T>), dim3(grid), dim3(kTopThreads), 0, st, reinterpret_cast<const T*>(x),
+                       reinterpret_cast<const T*>(g), d->C, d->H, d->W, ntx, nty, w0, s0, wl, sl, dll,
+                       reinterpret_cast<T*>(dx), part0, part1);
+    return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
+}
+
+template <typename T>
+int top_bwd_t(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0, const float* wl,
+              const float* sl, const float* dll, void* dx, float* part0, float* part1, hipStream_t st) {
+    switch (d->k) {
+        case 1: return top_bwd_k<1, T>(d, x, g, w0, s0, wl, sl, dll, dx, part0, part1, st);
+        case 3: return top_bwd_k<3, T>(d, x, g, w0, s0, wl, sl, dll, dx, part0, part1, st);
+        case 5: return top_bwd_k<5, T>(d, x, g, w0, s0, wl, sl, dll, dx, part0, part1, st);
+        case 7: return top_bwd_k<7, T>(d, x, g, w0, s0, wl, sl, dll, dx, part0, part1, st);
+        default: return WTC_ESHAPE;
+    }
+}
+
 }  // namespace
+
+size_t top_records(const wtc_desc* d) {
+    const size_t ntile = (size_t)((d->W + kTop - 1) / kTop) * ((d->H + kTop - 1) / kTop);
+    return (size_t)d->B * ntile * d->C * (d->k * d->k + 1);
+}
+
+int top_backward(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0, const float* wl,
+                 const float* sl, const float* dll, void* dx, float* part0, float* part1, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return d->dtype == WTC_BF16 ? top_bwd_t<uint16_t>(d, x, g, w0, s0, wl, sl, dll, dx, part0, part1, st)
+                                : top_bwd_t<float>(d, x, g, w0, s0, wl, sl, dll, dx, part0, part1, st);
+}
 
 int top_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
                 const float* wl, const float* sl, const float* zext, void* out, void* stream) {

@@ -612,6 +612,13 @@ void launch_conv(bool rot, const TI* in, int P, int nch, int h, int w, const flo
 
 }  // namespace
 
+int launch_corr_finalize(const float* part, int nch, int nblk, int k, const float* wt, const float* scale, float* dw,
+                         float* ds, float* db, void* stream) {
+    hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), part, nch,
+                       nblk, k, wt, scale, dw, ds, db);
+    return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
+}
+
 int unfused_corr_blocks(int nb, int nch, int h, int w) {
     // large planes: units are (batch entry, tile) pairs
     const int units = big_planes(h, w) ? nb * ((h + kBigTile - 1) / kBigTile) * ((w + kBigTile - 1) / kBigTile) : nb;
