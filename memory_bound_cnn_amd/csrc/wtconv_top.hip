@@ -26,6 +26,16 @@ constexpr int kTopThreads = 256;
 
 __device__ __forceinline__ float tld(const float* p, uint32_t i) { return p[i]; }
 __device__ __forceinline__ float tld(const uint16_t* p, uint32_t i) { return __uint_as_float(((uint32_t)p[i]) << 16); }
+// four consecutive values at a 4-element aligned index
+__device__ __forceinline__ void tld4(const float* p, uint32_t i, float (&v)[4]) {
+    const float4 q = *reinterpret_cast<const float4*>(p + i);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void tld4(const uint16_t* p, uint32_t i, float (&v)[4]) {
+    const uint2 q = *reinterpret_cast<const uint2*>(p + i);
+    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
+    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
+}
 __device__ __forceinline__ uint32_t tbf16(float v) {
     // round to nearest even (finite values)
     uint32_t u = __float_as_uint(v);
@@ -295,7 +305,7 @@ __global__ void __launch_bounds__(kTopThreads) k_top_fwd(const T* __restrict__ x
 // Records: part0[(b ntile + tile) C + c][k^2 + 1] (slot k^2: sum g), part1[(b
 // ntile + tile) 4C + 4c + u][k^2 + 1] (slot k^2: 0), for the per-level finalize.
 template <int K, typename T>
-__global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x, const T* __restrict__ g, int C,
+__global__ void __launch_bounds__(kTopThreads) __attribute__((amdgpu_waves_per_eu(K <= 5 ? 3 : 2))) k_top_bwd(const T* __restrict__ x, const T* __restrict__ g, int C,
                                                          int H, int W, int ntx, int nty, const float* __restrict__ w0,
                                                          const float* __restrict__ s0, const float* __restrict__ wl,
                                                          const float* __restrict__ sl, const float* __restrict__ dll,
@@ -304,7 +314,8 @@ __global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x
     using G = TopGeom<K>;
     constexpr int R = G::R, KK = K * K;
     __shared__ __align__(16) float gs[G::XN];       // g tile; then X1; then the level-1 results
-    __shared__ __align__(16) float bs[4 * G::BSZ];  // the four level-1 bands of g; then the reductions
+    __shared__ __align__(16) float bs[4 * G::BSZ];  // the four level-1 bands of g; then level-1 partials
+    __shared__ float r0[16][KK + 1];                 // base correlation partials, one per 16-lane row
     const int ntile = ntx * nty;
     const int p = blockIdx.x / ntile, tile = blockIdx.x - p * ntile;
     const int ty0 = (tile / ntx) * kTop, tx0 = (tile % ntx) * kTop;
@@ -333,12 +344,18 @@ __global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x
                 v[k][cc] = (r < G::XR && col < G::XS && y >= 0 && y < H && xg >= 0 && xg < W)
                                ? tld(gp, (uint32_t)(y * W + xg)) : 0.f;
             }
+        const bool xvec = (W & 3) == 0 && x0 + 4 <= W;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int y = ty0 + 4 * qy + i;
+            if (xvec) {
+                tld4(xp, (uint32_t)(min(y, H - 1) * W + x0), xb[i]);
+                if (y >= H) xb[i][0] = xb[i][1] = xb[i][2] = xb[i][3] = 0.f;
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                xb[i][j] = (y < H && x0 + j < W) ? tld(xp, (uint32_t)(y * W + x0 + j)) : 0.f;
+                for (int j = 0; j < 4; ++j)
+                    xb[i][j] = (y < H && x0 + j < W) ? tld(xp, (uint32_t)(y * W + x0 + j)) : 0.f;
+            }
         }
         const float* zp = dll ? dll + (size_t)p * h1 * w1 : nullptr;
 #pragma unroll
@@ -378,6 +395,16 @@ __global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x
             trow<4>(gc + i * G::XS, r4);
             sumg += (r4[0] + r4[1]) + (r4[2] + r4[3]);
         }
+    }
+    // base correlation: DPP row sums now (its accumulators are then free)
+    const int row = tid >> 4;   // 16 rows of 16 lanes
+#pragma unroll
+    for (int q = 0; q < KK; ++q) corr0[q] = trow_sum(corr0[q]);
+    sumg = trow_sum(sumg);
+    if ((lane & 15) == 15) {
+#pragma unroll
+        for (int q = 0; q < KK; ++q) r0[row][q] = corr0[q];
+        r0[row][KK] = sumg;
     }
     // ---- level-1 bands of g (positions -R .. 32 + R) into LDS
     for (int e = tid; e < G::BR * G::BR; e += kTopThreads) {
@@ -436,23 +463,13 @@ __global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<tf4*>(yo + i * G::YS) = tf4{su * y1[i][0], su * y1[i][1], su * y1[i][2], su * y1[i][3]};
     }
-    // ---- reductions: DPP row sums, one partial per 16-lane row in LDS (over the bands)
-    const int row = tid >> 4;   // 16 rows of 16 lanes
-    float* r0 = bs;                       // [16][KK + 1]
-    float* r1 = bs + 16 * (KK + 1);       // [16][KK]: rows 4u .. 4u + 3 belong to band u
+    // ---- level-1 correlation: DPP row sums, one partial per 16-lane row (over the bands)
+    float* r1 = bs;   // [16][KK]: rows 4u .. 4u + 3 belong to band u
 #pragma unroll
-    for (int q = 0; q < KK; ++q) {
-        corr0[q] = trow_sum(corr0[q]);
-        corr1[q] = trow_sum(corr1[q]);
-    }
-    sumg = trow_sum(sumg);
+    for (int q = 0; q < KK; ++q) corr1[q] = trow_sum(corr1[q]);
     if ((lane & 15) == 15) {
 #pragma unroll
-        for (int q = 0; q < KK; ++q) {
-            r0[row * (KK + 1) + q] = corr0[q];
-            r1[row * KK + q] = corr1[q];
-        }
-        r0[row * (KK + 1) + KK] = sumg;
+        for (int q = 0; q < KK; ++q) r1[row * KK + q] = corr1[q];
     }
     __syncthreads();
 
@@ -492,7 +509,7 @@ __global__ void __launch_bounds__(kTopThreads) k_top_bwd(const T* __restrict__ x
         if (e < KK + 1) {
             float v = 0.f;
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) v += r0[rr * (KK + 1) + (e < KK ? KK - 1 - e : KK)];
+            for (int rr = 0; rr < 16; ++rr) v += r0[rr][e < KK ? KK - 1 - e : KK];
             part0[(blk * C + c) * (KK + 1) + e] = v;
         } else {
             const int f = e - (KK + 1), ub = f / (KK + 1), d = f - ub * (KK + 1);
