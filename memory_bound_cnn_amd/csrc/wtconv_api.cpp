@@ -515,17 +515,22 @@ double io_fused(const wtc_desc* d, int dir, int depth) {
         // read x and g, write dx; params read; partials written then read; grads written
         return 3.0 * N * e + params + 2.0 * partials + params;
     }
-    // peeled plane: level 1 and the base level by level, the LL band recursively
+    // peeled plane: the LL band recursively, level 1 and the base fused over tiles
     PeelPlan pp;
     if (st != WTC_ESHAPE || peel_plan(d, dir == 1, depth, &pp) != WTC_OK) return -1.0;
-    double t = io_unfused(&pp.d1, dir);
+    if (d->L == 0) return io_unfused(&pp.d1, dir);   // the plain depthwise conv
+    const double ll = 4.0 * (double)pp.n1;
+    double t = 0.0;
     if (d->L >= 2) {
-        const double ll = 4.0 * (double)pp.n1;
-        // LL copies (forward: x; backward: x and g), read and written; the deeper
-        // term read once more by the level-1 synthesis
-        t += (dir == 0 ? 2.0 : 4.0) * ll + ll + io_fused(&pp.sub, dir, depth + 1);
+        // LL bands (forward: of x; backward: of x and g): read the tensor, write the band;
+        // then the sub-problem, whose result (gradient) the tile kernel reads once
+        t += (dir == 0 ? 1.0 : 2.0) * (N * e + ll) + io_fused(&pp.sub, dir, depth + 1) + ll;
     }
-    return t;
+    if (dir == 0) return t + 2.0 * N * e + params;   // tiles: read x, write out
+    // tiles: read g and x, write dx; per-tile correlation records (base and level 1)
+    // written and read back by the two finalizes; parameters read, gradients written
+    const double recs = 4.0 * 5.0 * (double)top_records(d);
+    return t + 3.0 * N * e + 2.0 * recs + 2.0 * params;
 }
 
 }  // namespace
