@@ -76,7 +76,8 @@ typedef struct {
 /* Bytes of device workspace wtconv_forward needs (0: none).  It is 0 for every
  * plane the on-chip pipeline holds (up to about 128 x 128 with k = 5); larger
  * planes peel one wavelet level (below) and need float32 tensors of their
- * level-1 bands, LL band and deeper result.  0 is also returned for a
+ * LL band and deeper result (the size also covers the level-by-level
+ * intermediates of the peeled level).  0 is also returned for a
  * descriptor that the forward pass rejects. */
 size_t wtconv_forward_workspace(const wtc_desc* d);
 
@@ -84,9 +85,10 @@ size_t wtconv_forward_workspace(const wtc_desc* d);
  * size is 0.
  * Planes beyond the on-chip pipeline: the levels >= 2 of the operator are the
  * operator itself (one level fewer, no base conv) applied to the level-1 LL
- * band, so level 1 and the base conv run level by level (the "_unfused"
- * kernels) and the LL band (half the size per side) recursively through this
- * path -- on chip as soon as it fits.  Same results, same contract. */
+ * band, so the LL band (half the size per side) runs recursively through this
+ * path -- on chip as soon as it fits -- and level 1 and the base conv run
+ * fused over 64 x 64 tiles of the full-resolution plane (L = 0: the
+ * level-by-level depthwise conv).  Same results, same contract. */
 int wtconv_forward(const wtc_desc* d, const void* x,
                    const float* w0, const float* s0, const float* b0,
                    const float* wl, const float* sl,
