@@ -17,6 +17,7 @@ bool launch_fused_static_p32(const FusedArgs&, int, int, int, int, size_t, int, 
 bool launch_fused_static_p128a(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
 bool launch_fused_static_p128b(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
 bool launch_fused_static_small(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
+bool launch_fused_static_p112(const FusedArgs&, int, int, int, int, size_t, int, void*, int*);
 bool launch_fused_static_dw(const FusedArgs&, int, int, int, int, int, size_t, int, void*, int*);
 
 namespace {
@@ -121,6 +122,7 @@ int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nth
             launch_fused_static_p32(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
             launch_fused_static_p128a(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
             launch_fused_static_p128b(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
+            launch_fused_static_p112(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err) ||
             launch_fused_static_small(a, dtype, bwd, bpq, nthr, lds_bytes, grid, stream, &err))
             return err;
     }

@@ -36,6 +36,7 @@ REDUCED = [
     (1, 3, 128, 128, 1, 5, 30, "fp32"),    # level sweep planes
     (1, 3, 128, 128, 3, 5, 31, "fp32"),
     (1, 2, 128, 128, 5, 5, 32, "fp32"),
+    (2, 2, 112, 112, 2, 5, 33, "fp32"),    # the LL band of the 224x224 planes (peeled path)
     (5, 8, 14, 14, 2, 5, 40, "fp32"),      # odd 14x14
     (9, 8, 7, 7, 1, 5, 41, "fp32"),        # odd 7x7
 ]
