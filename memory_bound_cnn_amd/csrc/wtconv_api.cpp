@@ -96,7 +96,9 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     // per pixel of the backward, that costs more than the occupancy it buys
     // (measured on 32x32 planes: 53 us without, 67 us with overlap), so the
     // forward pass overlaps only when nothing else fits.
-    const int wts_n = round_up(KK * (1 + 4 * d->L) + 4, 4);
+    // folded level weights (one 16-byte aligned set of round_up(k^2, 4) floats
+    // per level and band), base weights, bias and scale
+    const int wts_n = round_up(round_up(KK, 4) * 4 * d->L + KK + 4, 4);
     const int per_units = a.vec ? d->H * (d->W / 4) : d->H * d->W;
     struct Cand {
         Layout lay;

@@ -255,6 +255,20 @@ __device__ __forceinline__ void load_w(const float* p, float (&w)[K * K]) {
 #pragma unroll
     for (int t = 0; t < K * K; ++t) w[t] = p[ROT ? (K * K - 1 - t) : t];
 }
+// Same from a 16-byte aligned set padded to a multiple of 4 floats: 16-byte
+// LDS reads from one base address (immediate offsets).
+template <int K, bool ROT>
+__device__ __forceinline__ void load_w4(const float* p, float (&w)[K * K]) {
+    constexpr int KK = K * K, KKP = (KK + 3) & ~3;
+    float v[KKP];
+#pragma unroll
+    for (int q = 0; q < KKP; q += 4) {
+        const lds_f4 f = *reinterpret_cast<const lds_f4*>(p + q);
+        v[q] = f.x; v[q + 1] = f.y; v[q + 2] = f.z; v[q + 3] = f.w;
+    }
+#pragma unroll
+    for (int t = 0; t < KK; ++t) w[t] = v[ROT ? (KK - 1 - t) : t];
+}
 
 // Pixel (y, x) of a plane, zero outside [0,H) x [0,W).
 template <typename ST>
@@ -448,6 +462,7 @@ template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(BWD, BPQ, G::kNoLevels))))
 wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
+    constexpr int KKP = (KK + 3) & ~3;   // LDS stride of one (level, band) weight set
     // Direct-load mode: planes are copied from device memory into their LDS slot
     // by DMA (global_load_lds), one plane ahead, with no register staging.
     constexpr bool DL = G::kDL;
@@ -741,11 +756,12 @@ wtc_fused_kernel(const FusedArgs a) {
     // vector-memory load may sit behind the next planes' prefetch in the plane
     // loop (vector-memory completions are counted in order).
     float* wts = lds + g.wts_off();
-    float* wbase = wts + 4 * a.L * KK;          // unfolded base weights W0[c]
+    // (level i, band u) at wts + (4 i + u) KKP: 16-byte aligned sets
+    float* wbase = wts + 4 * a.L * KKP;         // unfolded base weights W0[c]
     for (int e = tid; e < 4 * a.L * KK; e += nthr) {
         const int i = e / (4 * KK), rem = e - i * 4 * KK, u = rem / KK, tap = rem - u * KK;
         const float sc = ldexpf(a.sl[((size_t)i * a.C + c) * 4 + u], -2 * (i + 1));
-        wts[e] = sc * a.wl[(((size_t)i * a.C + c) * 4 + u) * KK + tap];
+        wts[(i * 4 + u) * KKP + tap] = sc * a.wl[(((size_t)i * a.C + c) * 4 + u) * KK + tap];
     }
     for (int e = tid; e < KK; e += nthr) wbase[e] = a.w0[(size_t)c * KK + e];
     if (tid == 0) {
@@ -757,7 +773,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // tail levels (1x1 grids): kappa = sum of their folded centre taps
     float kappa = 0.f;
     for (int i = Lm; i < a.L; ++i)
-        for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KK + (KK >> 1)];
+        for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KKP + (KK >> 1)];
 
     // ---- persistent backward accumulators ----
     float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm - 2][K];
@@ -884,7 +900,7 @@ wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[s][i][j] = 0.f;
             float w[KK];
-            load_w<K, BWD>(wbase, w);
+            load_w4<K, BWD>(wbase, w);
             float xo[4][4];
             if constexpr (XDL) {
                 const float* xr = S + g.xp_off() + py0 * g.xp_S() + px0;
@@ -1004,7 +1020,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 const int u = m & 3, j = m >> 2;
                 const int jy = fdiv(j, dwi), jx = j - jy * wi;
                 float w[KK];
-                load_w<K, BWD>(wts + ((i - 1) * 4 + u) * KK, w);
+                load_w4<K, BWD>(wts + ((i - 1) * 4 + u) * KKP, w);
                 const float* win = Sl + g.b_off(i) + u * bs + jy * Si + jx;
                 float accv = 0.f;
 #pragma unroll
@@ -1082,7 +1098,7 @@ wtc_fused_kernel(const FusedArgs a) {
             }
             {
                 float w[KK];
-                load_w<K, BWD>(wts + t * KK, w);
+                load_w4<K, BWD>(wts + t * KKP, w);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1092,7 +1108,7 @@ wtc_fused_kernel(const FusedArgs a) {
             }
             if (Lm >= 2) {
                 float w[KK];
-                load_w<K, BWD>(wts + (4 + t) * KK, w);
+                load_w4<K, BWD>(wts + (4 + t) * KKP, w);
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
