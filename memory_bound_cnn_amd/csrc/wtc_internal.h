@@ -224,6 +224,13 @@ int launch_finalize(const FinalizeArgs& f, void* stream);
 // one 64-lane workgroup per 16 consecutive channels and ppw batch entries
 // (grid = ceil(C / 16) x ceil(B / ppw)); backward records [chunk][channel].
 int launch_tiny(const FusedArgs& a, int dtype, int bwd, int grid, void* stream);
+// One plane per lane for 7 x 7 planes with one level (k = 5): one wave per 64
+// batch entries of a channel (grid = C * ceil(B / 64)); backward records
+// [chunk][channel] as the register-resident kernel's.
+int launch_lane(const FusedArgs& a, int dtype, int bwd, int grid, void* stream);
+constexpr bool lane_supported(int k, int H, int W, int L, int Lm) {
+    return k == 5 && H == 7 && W == 7 && L == 1 && Lm == 1;
+}
 constexpr bool tiny_supported(int k, int Hq, int Wq, int L, int Lm) {
     return k == 5 && Hq == 8 && Wq == 8 && L == Lm && Lm >= 1 && Lm <= 2;
 }

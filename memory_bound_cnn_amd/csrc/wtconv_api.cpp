@@ -42,7 +42,7 @@ struct FusedPlan {
     FusedArgs a;
     int nthr, bpq, grid, nchunk;
     size_t lds;
-    int tiny;   // register-resident kernel for planes of at most 8 x 8
+    int tiny;   // 1: register-resident kernel for planes of at most 8 x 8; 2: one plane per lane (7 x 7)
     long nrec;  // backward partial records
 };
 
@@ -64,6 +64,19 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.qpp = (a.Hq / 8) * a.nqx;
     a.vec = (d->W % 4 == 0) ? 1 : 0;
     p->tiny = 0;
+    if (lane_supported(k, d->H, d->W, d->L, a.Lm)) {
+        // one plane per lane, one wave per 64 batch entries of a channel
+        p->tiny = 2;
+        a.P = partial_len(k, a.Lm);
+        a.ppw = 64;
+        p->nchunk = (d->B + 63) / 64;
+        p->grid = d->C * p->nchunk;
+        p->nrec = (long)p->nchunk * d->C;
+        p->nthr = 64;
+        p->bpq = 1;
+        p->lds = 0;
+        return WTC_OK;
+    }
     const long esize = d->dtype == WTC_BF16 ? 2 : 4;
     if (tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm) &&
         ((long)d->B + 16) * d->C * d->H * d->W * esize < (1L << 31)) {   // 32-bit buffer offsets
@@ -278,8 +291,9 @@ int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float
         a.w0 = w0; a.s0 = s0; a.b0 = b0; a.wl = wl; a.sl = sl;
         a.dst = out;
         a.partials = nullptr;
-        const int e = p.tiny ? launch_tiny(a, d->dtype, 0, p.grid, stream)
-                             : launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
+        const int e = p.tiny == 2 ? launch_lane(a, d->dtype, 0, p.grid, stream)
+                      : p.tiny    ? launch_tiny(a, d->dtype, 0, p.grid, stream)
+                                  : launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
         return e == 0 ? WTC_OK : WTC_EHIP;
     }
     if (st != WTC_ESHAPE) return st;
@@ -321,8 +335,9 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
         a.w0 = w0; a.s0 = s0; a.b0 = nullptr; a.wl = wl; a.sl = sl;
         a.dst = dx;
         a.partials = reinterpret_cast<float*>(ws);
-        int e = p.tiny ? launch_tiny(a, d->dtype, 1, p.grid, stream)
-                       : launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
+        int e = p.tiny == 2 ? launch_lane(a, d->dtype, 1, p.grid, stream)
+                : p.tiny    ? launch_tiny(a, d->dtype, 1, p.grid, stream)
+                            : launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);
         if (e != 0) return WTC_EHIP;
         FinalizeArgs f;
         f.partials = a.partials;

@@ -1,0 +1,288 @@
+// WTConv for 7 x 7 planes with one wavelet level (k = 5), one plane per lane
+// (gfx950).  (The kernel template takes any plane up to 8 x 8; only 7 x 7 is
+// instantiated: at 8 x 8 the backward no longer fits the register file.)
+//
+// A workgroup is one wave: 64 batch entries of one channel, so every weight is
+// uniform across the wave (scalar registers) and every index into a plane is
+// a compile-time constant: the base conv, the four level-1 subband convs and
+// the level-1 synthesis are straight-line multiply-adds over registers, with
+// the zero extension and the zero padding resolved at compile time (no work
+// on padding).  Planes move between device memory and registers through LDS:
+// a plane is 49 contiguous values, loaded and stored one plane per wave
+// instruction (coalesced), and read by its lane at an odd stride (no bank
+// conflicts).
+//
+// Same operator and conventions as the other fused kernels: raw +-1 Haar
+// butterflies, level weights folded as 4^-1 s_u W_u (applied to each conv
+// output), backward = the same pipeline on g with 180-degree-rotated weights,
+// plus the correlations C_0[d] = sum g[p] x[p + d] and
+// C_1^u[d] = sum G_u[j] X_u[j + d] (raw bands), reduced over the wave into one
+// record per (batch chunk, channel): [C_0][C_1 bands 0..3][sum g][tail = 0].
+#include <hip/hip_runtime.h>
+
+#include "wtc_internal.h"
+
+namespace wtc {
+namespace {
+
+constexpr int K = 5, R = 2, KK = 25;
+
+struct bf16v {
+    uint16_t bits;
+};
+__device__ __forceinline__ float lval(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float lval(const bf16v* p, size_t i) { return __uint_as_float(((uint32_t)p[i].bits) << 16); }
+__device__ __forceinline__ void lput(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void lput(bf16v* p, size_t i, float v) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite values)
+    p[i].bits = (uint16_t)(u >> 16);
+}
+
+// Value of v in lane l - N of the same 16-lane row (0 for the row's first N lanes).
+template <int N>
+__device__ __forceinline__ float lshr(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x110 | N, 0xF, 0xF, true));
+}
+// Lane 15 of every 16-lane row: the sum of v over the row.
+__device__ __forceinline__ float lrow_sum(float v) {
+    v += lshr<1>(v);
+    v += lshr<2>(v);
+    v += lshr<4>(v);
+    return v + lshr<8>(v);
+}
+
+// Plane staging: planes j = 0 .. 63 of the wave (batch entries b0 + j of
+// channel c, n valid) into lds[j * SP + e] (e < N values per plane).
+template <int N, int SP, typename ST>
+__device__ __forceinline__ void stage_in(float* lds, const ST* src, int C, int c, int b0, int n, int lane) {
+    constexpr int G = 16;   // planes per group of loads in flight
+#pragma unroll
+    for (int j0 = 0; j0 < 64; j0 += G) {
+        float v[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            v[j] = (lane < N && j0 + j < n) ? lval(src, ((size_t)(b0 + j0 + j) * C + c) * N + lane) : 0.f;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (lane < N) lds[(j0 + j) * SP + lane] = v[j];
+    }
+}
+template <int N, int SP, typename ST>
+__device__ __forceinline__ void stage_out(const float* lds, ST* dst, int C, int c, int b0, int n, int lane) {
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j)
+        if (lane < N && j < n) lput(dst, ((size_t)(b0 + j) * C + c) * N + lane, lds[j * SP + lane]);
+}
+
+// Raw Haar band u of the 2 x 2 block at level-1 position (jy, jx) of an
+// HP x WP plane held in registers (zero beyond the plane).
+template <int HP, int WP>
+__device__ __forceinline__ float band_at(const float (&P)[HP][WP], int u, int jy, int jx) {
+    const int y = 2 * jy, x = 2 * jx;
+    const float a = P[y][x];
+    const float b = (x + 1 < WP) ? P[y][x + 1] : 0.f;
+    const float c = (y + 1 < HP) ? P[y + 1][x] : 0.f;
+    const float d = (y + 1 < HP && x + 1 < WP) ? P[y + 1][x + 1] : 0.f;
+    switch (u) {
+        case 0: return (a + b) + (c + d);
+        case 1: return (a - b) + (c - d);
+        case 2: return (a + b) - (c + d);
+        default: return (a - b) - (c - d);
+    }
+}
+
+template <typename ST, bool BWD, int HP, int WP>
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(BWD ? 2 : 3)))
+k_lane(const FusedArgs a) {
+    constexpr int N = HP * WP, SP = (N % 2 == 0) ? N + 1 : N;
+    constexpr int H1 = (HP + 1) / 2, W1 = (WP + 1) / 2;   // level-1 grid
+    __shared__ float lds[64 * SP];
+    const int lane = threadIdx.x;
+    const int c = blockIdx.x % a.C, chunk = blockIdx.x / a.C;
+    const int b0 = chunk * 64, n = min(64, a.B - b0);
+    const ST* srcp = reinterpret_cast<const ST*>(a.src);
+    const ST* auxp = reinterpret_cast<const ST*>(a.aux);
+    ST* dstp = reinterpret_cast<ST*>(a.dst);
+
+    // ---- this lane's plane (g in the backward) and, backward, x
+    float P[HP][WP], X[HP][WP];
+    stage_in<N, SP, ST>(lds, srcp, a.C, c, b0, n, lane);
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < HP; ++y)
+#pragma unroll
+        for (int x = 0; x < WP; ++x) P[y][x] = lds[lane * SP + y * WP + x];
+    if constexpr (BWD) {
+        __syncthreads();
+        stage_in<N, SP, ST>(lds, auxp, a.C, c, b0, n, lane);
+        __syncthreads();
+#pragma unroll
+        for (int y = 0; y < HP; ++y)
+#pragma unroll
+            for (int x = 0; x < WP; ++x) X[y][x] = lds[lane * SP + y * WP + x];
+    }
+
+    // ---- base conv (rotated weights backward), zero padding resolved at compile time
+    float O[HP][WP];
+    {
+        float w[KK];
+#pragma unroll
+        for (int t = 0; t < KK; ++t) w[t] = a.w0[(size_t)c * KK + (BWD ? KK - 1 - t : t)];
+#pragma unroll
+        for (int y = 0; y < HP; ++y)
+#pragma unroll
+            for (int x = 0; x < WP; ++x) {
+                float s = 0.f;
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) {
+                        const int yy = y + ky - R, xx = x + kx - R;
+                        if (yy >= 0 && yy < HP && xx >= 0 && xx < WP) s = fmaf(w[ky * K + kx], P[yy][xx], s);
+                    }
+                O[y][x] = s;
+            }
+        const float s0 = a.s0[c], bias = BWD ? 0.f : a.b0[c];
+#pragma unroll
+        for (int y = 0; y < HP; ++y)
+#pragma unroll
+            for (int x = 0; x < WP; ++x) O[y][x] = fmaf(s0, O[y][x], bias);
+    }
+
+    // ---- backward: base correlation and sum of g, reduced over the wave
+    float* rec = BWD ? a.partials + ((size_t)chunk * a.C + c) * a.P : nullptr;
+    float* red = lds;   // [4 rows][...] row partials (after the planes are read)
+    if constexpr (BWD) {
+        float C0[KK], sg = 0.f;
+#pragma unroll
+        for (int t = 0; t < KK; ++t) C0[t] = 0.f;
+#pragma unroll
+        for (int y = 0; y < HP; ++y)
+#pragma unroll
+            for (int x = 0; x < WP; ++x) {
+                sg += P[y][x];
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) {
+                        const int yy = y + ky - R, xx = x + kx - R;
+                        if (yy >= 0 && yy < HP && xx >= 0 && xx < WP)
+                            C0[ky * K + kx] = fmaf(P[y][x], X[yy][xx], C0[ky * K + kx]);
+                    }
+            }
+        __syncthreads();   // every lane has read its planes
+#pragma unroll
+        for (int t = 0; t < KK; ++t) C0[t] = lrow_sum(C0[t]);
+        sg = lrow_sum(sg);
+        if ((lane & 15) == 15) {
+            const int row = lane >> 4;
+#pragma unroll
+            for (int t = 0; t < KK; ++t) red[row * (5 * KK + 1) + t] = C0[t];
+            red[row * (5 * KK + 1) + 5 * KK] = sg;
+        }
+    }
+
+    // ---- level 1, one subband at a time: raw band, conv with W_u (rotated
+    // backward), scaled by 4^-1 s_u, synthesised into O (raw +-1 signs)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        float Bv[H1][W1], Xv[H1][W1];
+#pragma unroll
+        for (int jy = 0; jy < H1; ++jy)
+#pragma unroll
+            for (int jx = 0; jx < W1; ++jx) {
+                Bv[jy][jx] = band_at<HP, WP>(P, u, jy, jx);
+                if constexpr (BWD) Xv[jy][jx] = band_at<HP, WP>(X, u, jy, jx);
+            }
+        const size_t pu = (size_t)c * 4 + u;
+        float w[KK];
+#pragma unroll
+        for (int t = 0; t < KK; ++t) w[t] = a.wl[pu * KK + (BWD ? KK - 1 - t : t)];
+        const float su = ldexpf(a.sl[pu], -2);
+#pragma unroll
+        for (int jy = 0; jy < H1; ++jy)
+#pragma unroll
+            for (int jx = 0; jx < W1; ++jx) {
+                float s = 0.f;
+#pragma unroll
+                for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < K; ++kx) {
+                        const int yy = jy + ky - R, xx = jx + kx - R;
+                        if (yy >= 0 && yy < H1 && xx >= 0 && xx < W1) s = fmaf(w[ky * K + kx], Bv[yy][xx], s);
+                    }
+                const float yv = su * s;
+                // synthesis: pixel (2 jy + dy, 2 jx + dx) gets sign_u(dy, dx) * yv
+#pragma unroll
+                for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+                    for (int dx = 0; dx < 2; ++dx) {
+                        const int y = 2 * jy + dy, x = 2 * jx + dx;
+                        if (y >= HP || x >= WP) continue;
+                        const bool neg = ((u & 1) && dx) != ((u & 2) && dy);
+                        O[y][x] = neg ? O[y][x] - yv : O[y][x] + yv;
+                    }
+            }
+        if constexpr (BWD) {
+            float C1[KK];
+#pragma unroll
+            for (int t = 0; t < KK; ++t) C1[t] = 0.f;
+#pragma unroll
+            for (int jy = 0; jy < H1; ++jy)
+#pragma unroll
+                for (int jx = 0; jx < W1; ++jx)
+#pragma unroll
+                    for (int ky = 0; ky < K; ++ky)
+#pragma unroll
+                        for (int kx = 0; kx < K; ++kx) {
+                            const int yy = jy + ky - R, xx = jx + kx - R;
+                            if (yy >= 0 && yy < H1 && xx >= 0 && xx < W1)
+                                C1[ky * K + kx] = fmaf(Bv[jy][jx], Xv[yy][xx], C1[ky * K + kx]);
+                        }
+#pragma unroll
+            for (int t = 0; t < KK; ++t) C1[t] = lrow_sum(C1[t]);
+            if ((lane & 15) == 15) {
+                const int row = lane >> 4;
+#pragma unroll
+                for (int t = 0; t < KK; ++t) red[row * (5 * KK + 1) + KK + u * KK + t] = C1[t];
+            }
+        }
+    }
+
+    // ---- results: records (backward), then the planes out through LDS
+    if constexpr (BWD) {
+        __syncthreads();
+        for (int e = lane; e < a.P; e += 64) {
+            float v = 0.f;
+            if (e < 5 * KK + 1)
+#pragma unroll
+                for (int row = 0; row < 4; ++row) v += red[row * (5 * KK + 1) + e];
+            rec[e] = v;   // e = P - 1: tail term, 0 (every level is on a grid larger than 1 x 1)
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < HP; ++y)
+#pragma unroll
+        for (int x = 0; x < WP; ++x) lds[lane * SP + y * WP + x] = O[y][x];
+    __syncthreads();
+    stage_out<N, SP, ST>(lds, dstp, a.C, c, b0, n, lane);
+}
+
+template <typename ST, bool BWD>
+hipError_t lane_launch(const FusedArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((k_lane<ST, BWD, 7, 7>), dim3(grid), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int launch_lane(const FusedArgs& a, int dtype, int bwd, int grid, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (dtype == WTC_BF16)
+        return (int)(bwd ? lane_launch<bf16v, true>(a, grid, st) : lane_launch<bf16v, false>(a, grid, st));
+    return (int)(bwd ? lane_launch<float, true>(a, grid, st) : lane_launch<float, false>(a, grid, st));
+}
+
+}  // namespace wtc

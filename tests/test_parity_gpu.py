@@ -76,6 +76,9 @@ TINY = [
     (17, 2, 7, 7, 2, 5, 73, "fp32"),
     (3, 4, 7, 7, 2, 5, 74, "bf16"),
     (5, 3, 2, 2, 1, 5, 75, "fp32"),
+    # 7 x 7 with one level: one plane per lane, 64 batch entries per wave
+    (70, 3, 7, 7, 1, 5, 76, "fp32"),       # a full and a partial wave per channel
+    (5, 4, 7, 7, 1, 5, 77, "bf16"),
 ]
 
 
