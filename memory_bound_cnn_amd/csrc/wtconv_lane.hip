@@ -56,7 +56,7 @@ __device__ __forceinline__ float lrow_sum(float v) {
 // channel c, n valid) into lds[j * SP + e] (e < N values per plane).
 template <int N, int SP, typename ST>
 __device__ __forceinline__ void stage_in(float* lds, const ST* src, int C, int c, int b0, int n, int lane) {
-    constexpr int G = 16;   // planes per group of loads in flight
+    constexpr int G = 32;   // planes per group of loads in flight
 #pragma unroll
     for (int j0 = 0; j0 < 64; j0 += G) {
         float v[G];
