@@ -76,8 +76,8 @@ typedef struct {
 /* Bytes of device workspace wtconv_forward needs (0: none).  It is 0 for every
  * plane the on-chip pipeline holds (up to about 128 x 128 with k = 5); larger
  * planes peel one wavelet level (below) and need float32 tensors of their
- * LL band and deeper result (the size also covers the level-by-level
- * intermediates of the peeled level).  0 is also returned for a
+ * LL band and deeper result (L = 0: the level-by-level depthwise conv's
+ * intermediates).  0 is also returned for a
  * descriptor that the forward pass rejects. */
 size_t wtconv_forward_workspace(const wtc_desc* d);
 
@@ -96,7 +96,8 @@ int wtconv_forward(const wtc_desc* d, const void* x,
 
 /* Bytes of device workspace wtconv_backward needs (per-workgroup partial
  * sums of the weight-gradient correlations; for planes beyond the on-chip
- * pipeline also the tensors of the peeled level and of the LL problem). */
+ * pipeline the per-tile correlation records of the peeled level and the
+ * tensors of the LL problem). */
 size_t wtconv_backward_workspace(const wtc_desc* d);
 
 /* Backward pass: given g = d loss / d out, writes

@@ -225,8 +225,9 @@ size_t al256(size_t v) { return (v + 255) / 256 * 256; }
 
 struct PeelPlan {
     wtc_desc d1, sub;   // level 1 of this plane; the LL problem (L - 1 levels, fp32)
-    UnfusedPlan u;
+    UnfusedPlan u;      // L = 0: the level-by-level depthwise conv
     size_t n1;          // floats of one LL tensor [B, C, h1, w1]
+    size_t rec1_off;    // backward: level-1 tile records (base records at 0)
     size_t a_off, b_off, c_off, par_off, sub_off, total;
 };
 
@@ -242,7 +243,18 @@ int peel_plan(const wtc_desc* d, bool bwd, int depth, PeelPlan* pp) {
     const int h1 = (d->H + 1) / 2, w1 = (d->W + 1) / 2;
     pp->n1 = (size_t)d->B * d->C * h1 * w1;
     pp->sub = wtc_desc{d->B, d->C, h1, w1, d->L - 1, d->k, WTC_FP32, 0};
-    size_t off = al256(pp->u.total);
+    // front of the workspace: L = 0, the level-by-level conv's intermediates;
+    // backward with levels, the tile kernel's correlation records (base, level 1)
+    size_t base = 0;
+    pp->rec1_off = 0;
+    if (d->L == 0) {
+        base = pp->u.total;
+    } else if (bwd) {
+        const size_t nrec = top_records(d);
+        pp->rec1_off = al256(nrec * sizeof(float));
+        base = pp->rec1_off + al256(4 * nrec * sizeof(float));
+    }
+    size_t off = al256(base);
     pp->a_off = off;   // forward: LL of x;  backward: LL of x
     pp->b_off = off = off + al256(pp->n1 * 4);   // forward: Z_2;  backward: LL of g
     pp->c_off = off = off + al256(pp->n1 * 4);   // backward: dLL_1
@@ -251,7 +263,7 @@ int peel_plan(const wtc_desc* d, bool bwd, int depth, PeelPlan* pp) {
     off += al256((size_t)4 * (2 * d->C + (bwd ? d->C * d->k * d->k + 2 * d->C : 0)));
     pp->sub_off = off;
     if (d->L < 2) {
-        pp->total = pp->u.total;
+        pp->total = base;
         return WTC_OK;
     }
     const size_t sw = bwd ? fused_bwd_ws(&pp->sub, depth + 1, &st) : fused_fwd_ws(&pp->sub, depth + 1, &st);
@@ -380,10 +392,8 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
     // level 1 and the base conv fused over tiles; the tiles' correlation
     // records go where the level-by-level intermediates would (unused here)
     const size_t nrec = top_records(d);
-    const size_t rec1_off = al256(nrec * sizeof(float));
-    if (rec1_off + 4 * nrec * sizeof(float) > pp.u.total) return WTC_EWORKSPACE;
     float* part0 = reinterpret_cast<float*>(ws);
-    float* part1 = reinterpret_cast<float*>(ws + rec1_off);
+    float* part1 = reinterpret_cast<float*>(ws + pp.rec1_off);
     if ((st = top_backward(d, x, g, w0, s0, wl, sl, zext, dx, part0, part1, stream)) != WTC_OK) return st;
     const int nblk = (int)(nrec / ((size_t)d->C * (d->k * d->k + 1)));
     if ((st = launch_corr_finalize(part0, d->C, nblk, d->k, w0, s0, dw0, ds0, db0, stream)) != WTC_OK) return st;

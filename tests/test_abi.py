@@ -157,21 +157,27 @@ def test_io_model_unfused_counts_intermediates():
 
 
 def test_large_planes_take_the_peeled_path():
-    """Planes beyond the on-chip pipeline run level 1 level by level and their
-    LL band recursively: both directions need a workspace there, none (forward)
-    or only the partial records (backward) where the fused kernels fit."""
+    """Planes beyond the on-chip pipeline run their LL band recursively and
+    level 1 with the base conv fused over tiles: a workspace for the LL band,
+    the deeper result and (backward) the per-tile records there; none
+    (forward) or only the partial records (backward) where the fused kernels
+    fit."""
     assert binding.wtconv_forward_workspace(32, 96, 64, 64, 3, 5) == 0
     small_b = binding.wtconv_backward_workspace(32, 96, 64, 64, 3, 5)
     assert 0 < small_b < 4 * 32 * 96 * 64 * 64
     for H, W, L in [(200, 150, 3), (300, 260, 4), (512, 512, 5), (260, 130, 0), (140, 140, 1)]:
         f = binding.wtconv_forward_workspace(2, 3, H, W, L, 5)
         b = binding.wtconv_backward_workspace(2, 3, H, W, L, 5)
+        h1, w1 = (H + 1) // 2, (W + 1) // 2
         if L == 0:
             assert f == 0 and b > 0
+        elif L == 1:
+            # the tile kernels need no forward workspace; the backward holds
+            # the per-tile correlation records only
+            assert f == 0 and 0 < b < 2 * 3 * H * W * 4, (H, W, L, f, b)
         else:
-            # at least the level-1 bands and their conv outputs
-            h1, w1 = (H + 1) // 2, (W + 1) // 2
-            assert f >= 2 * 4 * 2 * 3 * h1 * w1 * 4 and b > f, (H, W, L, f, b)
+            # at least the LL band and the deeper result, in float32
+            assert f >= 2 * 2 * 3 * h1 * w1 * 4 and b > f, (H, W, L, f, b)
     # the analytic traffic of the peeled forward exceeds the fused one's 2 N e
     n = 2 * 3 * 200 * 150 * 4
     assert binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=0, direction=0) > 2 * n
