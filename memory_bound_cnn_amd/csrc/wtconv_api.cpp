@@ -138,15 +138,22 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         if (better) best = Cand{lay, NP, nthr, bpq, wgs, score};
     };
     if (a.qpp > 256) return WTC_ESHAPE;
-    // direct loads (DMA into the LDS slot, layout mode 1): rows of 4-pixel
-    // vectors on the plane classes with fixed-geometry instances of that mode
-    // (fp32 32x32 and 64x64; bf16 32x32 backward only: its forward measured
-    // faster staging through registers, 54 us against 70 us), one plane per
-    // workgroup; tried first, so it wins ties
+    // direct loads (DMA into the LDS slot, layout mode 1): planes of 4-pixel
+    // rows with one block per quad (at most 128 quads), one plane per
+    // workgroup.  The backward, fp32 or bf16: staged through registers it holds
+    // a plane's prefetch next to its correlation accumulators and spills.  The
+    // forward on the plane classes with fixed-geometry instances of that mode
+    // (fp32 32x32 and 64x64; the bf16 forward measured faster staging through
+    // registers, 54 us against 70 us on 32x32 planes; elsewhere the mode-1
+    // layout is staged through registers).  Tried first, so it wins ties.
     const int esz = d->dtype == WTC_BF16 ? 2 : 4;
-    const bool dl_ok = a.vec && a.Hq == a.Wq &&
-                       ((d->dtype == WTC_FP32 && (k == 5 || (k == 7 && d->L == 0)) && (a.Hq == 32 || a.Hq == 64)) ||
-                        (d->dtype == WTC_BF16 && bwd && k == 5 && a.Hq == 32));
+    const bool dl_ok = a.vec && a.qpp <= 128 &&
+                       (bwd || (d->dtype == WTC_FP32 && (k == 5 || (k == 7 && d->L == 0)) && a.Hq == a.Wq &&
+                                (a.Hq == 32 || a.Hq == 64)));
+    // The backward takes direct loads whenever one plane fills a wave, even where
+    // the larger slot (it holds a plane of x too) leaves fewer workgroups resident
+    // (32x32 fp32: 7 instead of 8 per CU).
+    const bool dl_only = dl_ok && bwd && a.qpp >= 16;
     // then the layout without overlap (mode 2), which spares the per-plane ring
     // re-zeroing and wins ties against the overlapping one (32x32 bf16 forward:
     // 52 us against 54 us)
@@ -155,6 +162,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         const int bovl = variant < 0 ? 0 : variant;
         const int mode = dl ? 1 : (variant == -2 ? 2 : 0);
         if (dl && !dl_ok) continue;
+        if (!dl && dl_only && best.score >= 0) break;
         if (bovl > a.Lm) continue;
         Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl, mode, esz);
         if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl, mode, esz);

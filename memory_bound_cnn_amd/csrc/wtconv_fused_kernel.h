@@ -322,13 +322,18 @@ __device__ __forceinline__ float row_sum(float v) {
 // Plane geometry.  RtGeom reads it from the kernel arguments (any plane size);
 // CtGeom fixes it at compile time, so LDS strides and offsets become
 // immediates and the per-level loops unroll.  Both describe the same layout
-// (make_layout), so one kernel body serves both.
+// (make_layout), so one kernel body serves both.  kDeep = deep levels (>= 3)
+// whose backward correlation accumulators a thread holds across planes: the
+// runtime-geometry kernel is compiled for Lm <= 3 (one set) and for any Lm,
+// so that the common shallow plans keep 20 registers free.
 // ---------------------------------------------------------------------------
+template <bool DLM, int LMX>
 struct RtGeom {
-    static constexpr bool kDL = false;   // the runtime-geometry kernel stages planes through registers
+    static constexpr bool kDL = DLM;     // planes by DMA (layout mode 1) or staged through registers
     static constexpr bool kXSeg = false;
     static constexpr bool kFixed = false;
     static constexpr bool kNoLevels = false;
+    static constexpr int kDeep = LMX > 3 ? LMX - 2 : 1;
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
     __device__ int Lm() const { return a.Lm; }
@@ -371,6 +376,7 @@ struct CtGeom {
         MODE == 1 && (!BWDL || red_len(NTHR, K, LM, NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1) <= lay.a0_off);
     static constexpr bool kFixed = true;
     static constexpr bool kNoLevels = LM == 0;
+    static constexpr int kDeep = kMaxLm - 2;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -658,22 +664,22 @@ wtc_fused_kernel(const FusedArgs a) {
                 else rows(std::false_type{});
             }
         } else if constexpr (DL && !SDL) {
-            constexpr int CPR = (G::Wq() + 63) / 64;
-            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
+            // runtime geometry: one plane (the planner's direct-load plans have
+            // NP = 1), addressed once; rows dealt to the waves round-robin, each
+            // row in 64-pixel chunks
+            if (bbn >= bend) return;
+            // (lane from an opaque copy: no per-lane address is kept live across the plane loop)
+            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = opaque(tid0) & 63;
             const int nw = nthr >> 6;
-            const int per_plane = a.H * CPR;
-            for (int j = wave; j < g.NP() * per_plane; j += nw) {
-                const int s2 = g.NP() == 1 ? 0 : j / per_plane;
-                const int m = j - s2 * per_plane;
-                const int r = CPR == 1 ? m : m / CPR, cc = m - r * CPR;
-                if (bbn + s2 >= bend) continue;
-                const int col = cc * 64 + lane;
-                if (col < a.W)
-                    __builtin_amdgcn_global_load_lds(
-                        (const void*)(base + ((size_t)(bbn + s2) * a.C + ch) * plane_sz + (size_t)r * a.W + col),
-                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc +
-                                                                   cc * 64),
-                        4, 0, 0);
+            const ST* pb = base + ((size_t)bbn * a.C + ch) * plane_sz;
+            float* lb = lds + roff + rr * rS + rc;
+            for (int c0 = 0; c0 < a.W; c0 += 64) {
+                if (c0 + lane >= a.W) break;
+                const ST* src = pb + (size_t)wave * a.W + c0 + lane;
+                float* dst = lb + wave * rS + c0;
+                for (int r = wave; r < a.H; r += nw, src += (size_t)nw * a.W, dst += nw * rS)
+                    __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
+                                                     4, 0, 0);
             }
         }
     };
@@ -705,19 +711,17 @@ wtc_fused_kernel(const FusedArgs a) {
             if (words == G::Hq() * G::Wq() / 2 && words % 64 == 0) chunks(std::true_type{});
             else chunks(std::false_type{});
         } else if constexpr (SDL) {
-            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
+            // runtime geometry, one plane (NP = 1 with direct loads)
+            if (bbn >= bend) return;
+            const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = opaque(tid0) & 63;
             const int nw = nthr >> 6;
-            const int words = (a.H * a.W) >> 1, chunks = (words + 63) >> 6;
-            for (int j = wave; j < g.NP() * chunks; j += nw) {
-                const int s2 = g.NP() == 1 ? 0 : j / chunks, k = j - s2 * chunks;
-                if (bbn + s2 >= bend) continue;
-                const int i = k * 64 + lane;
-                if (i < words)
-                    __builtin_amdgcn_global_load_lds(
-                        (const void*)(reinterpret_cast<const uint32_t*>(srcp + ((size_t)(bbn + s2) * a.C + ch) * plane_sz) +
-                                      i),
-                        (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + g.st_off() + k * 64), 4, 0, 0);
-            }
+            const int words = (a.H * a.W) >> 1;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(srcp + ((size_t)bbn * a.C + ch) * plane_sz);
+            float* dst = lds + g.st_off();
+            for (int k = wave * 64; k < words; k += nw * 64)
+                if (k + lane < words)
+                    __builtin_amdgcn_global_load_lds((const void*)(src + k + lane),
+                                                     (__attribute__((address_space(3))) void*)(dst + k), 4, 0, 0);
         }
     };
     // the first planes' copies are issued before the set-up below, which they
@@ -776,11 +780,12 @@ wtc_fused_kernel(const FusedArgs a) {
         for (int u = 0; u < 4; ++u) kappa += wts[(i * 4 + u) * KKP + (KK >> 1)];
 
     // ---- persistent backward accumulators ----
-    float corr0[KK], corr1[KK], corr2[KK], cdeep[kMaxLm - 2][K];
+    constexpr int ND = G::kDeep;
+    float corr0[KK], corr1[KK], corr2[KK], cdeep[ND][K];
 #pragma unroll
     for (int i = 0; i < KK; ++i) corr0[i] = corr1[i] = corr2[i] = 0.f;
 #pragma unroll
-    for (int q = 0; q < kMaxLm - 2; ++q)
+    for (int q = 0; q < ND; ++q)
 #pragma unroll
         for (int kx = 0; kx < K; ++kx) cdeep[q][kx] = 0.f;
     float sumg = 0.f, tailc = 0.f;
@@ -1187,7 +1192,7 @@ wtc_fused_kernel(const FusedArgs a) {
                         }
                     }
 #pragma unroll
-                    for (int q = 0; q < kMaxLm - 2; ++q)
+                    for (int q = 0; q < ND; ++q)
                         if (q == i - 3)
 #pragma unroll
                             for (int kx = 0; kx < K; ++kx) cdeep[q][kx] += cv[kx];
@@ -1353,7 +1358,7 @@ wtc_fused_kernel(const FusedArgs a) {
         }
         if (dactive) {
 #pragma unroll
-            for (int q = 0; q < kMaxLm - 2; ++q)
+            for (int q = 0; q < ND; ++q)
                 if (q + 3 <= Lm)
 #pragma unroll
                     for (int kx = 0; kx < K; ++kx) dred[(q * droles + drole) * K + kx] = cdeep[q][kx];
@@ -1399,25 +1404,44 @@ hipError_t launch_t(const FusedArgs& a, int nthr, size_t lds, int grid, hipStrea
     return hipGetLastError();
 }
 
-// Runtime-geometry kernel for any plane the LDS pipeline holds.
+// Runtime-geometry kernel for any plane the LDS pipeline holds.  The backward
+// with a layout-mode-1 plan copies its planes by DMA (4-pixel rows, one block
+// per quad, one plane per workgroup); everything else is staged through
+// registers (the forward also on mode-1 layouts: nothing overlaps the level-0
+// plane there either).  The backward comes in two deep-level classes (Lm <= 3,
+// any Lm).
 template <int K>
 hipError_t launch_rt(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
                      hipStream_t st) {
-#define WTC_RT(ST_, BWD_)                                                                    \
-    do {                                                                                     \
-        if (a.vec) {                                                                         \
-            if (bpq == 1) return launch_t<K, ST_, BWD_, 1, true, RtGeom>(a, nthr, lds, grid, st); \
-            return launch_t<K, ST_, BWD_, 2, true, RtGeom>(a, nthr, lds, grid, st);          \
-        }                                                                                    \
-        if (bpq == 1) return launch_t<K, ST_, BWD_, 1, false, RtGeom>(a, nthr, lds, grid, st); \
-        return launch_t<K, ST_, BWD_, 2, false, RtGeom>(a, nthr, lds, grid, st);             \
+    if (a.Lm > kMaxLm) return hipErrorInvalidValue;
+    const bool shallow = a.Lm <= 3;
+    if (a.lay.dl && bwd) {
+        if (!a.vec || bpq != 1 || a.NP != 1) return hipErrorInvalidValue;
+        if (dtype == WTC_BF16) {
+            if (shallow) return launch_t<K, bf16_t, true, 1, true, RtGeom<true, 3>>(a, nthr, lds, grid, st);
+            return launch_t<K, bf16_t, true, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
+        }
+        if (shallow) return launch_t<K, float, true, 1, true, RtGeom<true, 3>>(a, nthr, lds, grid, st);
+        return launch_t<K, float, true, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
+    }
+#define WTC_RT(ST_, BWD_, LMX_)                                                                           \
+    do {                                                                                                 \
+        using G_ = RtGeom<false, LMX_>;                                                                  \
+        if (a.vec) {                                                                                     \
+            if (bpq == 1) return launch_t<K, ST_, BWD_, 1, true, G_>(a, nthr, lds, grid, st);            \
+            return launch_t<K, ST_, BWD_, 2, true, G_>(a, nthr, lds, grid, st);                          \
+        }                                                                                                \
+        if (bpq == 1) return launch_t<K, ST_, BWD_, 1, false, G_>(a, nthr, lds, grid, st);               \
+        return launch_t<K, ST_, BWD_, 2, false, G_>(a, nthr, lds, grid, st);                             \
     } while (0)
     if (dtype == WTC_BF16) {
-        if (bwd) WTC_RT(bf16_t, true);
-        WTC_RT(bf16_t, false);
+        if (bwd && shallow) WTC_RT(bf16_t, true, 3);
+        if (bwd) WTC_RT(bf16_t, true, kMaxLm);
+        WTC_RT(bf16_t, false, kMaxLm);
     }
-    if (bwd) WTC_RT(float, true);
-    WTC_RT(float, false);
+    if (bwd && shallow) WTC_RT(float, true, 3);
+    if (bwd) WTC_RT(float, true, kMaxLm);
+    WTC_RT(float, false, kMaxLm);
 #undef WTC_RT
 }
 
