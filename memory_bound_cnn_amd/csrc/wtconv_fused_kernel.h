@@ -543,8 +543,11 @@ wtc_fused_kernel(const FusedArgs a) {
     const int wv = VEC ? (a.W >> 2) : a.W;
     const int per = a.H * wv;
     const FastDiv dper = make_div(per), dwv = make_div(wv);
-    // (the backward kernel with two blocks per quad never has the capacity)
-    const bool pf_on = !DL && !(BWD && BPQ > 1) && a.pf_on != 0;
+    // (the backward kernel with two blocks per quad never has the capacity; the
+    // runtime-geometry backward stages synchronously: with a plane held in
+    // registers beside its correlation accumulators it spills, measured 5-13 %
+    // slower on 14x14 to 30x30 planes)
+    const bool pf_on = !DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0;
     float pf[PFU][UW];
     // With 4-pixel units the decode of each unit is done once per segment: its
     // offset within a plane group in device memory, and (packed) its plane
