@@ -142,14 +142,11 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     // rows with one block per quad (at most 128 quads), one plane per
     // workgroup.  The backward, fp32 or bf16: staged through registers it holds
     // a plane's prefetch next to its correlation accumulators and spills.  The
-    // forward on the plane classes with fixed-geometry instances of that mode
-    // (fp32 32x32 and 64x64; the bf16 forward measured faster staging through
-    // registers, 54 us against 70 us on 32x32 planes; elsewhere the mode-1
-    // layout is staged through registers).  Tried first, so it wins ties.
+    // fp32 forward: 7-8 % faster than register staging on 32x32 to 56x56
+    // planes; the bf16 forward measured faster staging through registers (54 us
+    // against 70 us on 32x32 planes).  Tried first, so it wins ties.
     const int esz = d->dtype == WTC_BF16 ? 2 : 4;
-    const bool dl_ok = a.vec && a.qpp <= 128 &&
-                       (bwd || (d->dtype == WTC_FP32 && (k == 5 || (k == 7 && d->L == 0)) && a.Hq == a.Wq &&
-                                (a.Hq == 32 || a.Hq == 64)));
+    const bool dl_ok = a.vec && a.qpp <= 128 && (bwd || d->dtype == WTC_FP32);
     // The backward takes direct loads whenever one plane fills a wave, even where
     // the larger slot (it holds a plane of x too) leaves fewer workgroups resident
     // (32x32 fp32: 7 instead of 8 per CU).

@@ -1407,19 +1407,19 @@ hipError_t launch_t(const FusedArgs& a, int nthr, size_t lds, int grid, hipStrea
     return hipGetLastError();
 }
 
-// Runtime-geometry kernel for any plane the LDS pipeline holds.  The backward
-// with a layout-mode-1 plan copies its planes by DMA (4-pixel rows, one block
-// per quad, one plane per workgroup); everything else is staged through
-// registers (the forward also on mode-1 layouts: nothing overlaps the level-0
-// plane there either).  The backward comes in two deep-level classes (Lm <= 3,
-// any Lm).
+// Runtime-geometry kernel for any plane the LDS pipeline holds.  Plans of
+// layout mode 1 copy their planes by DMA (4-pixel rows, one block per quad,
+// one plane per workgroup; fp32, or a bf16 backward); everything else is
+// staged through registers.  The backward comes in two deep-level classes
+// (Lm <= 3, any Lm).
 template <int K>
 hipError_t launch_rt(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
                      hipStream_t st) {
     if (a.Lm > kMaxLm) return hipErrorInvalidValue;
     const bool shallow = a.Lm <= 3;
-    if (a.lay.dl && bwd) {
-        if (!a.vec || bpq != 1 || a.NP != 1) return hipErrorInvalidValue;
+    if (a.lay.dl) {
+        if (!a.vec || bpq != 1 || a.NP != 1 || (dtype == WTC_BF16 && !bwd)) return hipErrorInvalidValue;
+        if (!bwd) return launch_t<K, float, false, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
         if (dtype == WTC_BF16) {
             if (shallow) return launch_t<K, bf16_t, true, 1, true, RtGeom<true, 3>>(a, nthr, lds, grid, st);
             return launch_t<K, bf16_t, true, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
