@@ -219,11 +219,14 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
 // ---------------------------------------------------------------------------
 // Planes beyond the on-chip pipeline: peel one wavelet level.
 // The levels >= 2 of WTConv are WTConv itself (one level fewer, no base conv)
-// applied to the level-1 LL band, so such a plane runs level 1 and the base
-// conv with the level-by-level kernels, and its LL band (half the size in each
-// direction) recursively through the fused entry points -- fused as soon as it
-// fits.  Workspace: [level-1 tensors][LL copies][deeper result][zero / scratch
-// parameters][the sub-problem's workspace].
+// applied to the level-1 LL band, so such a plane runs its LL band (half the
+// size in each direction) recursively through the fused entry points -- fused
+// as soon as it fits -- and level 1 with the base conv fused over tiles of the
+// full-resolution plane; with L = 0 (a depthwise conv too large for the
+// pipeline) the level-by-level conv.  Workspace: [L = 0: that conv's
+// intermediates; backward: the tile records][LL of x][Z_2 or LL of g][dLL_1]
+// [zero scale and bias, unused gradients][the sub-problem's workspace]; only
+// the front part when L < 2.
 // ---------------------------------------------------------------------------
 constexpr int kMaxPeel = 8;
 size_t al256(size_t v) { return (v + 255) / 256 * 256; }
