@@ -15,6 +15,10 @@ bool launch_fused_static_small(const FusedArgs& a, int dtype, int bwd, int bpq, 
         hit = try_static<5, float, 0, 1, false, 16, 16, 2, 2, 4, 64, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
         hit = try_static<5, float, 1, 1, false, 16, 16, 2, 2, 4, 64, 2>(a, bpq, nthr, lds, grid, st, &e);
+    if (!hit && dtype == WTC_BF16 && bwd == 0)
+        hit = try_static<5, bf16_t, 0, 1, false, 16, 16, 2, 2, 4, 64, 0>(a, bpq, nthr, lds, grid, st, &e);
+    if (!hit && dtype == WTC_BF16 && bwd == 1)
+        hit = try_static<5, bf16_t, 1, 1, false, 16, 16, 2, 2, 4, 64, 2>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 0)
         hit = try_static<5, float, 0, 1, false, 8, 8, 1, 1, 31, 128, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
