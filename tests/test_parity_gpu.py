@@ -92,10 +92,12 @@ def test_tiny_planes(B, C, H, W, L, k, seed, dtype):
 # both storage types, the shallow (Lm <= 3) and deep accumulator classes, k = 3,
 # 5 and 7, rows wider than one 64-lane copy, ragged heights.
 RUNTIME_DL = [
-    (3, 4, 32, 32, 3, 5, 80, "fp32"),
+    (3, 4, 32, 32, 3, 5, 80, "fp32"),      # (fixed-geometry instance, like 64x64 L3 bf16 below)
+    (3, 4, 32, 32, 4, 5, 88, "fp32"),      # Lm = 4
     (2, 4, 48, 48, 3, 5, 81, "fp32"),
     (2, 3, 40, 72, 4, 5, 82, "fp32"),      # Wq = 80: two row chunks; Lm = 4
     (2, 4, 64, 64, 3, 5, 83, "bf16"),
+    (2, 4, 64, 64, 2, 5, 89, "bf16"),
     (2, 3, 36, 44, 5, 3, 84, "bf16"),      # k = 3, five levels
     (2, 2, 56, 56, 2, 7, 85, "fp32"),      # k = 7
     (3, 2, 30, 100, 2, 5, 86, "fp32"),     # ragged height, Wq = 104
