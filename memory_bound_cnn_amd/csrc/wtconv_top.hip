@@ -231,7 +231,9 @@ __global__ void __launch_bounds__(kTopThreads) k_top_fwd(const T* __restrict__ x
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-    {
+    // (a block that starts below the plane stores nothing: in the bottom tiles
+    // of a plane whose height is not a multiple of the tile, whole waves skip)
+    if (ty0 + 4 * qy < H) {
         float w[KK];
 #pragma unroll
         for (int t = 0; t < KK; ++t) w[t] = w0[c * KK + t];
