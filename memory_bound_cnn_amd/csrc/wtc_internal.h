@@ -178,6 +178,7 @@ struct FusedArgs {
     int qpp, nqx;      // 8x8 pixel blocks ("quad blocks") per plane, per plane row
     int vec;           // W % 4 == 0: 4-pixel vector global accesses
     int pf_on;         // prefetch the next planes into registers
+    int nobase;        // skip the base conv: the LL problem of a peeled plane (its scale and bias are 0)
     Layout lay;
     int wts_off;       // folded weights (per workgroup)
     int red_off;       // reduction scratch (backward)

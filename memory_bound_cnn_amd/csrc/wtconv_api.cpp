@@ -311,6 +311,7 @@ int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float
         a.w0 = w0; a.s0 = s0; a.b0 = b0; a.wl = wl; a.sl = sl;
         a.dst = out;
         a.partials = nullptr;
+        a.nobase = depth > 0 ? 1 : 0;   // the LL problem of a peeled plane: scale and bias 0
         const int e = p.tiny == 2 ? launch_lane(a, d->dtype, 0, p.grid, stream)
                       : p.tiny    ? launch_tiny(a, d->dtype, 0, p.grid, stream)
                                   : launch_fused(a, d->k, d->dtype, 0, p.bpq, p.nthr, p.lds, p.grid, stream);
@@ -355,6 +356,7 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
         a.w0 = w0; a.s0 = s0; a.b0 = nullptr; a.wl = wl; a.sl = sl;
         a.dst = dx;
         a.partials = reinterpret_cast<float*>(ws);
+        a.nobase = depth > 0 ? 1 : 0;
         int e = p.tiny == 2 ? launch_lane(a, d->dtype, 1, p.grid, stream)
                 : p.tiny    ? launch_tiny(a, d->dtype, 1, p.grid, stream)
                             : launch_fused(a, d->k, d->dtype, 1, p.bpq, p.nthr, p.lds, p.grid, stream);

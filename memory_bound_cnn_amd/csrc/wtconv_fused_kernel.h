@@ -334,6 +334,7 @@ struct RtGeom {
     static constexpr bool kFixed = false;
     static constexpr bool kNoLevels = false;
     static constexpr int kDeep = LMX > 3 ? LMX - 2 : 1;
+    static constexpr bool kSub = true;   // may run the LL problem of a peeled plane
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
     __device__ int Lm() const { return a.Lm; }
@@ -377,6 +378,9 @@ struct CtGeom {
     static constexpr bool kFixed = true;
     static constexpr bool kNoLevels = LM == 0;
     static constexpr int kDeep = kMaxLm - 2;
+    // the LL problem of a peeled plane is over 64 pixels wide (its parent did
+    // not fit the pipeline): the smaller classes never check for it
+    static constexpr bool kSub = HQ > 64;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -926,7 +930,8 @@ wtc_fused_kernel(const FusedArgs a) {
                 }
             }
             const float* win = S + g.a0_off() + py0 * g.a0_S() + px0;
-            stencil<K, 4, 4, 4, BWD>(win, g.a0_S(), w, acc[s], xo, corr0);
+            // (the LL problem of a peeled plane has no base conv: scale and bias 0)
+            if (!(G::kSub && a.nobase)) stencil<K, 4, 4, 4, BWD>(win, g.a0_S(), w, acc[s], xo, corr0);
             // the block itself (window centre): raw analysis cascade in registers
             float ctr[4][4];
 #pragma unroll
