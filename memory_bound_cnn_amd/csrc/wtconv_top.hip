@@ -546,6 +546,26 @@ __global__ void __launch_bounds__(kTopThreads) k_top_ll(const T* __restrict__ x,
     }
 }
 
+// fp32 planes with W % 4 == 0: one workgroup per LL row (plane p, row jy), a
+// thread per two LL positions (one 16-byte load from each of the two x rows),
+// no per-element index divisions; same sums in the same order as k_top_ll
+__global__ void __launch_bounds__(64) k_top_ll4(const float* __restrict__ x, int H, int W, float* __restrict__ ll) {
+    const int h1 = (H + 1) >> 1, w1 = W >> 1;
+    const int row = blockIdx.x;   // p h1 + jy
+    const int p = row / h1, jy = row - p * h1;
+    const float* xr = x + (size_t)p * H * W + (size_t)(2 * jy) * W;
+    const bool ry = 2 * jy + 1 < H;
+    float* lr = ll + (size_t)row * w1;
+    for (int q = threadIdx.x; q < (W >> 2); q += 64) {
+        const float4 a = *reinterpret_cast<const float4*>(xr + 4 * q);
+        const float4 b = ry ? *reinterpret_cast<const float4*>(xr + W + 4 * q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float2 o;
+        o.x = 0.5f * ((a.x + a.y) + (b.x + b.y));
+        o.y = 0.5f * ((a.z + a.w) + (b.z + b.w));
+        *reinterpret_cast<float2*>(lr + 2 * q) = o;
+    }
+}
+
 template <int K, typename T>
 int top_fwd_k(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0, const float* wl,
               const float* sl, const float* zext, void* out, hipStream_t st) {
@@ -619,6 +639,9 @@ int top_ll(const wtc_desc* d, const void* x, float* ll, void* stream) {
     if (d->dtype == WTC_BF16)
         hipLaunchKernelGGL(k_top_ll<uint16_t>, dim3(grid), dim3(kTopThreads), 0, st,
                            reinterpret_cast<const uint16_t*>(x), n, d->H, d->W, ll);
+    else if (d->W % 4 == 0)
+        hipLaunchKernelGGL(k_top_ll4, dim3((uint32_t)d->B * d->C * ((d->H + 1) / 2)), dim3(64), 0, st,
+                           reinterpret_cast<const float*>(x), d->H, d->W, ll);
     else
         hipLaunchKernelGGL(k_top_ll<float>, dim3(grid), dim3(kTopThreads), 0, st, reinterpret_cast<const float*>(x),
                            n, d->H, d->W, ll);
