@@ -2,10 +2,15 @@
 
 Element-by-element comparisons at sizes the oracle finishes in seconds (several
 8x8 blocks per plane, ragged tails, every plane-size class the launch planner
-distinguishes), and sampled comparisons at the full benchmark shapes.
+distinguishes), and full-size launches at every benchmark shape (out and dx on sampled batch
+entries, every weight gradient over the whole batch).
 Tolerance per tensor: max|gpu - oracle| <= 1e-4 * RMS(oracle) for float32
 storage and 2e-2 * RMS(oracle) for bfloat16 storage.
 """
+
+import functools
+import hashlib
+import os
 
 import numpy as np
 import pytest
@@ -193,56 +198,83 @@ def test_finite_differences_tiny():
 FULL = ["stage1_b32c96_64x64_L3", "bf16_b64c192_32x32_L3", "odd_b128c384_14x14_L2", "odd_b128c768_7x7_L1",
         "large_b8c64_224x224_L3"]
 
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize_weight_grads.npz")
 
-def _full_sampled(wl_, L):
-    """Full-size launch (the benchmark's launch configuration); out and dx checked
-    on two sampled batch entries; weight gradients checked with g masked to
-    those entries, so the oracle only needs those entries."""
+
+@functools.lru_cache(maxsize=1)
+def _golden_file():
+    return np.load(GOLDEN)   # written by tests/golden/make_fullsize_grads.py (oracle only)
+
+
+def _golden(case):
+    z = _golden_file()
+    out = {k: z[f"{case}|{k}"] for k in ("dw0", "ds0", "db0", "dwl", "dsl") if f"{case}|{k}" in z.files}
+    return out, str(z[f"{case}|inputs_sha256"])
+
+
+def _inputs_sha256(d, L):
+    h = hashlib.sha256()
+    for key in ("x", "g", "w0", "s0", "b0", "wl", "sl"):
+        v = d[key]
+        if key in ("wl", "sl"):
+            v = v[:L] if (v is not None and L > 0) else None
+        h.update(key.encode())
+        if v is not None:
+            h.update(np.ascontiguousarray(v).tobytes())
+    return h.hexdigest()
+
+
+def _full_size(wl_, L):
+    """Full-size launch in the benchmark's launch configuration, with the real
+    upstream gradient over the whole batch.  out and dx are compared with the
+    oracle on two sampled batch entries; the weight gradients -- reductions
+    over all B*H*W positions of every channel -- with the oracle's values for
+    the whole batch (tests/golden/fullsize_weight_grads.npz, computed from the
+    same seeded inputs, whose hash is checked first)."""
     d = workload_inputs(wl_)
+    case = f"{wl_.name}_L{L}"
+    ref_w, sha = _golden(case)
+    assert _inputs_sha256(d, L) == sha, f"{case}: seeded inputs differ from the ones the golden values came from"
     rng = np.random.default_rng(7)
     batch = np.sort(rng.choice(wl_.B, size=2, replace=False))
-    mask = np.zeros(wl_.B, dtype=bool)
-    mask[batch] = True
-    d = dict(d)
-    d["g"] = np.where(mask[:, None, None, None], d["g"], 0.0).astype(np.float32)
     t = to_dev(d, wl_.dtype, L)
     if L < (t["wl"].shape[0] if t["wl"] is not None else 0):
         t["wl"], t["sl"] = t["wl"][:L].contiguous(), t["sl"][:L].contiguous()
     out, gr = run_fused(t, L)
+    o = host(out)[batch]
+    dxs = host(gr["dx"])[batch]
+    del out, t
     dd = dict(d)
     dd["x"], dd["g"] = d["x"][batch], d["g"][batch]
     ref_out, ref_gr = oracle_ref(dd, L)
-    o = host(out)[batch]
-    gr_h = {k: host(v) for k, v in gr.items()}
-    gr_h["dx"] = gr_h["dx"][batch]
     tol = 1e-4 if wl_.dtype == "fp32" else 2e-2
-    errs = {"out": rel_err(o, ref_out)}
-    for k in ("dx", "dw0", "ds0", "db0", "dwl", "dsl"):
-        if ref_gr.get(k) is not None:
-            errs[k] = rel_err(gr_h[k], ref_gr[k])
+    errs = {"out": rel_err(o, ref_out), "dx": rel_err(dxs, ref_gr["dx"])}
+    for k, ref in ref_w.items():
+        errs[k] = rel_err(host(gr[k]), ref)
+    assert set(errs) >= {"dw0", "ds0", "db0"} and (L == 0 or {"dwl", "dsl"} <= set(errs)), errs
     bad = {k: v for k, v in errs.items() if not v <= tol}
-    assert not bad, f"{wl_.name} L{L}: {bad} (all {errs})"
+    assert not bad, f"{case}: {bad} (all {errs})"
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
+def test_full_size(name):
     wl_ = WORKLOADS[name]
-    _full_sampled(wl_, wl_.L)
+    _full_size(wl_, wl_.L)
 
 
 @pytest.mark.parametrize("L", [1, 2, 3, 4, 5])
-def test_full_size_sweep_sampled(L):
-    _full_sampled(WORKLOADS["sweep_b64c96_128x128"], L)
+def test_full_size_sweep(L):
+    _full_size(WORKLOADS["sweep_b64c96_128x128"], L)
 
 
 @pytest.mark.parametrize("k", [5, 7])
-def test_full_size_dwconv_sampled(k):
+def test_full_size_dwconv(k):
     """The plain depthwise-conv paths that WTConv is timed against: L = 0 at the
     headline block shape, k = 5 and k = 7, in the benchmark's launch configuration."""
     import dataclasses
     wl_ = dataclasses.replace(WORKLOADS["stage1_b32c96_64x64_L3"], name=f"stage1_L0_k{k}", L=0, k=k, L_max=0,
                               sweep=())
-    _full_sampled(wl_, 0)
+    _full_size(wl_, 0)
 
 
 # Planes beyond the on-chip pipeline: level 1 and the base conv level by level,
