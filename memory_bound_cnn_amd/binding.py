@@ -145,6 +145,11 @@ def _check_params(x, w0, s0, b0, wl, sl, L):
 
 
 def _workspace(nbytes, device, workspace):
+    """The caller's workspace if it is large enough, else a new one.  A given
+    workspace must be a contiguous tensor on the call's device."""
+    if workspace is not None:
+        if not workspace.is_cuda or workspace.device != device or not workspace.is_contiguous():
+            raise ValueError(f"workspace must be a contiguous CUDA tensor on {device}")
     if nbytes == 0:
         return None, 0
     if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
@@ -169,8 +174,30 @@ def _fwd_common(fn_name, ws_name, x, w0, s0, b0, wl, sl, L, out, workspace):
     return out
 
 
-def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace):
+def _grad_buffers(x, L, k, grads):
+    """Output buffers of the weight gradients: new ones, or the caller's,
+    checked for device, dtype, shape and contiguity (the library writes through
+    these pointers)."""
     C = x.shape[1]
+    f32 = dict(dtype=torch.float32, device=x.device)
+    shapes = dict(dw0=(C, k, k), ds0=(C,), db0=(C,), dwl=(L, 4 * C, k, k), dsl=(L, 4 * C))
+    if grads is None:
+        return {name: (torch.empty(shp, **f32) if (L > 0 or name in ("dw0", "ds0", "db0")) else None)
+                for name, shp in shapes.items()}
+    out = {}
+    for name, shp in shapes.items():
+        t = grads.get(name)
+        if L == 0 and name in ("dwl", "dsl"):
+            out[name] = None
+            continue
+        if t is None:
+            raise ValueError(f"grads[{name!r}] is required")
+        _check_tensor(t, name, (torch.float32,), x.device, shp)
+        out[name] = t
+    return out
+
+
+def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace):
     k = _check_params(x, w0, s0, None, wl, sl, L)
     _check_tensor(g, "g", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
     lib = load_library()
@@ -178,16 +205,12 @@ def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace)
     if dx is None:
         dx = torch.empty_like(x)
     _check_tensor(dx, "dx", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
-    if grads is None:
-        f32 = dict(dtype=torch.float32, device=x.device)
-        grads = dict(dw0=torch.empty(C, k, k, **f32), ds0=torch.empty(C, **f32), db0=torch.empty(C, **f32),
-                     dwl=torch.empty(L, 4 * C, k, k, **f32) if L > 0 else None,
-                     dsl=torch.empty(L, 4 * C, **f32) if L > 0 else None)
+    grads = _grad_buffers(x, L, k, grads)
+    args = [ctypes.byref(d), _ptr(x), _ptr(g), _ptr(w0), _ptr(s0),
+            _ptr(wl if L > 0 else None), _ptr(sl if L > 0 else None), _ptr(dx),
+            _ptr(grads["dw0"]), _ptr(grads["ds0"]), _ptr(grads["db0"]), _ptr(grads["dwl"]), _ptr(grads["dsl"])]
     ws, wsb = _workspace(getattr(lib, ws_name)(ctypes.byref(d)), x.device, workspace)
-    st = getattr(lib, fn_name)(ctypes.byref(d), _ptr(x), _ptr(g), _ptr(w0), _ptr(s0),
-                               _ptr(wl if L > 0 else None), _ptr(sl if L > 0 else None), _ptr(dx),
-                               _ptr(grads["dw0"]), _ptr(grads["ds0"]), _ptr(grads["db0"]),
-                               _ptr(grads["dwl"]), _ptr(grads["dsl"]), _ptr(ws), wsb, _stream(x.device))
+    st = getattr(lib, fn_name)(*args, _ptr(ws), wsb, _stream(x.device))
     if st != WTC_OK:
         raise WTCError(st, fn_name)
     out = dict(grads)
