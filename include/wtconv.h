@@ -60,7 +60,9 @@ typedef enum {
     WTC_ESHAPE = -2,     /* k > 7, or a tensor of 2^31 elements or more */
     WTC_EDTYPE = -3,     /* dtype or layout not supported (layout > 1) */
     WTC_EWORKSPACE = -4, /* workspace NULL or smaller than the queried size */
-    WTC_EHIP = -5        /* a HIP launch or runtime call failed */
+    WTC_EHIP = -5,       /* a HIP launch or runtime call failed */
+    WTC_ESCRATCH = -6    /* wtconv_backward_noalloc: the call needs more than
+                            WTCONV_NOALLOC_SCRATCH_BYTES of scratch */
 } wtc_status;
 
 typedef enum { WTC_FP32 = 0, WTC_BF16 = 1 } wtc_dtype;
@@ -112,6 +114,29 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g,
                     void* dx, float* dw0, float* ds0, float* db0,
                     float* dwl, float* dsl,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass that allocates nothing and takes no workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same arguments, results
+ * and checks as wtconv_backward without the workspace pair; the scratch that
+ * wtconv_backward takes from the workspace (the weight-gradient partial
+ * records) is a fixed array of WTCONV_NOALLOC_SCRATCH_BYTES in device memory,
+ * one per GPU, held from the first call on that GPU until the process ends.
+ * Runs on the device current at the call (the one of `stream` and the
+ * tensors).  A call whose wtconv_backward_workspace(d) exceeds the array
+ * returns WTC_ESCRATCH before any HIP call: planes beyond the on-chip
+ * pipeline (above about 128 x 128 at k = 5) and channels-last tensors need
+ * far more.  Nothing in the array has to start at zero (every record is
+ * written before it is read), but all calls on one GPU share it: calls that
+ * overlap in time on one GPU (two streams, or two threads) race and must be
+ * serialised by the caller.  The first call on a device also looks up the
+ * array's device address (hipGetSymbolAddress), which is not an allocation. */
+#define WTCONV_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int wtconv_backward_noalloc(const wtc_desc* d, const void* x, const void* g,
+                            const float* w0, const float* s0,
+                            const float* wl, const float* sl,
+                            void* dx, float* dw0, float* ds0, float* db0,
+                            float* dwl, float* dsl, void* stream);
 
 /* Level-by-level baseline: one kernel per step, every intermediate (bands,
  * convolved bands, partial syntheses) a float32 tensor in the workspace.

@@ -14,6 +14,7 @@ import torch
 __all__ = [
     "WTCError", "load_library", "wtc_desc", "make_desc",
     "wtconv_forward", "wtconv_backward", "wtconv_forward_unfused", "wtconv_backward_unfused",
+    "wtconv_backward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "wtconv_forward_workspace", "wtconv_backward_workspace",
     "wtconv_forward_unfused_workspace", "wtconv_backward_unfused_workspace",
     "wtconv_io_model_bytes", "wtconv_flops", "wtconv_status_string",
@@ -22,7 +23,8 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwtconv.so")
 
-WTC_OK, WTC_EINVAL, WTC_ESHAPE, WTC_EDTYPE, WTC_EWORKSPACE, WTC_EHIP = 0, -1, -2, -3, -4, -5
+WTC_OK, WTC_EINVAL, WTC_ESHAPE, WTC_EDTYPE, WTC_EWORKSPACE, WTC_EHIP, WTC_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
+NOALLOC_SCRATCH_BYTES = 8 << 20   # WTCONV_NOALLOC_SCRATCH_BYTES in include/wtconv.h
 WTC_FP32, WTC_BF16 = 0, 1
 
 
@@ -67,6 +69,8 @@ def load_library(path=None):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.wtconv_backward_noalloc.restype = ctypes.c_int
+    lib.wtconv_backward_noalloc.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
     lib.wtconv_io_model_bytes.restype = ctypes.c_double
     lib.wtconv_io_model_bytes.argtypes = [_D, ctypes.c_int, ctypes.c_int]
     lib.wtconv_flops.restype = ctypes.c_double
@@ -209,8 +213,13 @@ def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace)
     args = [ctypes.byref(d), _ptr(x), _ptr(g), _ptr(w0), _ptr(s0),
             _ptr(wl if L > 0 else None), _ptr(sl if L > 0 else None), _ptr(dx),
             _ptr(grads["dw0"]), _ptr(grads["ds0"]), _ptr(grads["db0"]), _ptr(grads["dwl"]), _ptr(grads["dsl"])]
-    ws, wsb = _workspace(getattr(lib, ws_name)(ctypes.byref(d)), x.device, workspace)
-    st = getattr(lib, fn_name)(*args, _ptr(ws), wsb, _stream(x.device))
+    if ws_name is None:
+        # no workspace: the library's fixed scratch array of the current device
+        with torch.cuda.device(x.device):
+            st = getattr(lib, fn_name)(*args, _stream(x.device))
+    else:
+        ws, wsb = _workspace(getattr(lib, ws_name)(ctypes.byref(d)), x.device, workspace)
+        st = getattr(lib, fn_name)(*args, _ptr(ws), wsb, _stream(x.device))
     if st != WTC_OK:
         raise WTCError(st, fn_name)
     out = dict(grads)
@@ -233,6 +242,13 @@ def wtconv_backward(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None
     """Returns dict(dx, dw0, ds0, db0, dwl, dsl) for upstream gradient g (fused kernels)."""
     return _bwd_common("wtconv_backward", "wtconv_backward_workspace", x, g, w0, s0, wl, sl, L, dx, grads,
                        workspace)
+
+
+def wtconv_backward_noalloc(x, g, w0, s0, wl, sl, L, dx=None, grads=None):
+    """:func:`wtconv_backward` without a workspace: the library allocates
+    nothing (its scratch is a fixed per-GPU array of NOALLOC_SCRATCH_BYTES).
+    Pass dx and grads to have no allocation on this side either."""
+    return _bwd_common("wtconv_backward_noalloc", None, x, g, w0, s0, wl, sl, L, dx, grads, None)
 
 
 def wtconv_backward_unfused(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None):

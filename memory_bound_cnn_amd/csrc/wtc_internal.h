@@ -283,6 +283,11 @@ int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, con
                      float* dw0, float* ds0, float* db0, float* dwl, float* dsl, char* ws,
                      void* stream, int stage = 0, const float* zext = nullptr);
 int launch_fill_zero(float* p, int n, void* stream);
+// Argument checks of the backward entry points (descriptor, then pointers):
+// WTC_OK or the status the entry point returns, before any HIP call.
+int backward_check(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
+                   const float* wl, const float* sl, const void* dx, const float* dw0, const float* ds0,
+                   const float* db0, const float* dwl, const float* dsl);
 // [batch][rows][cols] -> [batch][cols][rows], elements of esize (4 or 2) bytes
 int launch_transpose(const void* src, void* dst, int batch, int rows, int cols, int esize, void* stream);
 

@@ -571,6 +571,17 @@ double io_fused(const wtc_desc* d, int dir, int depth) {
 }
 
 }  // namespace
+
+int backward_check(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
+                   const float* wl, const float* sl, const void* dx, const float* dw0, const float* ds0,
+                   const float* db0, const float* dwl, const float* dsl) {
+    const int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
+    if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
+    return WTC_OK;
+}
+
 }  // namespace wtc
 
 using namespace wtc;
@@ -585,6 +596,7 @@ const char* wtconv_status_string(int s) {
         case WTC_EDTYPE: return "unsupported dtype or layout";
         case WTC_EWORKSPACE: return "workspace missing or too small";
         case WTC_EHIP: return "HIP launch or runtime error";
+        case WTC_ESCRATCH: return "needs more scratch than the fixed no-allocation buffer holds";
         default: return "unknown status";
     }
 }
@@ -624,10 +636,8 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
                     const float* s0, const float* wl, const float* sl, void* dx, float* dw0,
                     float* ds0, float* db0, float* dwl, float* dsl, void* workspace,
                     size_t workspace_bytes, void* stream) {
-    int st = check_desc(d);
+    const int st = backward_check(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl);
     if (st != WTC_OK) return st;
-    if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
-    if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
     if (d->layout == 1)
         return nhwc_backward(d, false, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
                              static_cast<char*>(workspace), workspace_bytes, stream);

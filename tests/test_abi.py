@@ -76,7 +76,7 @@ def test_backward_workspace_checked():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert binding.wtconv_status_string(s)
     assert "unknown" in binding.wtconv_status_string(42)
 
@@ -202,3 +202,33 @@ def test_channels_last_workspace_and_model():
         assert binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction, layout=1) == \
             binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction) + extra * t
     assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=2) == 0
+
+
+def test_noalloc_checks_before_any_hip_call():
+    """wtconv_backward_noalloc: argument checks, then the scratch limit, both
+    before any HIP call (so they hold on a host without a GPU)."""
+    lib = binding.load_library()
+    d = _desc(k=4)
+    args = [FAKE] * 12 + [None]
+    assert lib.wtconv_backward_noalloc(ctypes.byref(d), *args) == binding.WTC_EINVAL
+    d = _desc()
+    assert lib.wtconv_backward_noalloc(ctypes.byref(d), None, *args[1:]) == binding.WTC_EINVAL
+    # a plane beyond the on-chip pipeline needs far more than the fixed array
+    d = _desc(B=8, C=64, H=224, W=224, L=3)
+    assert lib.wtconv_backward_workspace(ctypes.byref(d)) > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.wtconv_backward_noalloc(ctypes.byref(d), *args) == binding.WTC_ESCRATCH
+    # channels-last needs three tensor copies of workspace
+    d = _desc(B=32, C=96, H=64, W=64, L=3, layout=1)
+    assert lib.wtconv_backward_noalloc(ctypes.byref(d), *args) == binding.WTC_ESCRATCH
+    assert binding.wtconv_status_string(binding.WTC_ESCRATCH) != binding.wtconv_status_string(42)
+
+
+def test_noalloc_scratch_covers_the_benchmark_shapes():
+    """The fixed scratch holds the backward partial records of every benchmark
+    workload whose planes the on-chip pipeline holds."""
+    from memory_bound_cnn_amd.inputs import WORKLOADS
+    for w in WORKLOADS.values():
+        for L in (w.sweep or (w.L,)):
+            need = binding.wtconv_backward_workspace(w.B, w.C, w.H, w.W, L, w.k, w.dtype)
+            if w.H <= 128 and w.W <= 128:
+                assert need <= binding.NOALLOC_SCRATCH_BYTES, (w.name, L, need)
