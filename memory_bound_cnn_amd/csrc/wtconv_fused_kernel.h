@@ -46,6 +46,7 @@
 #include <type_traits>
 
 #include "wtc_internal.h"
+#include "wtc_numeric.h"
 
 namespace wtc {
 namespace fused_detail {
@@ -61,12 +62,7 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v.bits) << 16); }
 
 __device__ __forceinline__ void from_f32(float& d, float v) { d = v; }
-__device__ __forceinline__ void from_f32(bf16_t& d, float v) {
-    // round to nearest, ties to even (finite inputs)
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    d.bits = (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ void from_f32(bf16_t& d, float v) { d.bits = bf16_rne(v); }
 
 // Four consecutive pixels (the caller guarantees 4-pixel alignment).
 __device__ __forceinline__ void load4(const float* p, float (&v)[4]) {
@@ -166,21 +162,7 @@ template <int R, class G>
 __device__ __forceinline__ void zero_rings(float* lds, const G& g, int off, int astride, int na, int rows, int S, int h, int w,
                            int tid, int nthr);
 
-// Integer division of 0 <= e < 2^16 by a loop-invariant 1 <= d <= 4096 with a
-// biased float reciprocal (exact in that range: checked exhaustively on the
-// host, including a reciprocal one ulp off).  Three full-rate VALU ops instead
-// of the ~15-op integer division sequence.
-struct FastDiv {
-    int d;
-    float r;
-};
-__device__ __forceinline__ FastDiv make_div(int d) {
-    FastDiv f;
-    f.d = d;
-    f.r = (1.0f / (float)d) * 1.0000076f;  // 1 + 2^-17
-    return f;
-}
-__device__ __forceinline__ int fdiv(int e, const FastDiv& f) { return (int)((float)e * f.r); }
+// (FastDiv, make_div, fdiv: integer division by a float reciprocal, wtc_numeric.h)
 
 template <int R, class G>
 __device__ __forceinline__ void zero_rings(float* lds, const G& g, int off, int astride, int na, int rows, int S, int h, int w,

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 
 #include "wtc_internal.h"
+#include "wtc_numeric.h"
 
 namespace wtc {
 namespace {
@@ -39,11 +40,7 @@ struct bf16v {
 __device__ __forceinline__ float lval(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ float lval(const bf16v* p, size_t i) { return __uint_as_float(((uint32_t)p[i].bits) << 16); }
 __device__ __forceinline__ void lput(float* p, size_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void lput(bf16v* p, size_t i, float v) {
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite values)
-    p[i].bits = (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ void lput(bf16v* p, size_t i, float v) { p[i].bits = bf16_rne(v); }
 
 // Value of v in lane l - N of the same 16-lane row (0 for the row's first N lanes).
 template <int N>

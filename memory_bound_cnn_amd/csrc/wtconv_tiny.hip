@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include "wtc_internal.h"
+#include "wtc_numeric.h"
 
 namespace wtc {
 namespace tiny {
@@ -47,9 +48,7 @@ __device__ __forceinline__ void bstore(rsrc_t r, int off, float v, float*) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
 }
 __device__ __forceinline__ void bstore(rsrc_t r, int off, float v, bf16v*) {
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);   // round to nearest even (finite values)
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(u >> 16), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)bf16_rne(v), r, off, 0, 0);
 }
 
 // Value of `v` in quad lane (lane ^ X); X = 0 is the lane itself.

@@ -17,6 +17,7 @@
 #include <algorithm>
 
 #include "wtc_internal.h"
+#include "wtc_numeric.h"
 
 namespace wtc {
 namespace {
@@ -36,12 +37,7 @@ __device__ __forceinline__ void tld4(const uint16_t* p, uint32_t i, float (&v)[4
     v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xFFFF0000u);
     v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xFFFF0000u);
 }
-__device__ __forceinline__ uint32_t tbf16(float v) {
-    // round to nearest even (finite values)
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+__device__ __forceinline__ uint32_t tbf16(float v) { return bf16_rne(v); }
 __device__ __forceinline__ void tst(float* p, uint32_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void tst(uint16_t* p, uint32_t i, float v) { p[i] = (uint16_t)tbf16(v); }
 __device__ __forceinline__ void tst4(float* p, uint32_t i, const float (&v)[4]) {

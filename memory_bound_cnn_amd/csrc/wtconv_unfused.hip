@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "wtc_internal.h"
+#include "wtc_numeric.h"
 
 namespace wtc {
 namespace {
@@ -37,22 +38,12 @@ __device__ __forceinline__ void stv(float* p, uint32_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void st4(float* p, uint32_t i, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p + i) = make_float4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ uint32_t bf16_bits(float v) {
-    // round to nearest even (finite values)
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
+__device__ __forceinline__ uint32_t bf16_bits(float v) { return bf16_rne(v); }
 __device__ __forceinline__ void st4(uint16_t* p, uint32_t i, const float (&v)[4]) {
     *reinterpret_cast<uint2*>(p + i) = make_uint2(bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
                                                   bf16_bits(v[2]) | (bf16_bits(v[3]) << 16));
 }
-__device__ __forceinline__ void stv(uint16_t* p, uint32_t i, float v) {
-    // round to nearest even (finite values)
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    p[i] = (uint16_t)(u >> 16);
-}
+__device__ __forceinline__ void stv(uint16_t* p, uint32_t i, float v) { p[i] = (uint16_t)bf16_rne(v); }
 
 uint32_t blocks_for(uint64_t n) {
     const uint64_t b = (n + kThreads - 1) / kThreads;
