@@ -240,6 +240,14 @@ constexpr bool tiny_supported(int k, int Hq, int Wq, int L, int Lm) {
 // Unfused (level-by-level) baseline
 // ---------------------------------------------------------------------------
 constexpr int kMaxUnfusedL = 30;   // levels the baseline accepts (grids stay 1x1 beyond log2 size)
+// Large planes of the baseline (both sides >= kUnfusedBigSide) run 64 x 64
+// tiles; its weight-gradient correlations aim at kUnfusedCorrTarget workgroups
+// per launch.  The peeled top level runs kTopTile x kTopTile output tiles.
+constexpr int kUnfusedBigTile = 64;
+constexpr int kUnfusedBigSide = 48;
+constexpr int kUnfusedCorrTarget = 2048;
+constexpr int kTopTile = 64;
+inline bool unfused_big_planes(int h, int w) { return h >= kUnfusedBigSide && w >= kUnfusedBigSide; }
 
 struct UnfusedPlan {
     // workspace offsets in bytes, per level 1..L (float32 tensors)

@@ -1,7 +1,5 @@
 // Host side of libwtconv: argument checks, launch planning, dispatch, and the
 // analytic HBM-traffic model.  See include/wtconv.h for the contract.
-#include <hip/hip_runtime.h>
-
 #include <algorithm>
 #include <cstring>
 

@@ -22,7 +22,7 @@
 namespace wtc {
 namespace {
 
-constexpr int kTop = 64;        // output tile side
+constexpr int kTop = kTopTile;  // output tile side
 constexpr int kTopThreads = 256;
 
 __device__ __forceinline__ float tld(const float* p, uint32_t i) { return p[i]; }
@@ -608,11 +608,6 @@ int top_bwd_t(const wtc_desc* d, const void* x, const void* g, const float* w0, 
 }
 
 }  // namespace
-
-size_t top_records(const wtc_desc* d) {
-    const size_t ntile = (size_t)((d->W + kTop - 1) / kTop) * ((d->H + kTop - 1) / kTop);
-    return (size_t)d->B * ntile * d->C * (d->k * d->k + 1);
-}
 
 int top_backward(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0, const float* wl,
                  const float* sl, const float* dll, void* dx, float* part0, float* part1, void* stream) {

@@ -27,7 +27,6 @@ namespace wtc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCorrTarget = 2048;   // correlation workgroups per launch (before the batch cap)
 
 __device__ __forceinline__ float ldv(const float* p, uint32_t i) { return p[i]; }
 __device__ __forceinline__ float ldv(const uint16_t* p, uint32_t i) {
@@ -341,12 +340,11 @@ __global__ void __launch_bounds__(kThreads) k_tcorr(const TA* __restrict__ A, co
 // block with a register-blocked window (two window rows live, read as 16-byte
 // LDS rows), so a window row of X serves 4 x K multiply-adds per value.
 // ---------------------------------------------------------------------------
-constexpr int kBigTile = 64;
-constexpr int kBigSide = 48;
+constexpr int kBigTile = kUnfusedBigTile;
 
 __host__ __device__ constexpr int big_xs_stride(int R) { return (kBigTile + 2 * R + 3) & ~3; }
 
-bool big_planes(int h, int w) { return h >= kBigSide && w >= kBigSide; }
+bool big_planes(int h, int w) { return unfused_big_planes(h, w); }
 
 // Stage rows [y0, y0 + rows) x columns [x0, x0 + cols) of plane `src` (h x w,
 // zero outside) into lds[r * stride + c]; cols <= 64 + 2 * kMaxK.  Wave v takes
@@ -610,11 +608,6 @@ int launch_corr_finalize(const float* part, int nch, int nblk, int k, const floa
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
-int unfused_corr_blocks(int nb, int nch, int h, int w) {
-    // large planes: units are (batch entry, tile) pairs
-    const int units = big_planes(h, w) ? nb * ((h + kBigTile - 1) / kBigTile) * ((w + kBigTile - 1) / kBigTile) : nb;
-    return std::max(1, std::min(units, (kCorrTarget + nch - 1) / nch));
-}
 
 namespace {
 
@@ -706,53 +699,8 @@ int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
-size_t align256_host(size_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
-
-// Workspace (float32 tensors, 256-byte aligned).  Per level i:
-//   S_i  [B, C, 4, h_i, w_i]       bands of x
-//   Y_i  same shape                forward: scaled conv output;  backward: dS_i
-//   Z_i  [B, C, h_{i-1}, w_{i-1}]  forward: partial synthesis;  backward: dLL_{i-1}
-//   dT_i same shape as S_i         backward only: analysis of g
-// then the correlation partials (backward).
-int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p) {
-    if (d->k > kMaxK) return WTC_ESHAPE;
-    if (d->L > kMaxUnfusedL) return WTC_ESHAPE;
-    const uint64_t BC = (uint64_t)d->B * d->C;
-    // 32-bit element indexing of every tensor (the level-1 bands are the largest)
-    const uint64_t h1 = (d->H + 1) / 2, w1 = (d->W + 1) / 2;
-    if (BC * d->H * d->W >= (1ull << 31) || BC * 4 * h1 * w1 >= (1ull << 31)) return WTC_ESHAPE;
-    p->h[0] = d->H;
-    p->w[0] = d->W;
-    size_t off = 0;
-    for (int i = 1; i <= d->L; ++i) {
-        p->h[i] = (p->h[i - 1] + 1) / 2;
-        p->w[i] = (p->w[i - 1] + 1) / 2;
-        const size_t n4 = BC * 4 * p->h[i] * p->w[i] * sizeof(float);
-        const size_t nz = BC * p->h[i - 1] * p->w[i - 1] * sizeof(float);
-        p->s_off[i] = off;
-        off += align256_host(n4);
-        p->y_off[i] = off;
-        off += align256_host(n4);
-        p->z_off[i] = off;
-        off += align256_host(nz);
-        if (bwd) {
-            p->dt_off[i] = off;
-            off += align256_host(n4);
-        }
-    }
-    p->part_off = off;
-    if (bwd) {
-        const int kk1 = d->k * d->k + 1;
-        size_t np = (size_t)unfused_corr_blocks(d->B, d->C, d->H, d->W) * d->C * kk1;
-        for (int i = 1; i <= d->L; ++i)
-            np = std::max(np, (size_t)unfused_corr_blocks(d->B, 4 * d->C, p->h[i], p->w[i]) * 4 * d->C * kk1);
-        off += align256_host(np * sizeof(float));
-    }
-    p->total = off;
-    return WTC_OK;
-}
 
 namespace {
 
