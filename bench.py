@@ -1,18 +1,25 @@
 """Benchmark of the fused WTConv forward + backward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--impl fused|unfused]
-                    [--no-cpu-baseline] [--no-summary]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--level L]
+                    [--impl fused|unfused] [--no-cpu-baseline] [--no-summary]
 
 One step = one wtconv_forward + one wtconv_backward (every kernel of the hot
 path) over one batch of synthetic, seeded inputs already resident in HBM.
 Input buffer sets are rotated so that the working set of consecutive steps
 exceeds the 256 MB Infinity Cache.  Prints ONE JSON line.
 
-value  = achieved HBM throughput of the step in GB/s: the fused I/O model's
-         algorithmic bytes (forward: read x, write out; backward: read x and g,
-         write dx; plus parameters and partial sums) / measured step time.
-roofline = the dominant call (the backward pass) against the VALU peak it is
-         bound by, timed live with HIP events on the launch stream.
+Default workload: the level sweep block, B=64, C=96, 128 x 128, k=5, fp32, at
+L=3 (the largest single-GPU configuration; the other levels and every other
+workload are timed in `per_workload`).
+
+value    = achieved HBM throughput of the step in GB/s: the fused I/O model's
+           bytes (forward: read x, write out; backward: read x and g, write
+           dx; plus parameters and partial sums) / measured step time.
+roofline = the dominant call, wtconv_backward (the fused backward kernel and
+           its small finalize), against the 8 TB/s HBM peak: algorithmic bytes
+           per call (3 e N: read x and g, write dx) / its duration, timed live
+           with HIP events on the launch stream over the timed steps; beside
+           it the same call against the VALU peaks.
 cpu_baseline = the float64 CPU oracle on the host's cores (a baseline, not a target).
 """
 
@@ -29,12 +36,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-# fp32 VALU peak without packed-FP32 instructions: 256 CUs x 4 SIMDs x 16 lanes
-# x 2 flop (FMA) x 2.4 GHz.  (Packed FP32 FMA doubles this to 157.3 TFLOP/s;
-# the library is built with packed-FP32 instructions disabled.)
+# Published fp32 vector peak of MI355X (packed FP32 FMA): 157.3 TFLOP/s.  The
+# library is built with packed-FP32 instructions disabled, so the peak its
+# code can reach is half of it: 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA)
+# x 2.4 GHz = 78.6 TFLOP/s.
+VALU_PACKED_PEAK_TFLOPS = 157.3
 VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
-VALU_PACKED_PEAK_TFLOPS = 2 * VALU_PEAK_TFLOPS
-HEADLINE = "stage1_b32c96_64x64_L3"
+HEADLINE = "sweep_b64c96_128x128"
+HEADLINE_L = 3
 MALL_BYTES = 256 * 2 ** 20
 COPY_PROBE_MIB = 1024
 
@@ -52,18 +61,26 @@ def parse():
     p.add_argument("--torch-dwconv", action="store_true",
                    help="also time PyTorch's depthwise k x k convolution (MIOpen) at the headline shape")
     p.add_argument("--profile-steps", type=int, default=None,
-                   help="run only this many steps, no summary / CPU baseline (for rocprofv3)")
+                   help="run only this many calls, no summary / CPU baseline (for rocprofv3)")
+    p.add_argument("--profile-only", default="both", choices=["both", "fwd", "bwd"],
+                   help="with --profile-steps: call only the forward or only the backward entry point, so "
+                        "that every library kernel of the run belongs to that direction")
     p.add_argument("--copy-probe-mib", type=int, default=None,
                    help="run a plain device copy (read N + write N bytes) 3 times, to calibrate "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known traffic")
     p.add_argument("--stats-summary", nargs=2, metavar=("PROFILE_DIR", "OUT_TXT"), default=None,
                    help="format the kernel_stats.csv of a rocprofv3 --kernel-trace --stats --output-format csv "
                         "run as a text summary (no GPU needed)")
-    p.add_argument("--pmc-summary", nargs=5, default=None,
-                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "OUT_TXT"),
-                   help="turn FETCH_SIZE / WRITE_SIZE counter runs of --profile-steps and of --copy-probe-mib "
-                        "into calibrated HBM bytes per launch: writes OUT_TXT and profiles/pmc_traffic.json")
+    p.add_argument("--pmc-summary", nargs=7, default=None,
+                   metavar=("FWD_FETCH_DIR", "FWD_WRITE_DIR", "BWD_FETCH_DIR", "BWD_WRITE_DIR", "COPY_FETCH_DIR",
+                            "COPY_WRITE_DIR", "OUT_TXT"),
+                   help="turn FETCH_SIZE / WRITE_SIZE counter runs of --profile-steps --profile-only fwd|bwd and "
+                        "of --copy-probe-mib into calibrated HBM bytes per call: writes OUT_TXT and "
+                        "profiles/pmc_traffic.json")
     p.add_argument("--cmd", default="", help="command line recorded in a summary")
+    p.add_argument("--source-hash", default=None,
+                   help="with --pmc-summary: the kernel-source hash the profiled run printed (default: the "
+                        "current sources')")
     return p.parse_args()
 
 
@@ -119,15 +136,18 @@ class Runner:
         self.ws_b = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
         self.N, self.e = N, e
 
-    def step(self, i, ev=None):
+    def step(self, i, ev=None, only="both"):
         s = self.sets[i % self.R]
         if ev is not None:
             ev[0].record()
-        self.fwd(s["x"], self.w0, self.s0, self.b0, self.wl_, self.sl_, self.L, out=s["out"], workspace=self.ws_f)
+        if only != "bwd":
+            self.fwd(s["x"], self.w0, self.s0, self.b0, self.wl_, self.sl_, self.L, out=s["out"],
+                     workspace=self.ws_f)
         if ev is not None:
             ev[1].record()
-        self.bwd(s["x"], s["g"], self.w0, self.s0, self.wl_, self.sl_, self.L, dx=s["dx"], grads=self.grads,
-                 workspace=self.ws_b)
+        if only != "fwd":
+            self.bwd(s["x"], s["g"], self.w0, self.s0, self.wl_, self.sl_, self.L, dx=s["dx"], grads=self.grads,
+                     workspace=self.ws_b)
         if ev is not None:
             ev[2].record()
 
@@ -244,22 +264,31 @@ def _oracle_task(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
-    """Time the float64 oracle (forward + backward) on a bounded sample of the
-    workload: whole batch entries, one per task, in a pool of host processes,
-    about `budget_s` seconds of CPU work in total (the batch is cycled through
-    when one pass over it is shorter than that)."""
-    from memory_bound_cnn_amd.inputs import workload_inputs
+def host_cores():
+    """Host cores this process may use, capped at the 16 host CPUs a one-GPU
+    share of the box provides (whatever the affinity mask lists)."""
     try:
         ncpu = len(os.sched_getaffinity(0))
     except AttributeError:
         ncpu = os.cpu_count() or 1
-    cores = max(1, min(16, ncpu))
+    return max(1, min(16, ncpu)), ncpu
+
+
+def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
+    """Time the float64 oracle (forward + backward) on a bounded sample of the
+    workload: whole batch entries, one per task, on a pool of host processes
+    (one per usable core, one thread each), about `budget_s` seconds of CPU
+    work in total (the batch is cycled through when one pass over it is
+    shorter than that).  Also the warm one-core time of one entry (after a
+    first call has paid the imports and page faults)."""
+    from memory_bound_cnn_amd.inputs import workload_inputs
+    cores, ncpu = host_cores()
     d = workload_inputs(wl)
     wl_ = d["wl"][:L] if L > 0 else None
     sl_ = d["sl"][:L] if L > 0 else None
     task = lambda b: (d["x"][b:b + 1], d["g"][b:b + 1], d["w0"], d["s0"], d["b0"], wl_, sl_, L)
-    t1 = _oracle_task(task(0))                      # one entry, one core: sizes the sample
+    _oracle_task(task(0))                           # cold call: imports, page faults
+    t1 = _oracle_task(task(1 % wl.B))               # warm: one entry, one core
     n_entries = int(max(cores, math.ceil(budget_s / max(t1, 1e-3))))
     ctx = mp.get_context("spawn")
     with ctx.Pool(cores) as pool:
@@ -269,11 +298,13 @@ def cpu_baseline(wl, L, bytes_per_batch_entry, budget_s=20.0):
         wall = time.perf_counter() - t0
     value = n_entries * bytes_per_batch_entry / wall / 1e9
     return dict(value=value, unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{n_entries} batch entries (the {wl.B} of {wl.name}, L={L}, cycled; about {budget_s:.0f} s "
-                       f"of CPU work): float64 NumPy oracle, forward + backward, one batch entry per task on a "
-                       f"pool of {cores} processes (1 thread each); wall {wall:.2f} s; one entry on one core "
-                       f"{t1:.3f} s",
-                wall_s=round(wall, 3), entries=n_entries)
+                sample=f"{n_entries} batch entries of {wl.name} at L={L} (B={wl.B}; entries cycled), "
+                       f"{n_entries * t1:.0f} s of CPU work at the warm one-core rate: float64 NumPy oracle, forward + "
+                       f"backward, one batch entry per task on a pool of {cores} processes (1 thread each; affinity "
+                       f"lists {ncpu} CPUs, a one-GPU share is 16); wall {wall:.2f} s",
+                wall_s=round(wall, 3), entries=n_entries,
+                one_core=dict(value=round(bytes_per_batch_entry / t1 / 1e9, 4), unit="GB/s",
+                              seconds_per_entry=round(t1, 3)))
 
 
 # ---------------------------------------------------------------------------
@@ -300,16 +331,10 @@ def _col(row, *names):
     raise KeyError(names)
 
 
-def kernel_role(name):
-    """'fwd' / 'bwd' for the fused kernels, None for anything else."""
-    import re
-    if "wtc_finalize_kernel" in name:
-        return "bwd"
-    m = re.search(r"wtc_fused_kernel<\s*\d+\s*,[^,]+,\s*(true|false)", name) or \
-        re.search(r"wtc_tiny_kernel<[^,]+,\s*(true|false)", name)
-    if m:
-        return "bwd" if m.group(1) == "true" else "fwd"
-    return None
+def is_library_kernel(name):
+    """Kernels of libwtconv (namespace wtc); torch's own set-up kernels and
+    runtime copies are not."""
+    return "wtc::" in name
 
 
 def _short(name, n=96):
@@ -331,48 +356,59 @@ def stats_summary(prof_dir, out_txt, cmd):
     print("\n".join(lines))
 
 
-def _pmc_avg(d, counter):
-    """Average counter value (KiB) per dispatch, per kernel name."""
+def _pmc_totals(d, counter):
+    """Per kernel name: (sum of the counter over its dispatches in KiB, dispatches)."""
     acc = {}
     for r in _rows(_find_csv(d, "counter_collection.csv")):
         if _col(r, "Counter_Name", "counter_name") != counter:
             continue
         k = _col(r, "Kernel_Name", "kernel_name")
-        acc.setdefault(k, []).append(float(_col(r, "Counter_Value", "value")))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+        v = acc.setdefault(k, [0.0, 0])
+        v[0] += float(_col(r, "Counter_Value", "value"))
+        v[1] += 1
+    return acc
 
 
-def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_txt, cmd, wl_name, L):
+def pmc_summary(dirs, out_txt, cmd, wl_name, L, source_hash=None):
+    """Calibrated HBM bytes per call of each direction from FETCH_SIZE and
+    WRITE_SIZE runs (one counter per run) that called only that direction.
+    Every library kernel of such a run belongs to the direction; the calls
+    are counted as the fewest dispatches of any library kernel (each kernel
+    of a call runs at least once per call)."""
     from memory_bound_cnn_amd.inputs import WORKLOADS
-    fetch, write = _pmc_avg(fetch_dir, "FETCH_SIZE"), _pmc_avg(write_dir, "WRITE_SIZE")
-    cf, cw = _pmc_avg(cfetch_dir, "FETCH_SIZE"), _pmc_avg(cwrite_dir, "WRITE_SIZE")
-    # the copy probe's kernel is the one elementwise kernel moving the most bytes
-    ck = max(cf, key=lambda k: cf[k])
+    fwd_f, fwd_w, bwd_f, bwd_w, cfetch_dir, cwrite_dir = dirs
+    cf, cw = _pmc_totals(cfetch_dir, "FETCH_SIZE"), _pmc_totals(cwrite_dir, "WRITE_SIZE")
+    # the copy probe's kernel is the kernel moving the most bytes per dispatch
+    ck = max(cf, key=lambda k: cf[k][0] / cf[k][1])
     copy_bytes = float(COPY_PROBE_MIB * 2 ** 20)
-    f_fac = copy_bytes / (cf[ck] * 1024.0)
-    w_fac = copy_bytes / (cw[ck] * 1024.0)
+    f_fac = copy_bytes / (cf[ck][0] / cf[ck][1] * 1024.0)
+    w_fac = copy_bytes / (cw[ck][0] / cw[ck][1] * 1024.0)
     wl = WORKLOADS[wl_name]
     shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
-    tot = {"fwd": 0.0, "bwd": 0.0}
-    per_kernel = {}
-    for k in sorted(set(fetch) | set(write)):
-        role = kernel_role(k)
-        if role is None:
-            continue
-        rb = fetch.get(k, 0.0) * 1024.0 * f_fac
-        wb = write.get(k, 0.0) * 1024.0 * w_fac
-        tot[role] += rb + wb
-        per_kernel[_short(k)] = {"role": role, "read_bytes": rb, "write_bytes": wb,
-                                 "fetch_kib_raw": fetch.get(k), "write_kib_raw": write.get(k)}
+    tot, per_kernel = {}, {}
+    for role, fd, wd in (("fwd", fwd_f, fwd_w), ("bwd", bwd_f, bwd_w)):
+        fetch = {k: v for k, v in _pmc_totals(fd, "FETCH_SIZE").items() if is_library_kernel(k)}
+        write = {k: v for k, v in _pmc_totals(wd, "WRITE_SIZE").items() if is_library_kernel(k)}
+        calls_f = min(v[1] for v in fetch.values())
+        calls_w = min(v[1] for v in write.values())
+        rb = sum(v[0] for v in fetch.values()) * 1024.0 * f_fac / calls_f
+        wb = sum(v[0] for v in write.values()) * 1024.0 * w_fac / calls_w
+        tot[role] = rb + wb
+        for k in sorted(set(fetch) | set(write)):
+            fv, wv = fetch.get(k, (0.0, 1)), write.get(k, (0.0, 1))
+            per_kernel[f"{role}: {_short(k)}"] = {
+                "read_bytes_per_call": fv[0] * 1024.0 * f_fac / calls_f,
+                "write_bytes_per_call": wv[0] * 1024.0 * w_fac / calls_w,
+                "dispatches_per_call": fv[1] / calls_f}
     from memory_bound_cnn_amd import binding
     model = {"fwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=0),
              "bwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=1)}
-    rec = {"source_hash": kernel_source_hash(), "command": cmd,
+    rec = {"source_hash": source_hash or kernel_source_hash(),
            "calibration": {"copy_kernel": _short(ck), "copy_bytes_each_way": copy_bytes,
                            "fetch_factor": f_fac, "write_factor": w_fac},
            "workloads": {f"{wl_name}_L{L}": {"fwd_bytes": tot["fwd"], "bwd_bytes": tot["bwd"],
                                              "model_fwd_bytes": model["fwd"], "model_bwd_bytes": model["bwd"],
-                                             "kernels": per_kernel}}}
+                                             "command": cmd, "kernels": per_kernel}}}
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     old = {}
     if os.path.exists(path):
@@ -384,14 +420,15 @@ def pmc_summary(fetch_dir, write_dir, cfetch_dir, cwrite_dir, out_txt, cmd, wl_n
         old["workloads"].update(rec["workloads"])
         rec["workloads"] = old["workloads"]
     json.dump(rec, open(path, "w"), indent=1)
-    lines = ["# rocprofv3 FETCH_SIZE / WRITE_SIZE per dispatch, calibrated against a plain copy",
+    lines = ["# rocprofv3 FETCH_SIZE / WRITE_SIZE per call, calibrated against a plain copy",
              f"# command: {cmd}", "",
              f"copy probe: {_short(ck)} moving {copy_bytes:.0f} B each way; FETCH_SIZE reads "
-             f"{cf[ck]:.1f} KiB -> factor {f_fac:.4f}; WRITE_SIZE reads {cw[ck]:.1f} KiB -> factor {w_fac:.4f}",
+             f"{cf[ck][0] / cf[ck][1]:.1f} KiB -> factor {f_fac:.4f}; WRITE_SIZE reads "
+             f"{cw[ck][0] / cw[ck][1]:.1f} KiB -> factor {w_fac:.4f}",
              f"workload {wl_name} L={L}", ""]
     for k, v in per_kernel.items():
-        lines.append(f"{k:96s} {v['role']}: FETCH {v['fetch_kib_raw']} KiB, WRITE {v['write_kib_raw']} KiB "
-                     f"-> read {v['read_bytes'] / 1e6:.2f} MB, write {v['write_bytes'] / 1e6:.2f} MB")
+        lines.append(f"{k:104s} x{v['dispatches_per_call']:.0f}/call: read {v['read_bytes_per_call'] / 1e6:9.2f} MB, "
+                     f"write {v['write_bytes_per_call'] / 1e6:9.2f} MB")
     for r in ("fwd", "bwd"):
         lines.append(f"{r}: measured {tot[r] / 1e6:.2f} MB per call vs I/O model {model[r] / 1e6:.2f} MB "
                      f"(ratio {tot[r] / model[r]:.3f})")
@@ -427,12 +464,12 @@ def main():
     from memory_bound_cnn_amd.inputs import WORKLOADS
     binding.load_library()
     wl = WORKLOADS[a.workload]
-    L = wl.L if a.level is None else a.level
+    L = (HEADLINE_L if wl.name == HEADLINE else wl.L) if a.level is None else a.level
     if a.stats_summary:
         stats_summary(a.stats_summary[0], a.stats_summary[1], a.cmd)
         return
     if a.pmc_summary:
-        pmc_summary(*a.pmc_summary, a.cmd, wl.name, L)
+        pmc_summary(a.pmc_summary[:6], a.pmc_summary[6], a.cmd, wl.name, L, a.source_hash)
         return
     shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
     io_f = binding.wtconv_io_model_bytes(*shp, impl=0, direction=0)
@@ -462,8 +499,11 @@ def main():
 
     if a.profile_steps is not None:
         r = Runner(wl, L, a.impl, torch, binding)
-        r.time(a.profile_steps, 2)
-        print(json.dumps({"profile_run": wl.name, "L": L, "impl": a.impl, "steps": a.profile_steps}))
+        for i in range(a.profile_steps):
+            r.step(i, only=a.profile_only)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_run": wl.name, "L": L, "impl": a.impl, "calls": a.profile_steps,
+                          "only": a.profile_only, "source_hash": kernel_source_hash()}))
         return
 
     r = Runner(wl, L, a.impl, torch, binding)
@@ -496,21 +536,35 @@ def main():
         "buffer_sets_rotated": r.R,
     }
     tr = traffic_from_profiles(wl, L)
+    # dominant call: wtconv_backward; algorithmic bytes per call = 3 e N
+    alg_b = 3.0 * r.e * r.N
+    alg_f = 2.0 * r.e * r.N
+    gbps_b = alg_b / (bwd_ms * 1e-3) / 1e9
+    gbps_f = alg_f / (fwd_ms * 1e-3) / 1e9
     line["roofline"] = {
-        "bound": "alu",
-        "kernel": "wtconv_backward (fused backward kernel + finalize), the dominant call",
-        "achieved": round(tflops_b, 3),
-        "peak": round(VALU_PEAK_TFLOPS, 1),
-        "unit": "TFLOP/s",
-        "frac": round(tflops_b / VALU_PEAK_TFLOPS, 4),
+        "bound": "hbm",
+        "kernel": "wtconv_backward: the fused backward kernel and its finalize (the dominant call of the step)",
+        "achieved": round(gbps_b, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(gbps_b / HBM_PEAK_GBPS, 4),
         "traffic": tr["bwd_bytes"] if tr else None,
-        "peak_packed_fp32": round(VALU_PACKED_PEAK_TFLOPS, 1),
-        "algorithmic_flops_per_launch": fl_b,
+        "algorithmic_bytes_per_launch": alg_b,
+        "algorithmic_bytes_per_pixel": 3 * r.e,
+        "pixels_per_launch": r.N,
         "launch_ms": round(bwd_ms, 5),
-        "hbm_gbps_of_kernel": round(io_b / (bwd_ms * 1e-3) / 1e9, 1),
-        "forward": {"achieved": round(tflops_f, 3), "frac": round(tflops_f / VALU_PEAK_TFLOPS, 4),
-                    "hbm_gbps": round(io_f / (fwd_ms * 1e-3) / 1e9, 1),
-                    "traffic": tr["fwd_bytes"] if tr else None},
+        "timing": "HIP events on the launch stream around each wtconv_backward call of the timed steps, averaged",
+        "alu": {"achieved_tflops": round(tflops_b, 3),
+                "frac_of_published_fp32_peak": round(tflops_b / VALU_PACKED_PEAK_TFLOPS, 4),
+                "published_fp32_peak_tflops": VALU_PACKED_PEAK_TFLOPS,
+                "frac_of_nonpacked_peak": round(tflops_b / VALU_PEAK_TFLOPS, 4),
+                "nonpacked_peak_tflops": round(VALU_PEAK_TFLOPS, 1),
+                "note": "the library is built without packed-FP32 instructions, so 78.6 TFLOP/s is the "
+                        "highest VALU rate its code can reach"},
+        "forward": {"achieved": round(gbps_f, 1), "frac": round(gbps_f / HBM_PEAK_GBPS, 4),
+                    "launch_ms": round(fwd_ms, 5), "algorithmic_bytes_per_launch": alg_f,
+                    "traffic": tr["fwd_bytes"] if tr else None,
+                    "alu_frac_of_nonpacked_peak": round(tflops_f / VALU_PEAK_TFLOPS, 4)},
     }
     if tr:
         line["measured_bytes_over_model"] = {"fwd": tr["fwd_bytes"] / io_f, "bwd": tr["bwd_bytes"] / io_b}
@@ -540,6 +594,14 @@ def main():
                                  "gbps_fused_model": round(model / (m * 1e-3) / 1e9, 1),
                                  "pct_hbm_peak": round(100 * model / (m * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                                  "pct_valu_peak": round(100 * fl / (m * 1e-3) / 1e12 / VALU_PEAK_TFLOPS, 2)}
+                trw = traffic_from_profiles(ww, Lw)
+                if trw and "ms" in row.get("fused", {}):
+                    mf_ = binding.wtconv_io_model_bytes(*sh, impl=0, direction=0)
+                    mb_ = binding.wtconv_io_model_bytes(*sh, impl=0, direction=1)
+                    row["fused"]["measured_bytes_over_model"] = {"fwd": round(trw["fwd_bytes"] / mf_, 4),
+                                                                 "bwd": round(trw["bwd_bytes"] / mb_, 4)}
+                    row["fused"]["gbps_measured_bytes"] = round(
+                        (trw["fwd_bytes"] + trw["bwd_bytes"]) / (row["fused"]["ms"] * 1e-3) / 1e9, 1)
                 if "ms" in row.get("fused", {}) and "ms" in row.get("unfused", {}):
                     row["speedup_vs_unfused"] = round(row["unfused"]["ms"] / row["fused"]["ms"], 3)
                     row["unfused_model_bytes"] = binding.wtconv_io_model_bytes(*sh, impl=1, direction=0) + \
