@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
     WTC_OK = 0,
     WTC_EINVAL = -1,     /* null pointer, k even or < 1, L < 0, B/C/H/W < 1, bad impl/dir */
-    WTC_ESHAPE = -2,     /* k > 7, or a tensor of 2^31 elements or more */
+    WTC_ESHAPE = -2,     /* k > 31, or a tensor of 2^31 elements or more */
     WTC_EDTYPE = -3,     /* dtype or layout not supported (layout > 1) */
     WTC_EWORKSPACE = -4, /* workspace NULL or smaller than the queried size */
     WTC_EHIP = -5,       /* a HIP launch or runtime call failed */
@@ -70,7 +70,7 @@ typedef enum { WTC_FP32 = 0, WTC_BF16 = 1 } wtc_dtype;
 typedef struct {
     int B, C, H, W; /* batch, channels, height, width (all >= 1)              */
     int L;          /* wavelet levels (>= 0)                                  */
-    int k;          /* kernel size (odd, 1..7 on the fused path)              */
+    int k;          /* kernel size: odd, 1..31 (fused kernels for k <= 7)     */
     int dtype;      /* wtc_dtype: storage type of x / out / g / dx           */
     int layout;     /* 0 = NCHW, 1 = channels-last (NHWC)                     */
 } wtc_desc;
@@ -85,6 +85,11 @@ size_t wtconv_forward_workspace(const wtc_desc* d);
 
 /* Forward pass: out = WTConv(x).  `workspace` may be NULL when the queried
  * size is 0.
+ * Kernel sizes 9..31 have no fused kernels (their k^2 weights and correlation
+ * accumulators per lane exceed the register file): such calls run the
+ * level-by-level kernels below with the taps looped at run time, and the
+ * workspace queries and the I/O model count that path.  Same results, same
+ * contract.
  * Planes beyond the on-chip pipeline: the levels >= 2 of the operator are the
  * operator itself (one level fewer, no base conv) applied to the level-1 LL
  * band, so the LL band (half the size per side) runs recursively through this
@@ -141,7 +146,7 @@ int wtconv_backward_noalloc(const wtc_desc* d, const void* x, const void* g,
 /* Level-by-level baseline: one kernel per step, every intermediate (bands,
  * convolved bands, partial syntheses) a float32 tensor in the workspace.
  * Same arguments and results as above.  It accepts any plane size but
- * returns WTC_ESHAPE for k > 7, L > 30, or tensors of 2^31 elements or more
+ * returns WTC_ESHAPE for k > 31, L > 30, or tensors of 2^31 elements or more
  * (32-bit indexing).  Its weight-gradient reduction is also deterministic.
  * The forward workspace is 0 bytes when L == 0. */
 size_t wtconv_forward_unfused_workspace(const wtc_desc* d);
@@ -158,15 +163,26 @@ int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Analytic model of device-memory (HBM) traffic in bytes for one call:
- * impl 0 = fused, 1 = unfused; dir 0 = forward, 1 = backward.
+ * impl 0 = fused, 1 = unfused; dir 0 = forward, 1 = backward.  The pages
+ * build an I/O model of WTConv to show where its time goes ("Fast and
+ * Memory-Efficient Wavelet Convolutions via I/O-Aware Reformulation", arXiv
+ * 2608.10805, Abstract); their equations are not given, so this model is the
+ * library's own: every tensor counted once per kernel that reads or writes it
+ * (fused forward 2 N e, backward 3 N e, plus parameters and partial records;
+ * the level-by-level path adds every band and partial synthesis).
  * Returns a negative value for an invalid descriptor or impl/dir. */
 double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir);
 
 /* Algorithmic floating-point operations of one call (an FMA counts 2),
- * dir 0 = forward, 1 = backward; negative for an invalid descriptor. */
+ * dir 0 = forward, 1 = backward; negative for an invalid descriptor.  Counted
+ * from the operator's definition (same Abstract): the base k x k depthwise
+ * convolution, per level the four subband k x k convolutions and the 2 x 2
+ * analysis and synthesis butterflies; the backward repeats the convolutions
+ * for dx and once more for the weight-gradient correlations, plus the analysis
+ * of x. */
 double wtconv_flops(const wtc_desc* d, int dir);
 
-/* Static description of a status code. */
+/* Static description of a status code (library convention, no passage). */
 const char* wtconv_status_string(int status);
 
 #ifdef __cplusplus

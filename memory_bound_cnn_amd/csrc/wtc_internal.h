@@ -10,7 +10,8 @@
 namespace wtc {
 
 constexpr int kMaxLm = 7;   // levels evaluated on a grid larger than 1x1 (planes <= 128)
-constexpr int kMaxK = 7;
+constexpr int kMaxK = 7;       // largest kernel size of the fused and the unrolled kernels
+constexpr int kMaxKAny = 31;   // largest kernel size at all (runtime-size level-by-level kernels)
 
 // LDS layout of one plane slot (all offsets and sizes in floats).
 // Without band overlap: [level-1 .. level-early bands][level-0 plane | later

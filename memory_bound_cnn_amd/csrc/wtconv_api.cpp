@@ -278,7 +278,16 @@ int peel_plan(const wtc_desc* d, bool bwd, int depth, PeelPlan* pp) {
     return WTC_OK;
 }
 
+// Kernel sizes beyond the fused kernels (k > kMaxK) run the level-by-level
+// kernels with the taps looped at run time: same results, same contract.
+bool beyond_fused_k(const wtc_desc* d) { return d->k > kMaxK; }
+
 size_t fused_fwd_ws(const wtc_desc* d, int depth, int* st) {
+    if (beyond_fused_k(d)) {
+        UnfusedPlan u;
+        *st = unfused_plan(d, 0, &u);
+        return *st == WTC_OK ? u.total : 0;
+    }
     FusedPlan p;
     *st = plan_fused(d, false, &p);
     if (*st == WTC_OK) return 0;
@@ -289,6 +298,11 @@ size_t fused_fwd_ws(const wtc_desc* d, int depth, int* st) {
 }
 
 size_t fused_bwd_ws(const wtc_desc* d, int depth, int* st) {
+    if (beyond_fused_k(d)) {
+        UnfusedPlan u;
+        *st = unfused_plan(d, 1, &u);
+        return *st == WTC_OK ? u.total : 0;
+    }
     FusedPlan p;
     *st = plan_fused(d, true, &p);
     if (*st == WTC_OK) return (size_t)p.nrec * p.a.P * sizeof(float);
@@ -298,8 +312,15 @@ size_t fused_bwd_ws(const wtc_desc* d, int depth, int* st) {
     return *st == WTC_OK ? pp.total : 0;
 }
 
+int unf_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
+                const float* wl, const float* sl, void* out, char* ws, size_t wsb, void* stream);
+int unf_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
+                const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0, float* dwl,
+                float* dsl, char* ws, size_t wsb, void* stream);
+
 int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0,
                   const float* wl, const float* sl, void* out, char* ws, size_t wsb, void* stream, int depth) {
+    if (beyond_fused_k(d)) return unf_fwd_run(d, x, w0, s0, b0, wl, sl, out, ws, wsb, stream);
     FusedPlan p;
     int st = plan_fused(d, false, &p);
     if (st == WTC_OK) {
@@ -343,6 +364,7 @@ int fused_fwd_run(const wtc_desc* d, const void* x, const float* w0, const float
 int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
                   const float* wl, const float* sl, void* dx, float* dw0, float* ds0, float* db0, float* dwl,
                   float* dsl, char* ws, size_t wsb, void* stream, int depth) {
+    if (beyond_fused_k(d)) return unf_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, wsb, stream);
     FusedPlan p;
     int st = plan_fused(d, true, &p);
     if (st == WTC_OK) {
@@ -536,7 +558,10 @@ double io_unfused(const wtc_desc* d, int dir) {
     return t + 3.0 * params;
 }
 
+double io_unfused(const wtc_desc* d, int dir);
+
 double io_fused(const wtc_desc* d, int dir, int depth) {
+    if (beyond_fused_k(d)) return io_unfused(d, dir);
     const double e = d->dtype == WTC_BF16 ? 2.0 : 4.0;
     const double KK = (double)d->k * d->k;
     const double BC = (double)d->B * d->C;

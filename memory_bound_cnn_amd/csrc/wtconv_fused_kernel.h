@@ -317,6 +317,7 @@ struct RtGeom {
     static constexpr bool kNoLevels = false;
     static constexpr int kDeep = LMX > 3 ? LMX - 2 : 1;
     static constexpr bool kSub = true;   // may run the LL problem of a peeled plane
+    static constexpr int kMaxThreads = 512;
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
     __device__ int Lm() const { return a.Lm; }
@@ -363,6 +364,7 @@ struct CtGeom {
     // the LL problem of a peeled plane is over 64 pixels wide (its parent did
     // not fit the pipeline): the smaller classes never check for it
     static constexpr bool kSub = HQ > 64;
+    static constexpr int kMaxThreads = NTHR > 512 ? NTHR : 512;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -450,8 +452,15 @@ __device__ __forceinline__ void quad_rows(const float (&xk)[4][4], float (&r0)[2
     }
 }
 
+// Waves per SIMD a kernel is compiled for: a workgroup of 1024 threads (one
+// per CU) needs 4; otherwise the register budget of fused_waves_per_simd.
+template <class G, bool BWD, int BPQ>
+constexpr int kernel_waves() {
+    return G::kMaxThreads > 512 ? 4 : fused_waves_per_simd(BWD, BPQ, G::kNoLevels);
+}
+
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(fused_waves_per_simd(BWD, BPQ, G::kNoLevels))))
+__global__ void __launch_bounds__(G::kMaxThreads) __attribute__((amdgpu_waves_per_eu(kernel_waves<G, BWD, BPQ>())))
 wtc_fused_kernel(const FusedArgs a) {
     constexpr int R = K / 2, KK = K * K;
     constexpr int KKP = (KK + 3) & ~3;   // LDS stride of one (level, band) weight set

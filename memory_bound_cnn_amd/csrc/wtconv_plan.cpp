@@ -33,7 +33,7 @@ size_t top_records(const wtc_desc* d) {
 //   dT_i same shape as S_i         backward only: analysis of g
 // then the correlation partials (backward).
 int unfused_plan(const wtc_desc* d, int bwd, UnfusedPlan* p) {
-    if (d->k > kMaxK) return WTC_ESHAPE;
+    if (d->k > kMaxKAny) return WTC_ESHAPE;
     if (d->L > kMaxUnfusedL) return WTC_ESHAPE;
     const uint64_t BC = (uint64_t)d->B * d->C;
     // 32-bit element indexing of every tensor (the level-1 bands are the largest)

@@ -335,6 +335,116 @@ __global__ void __launch_bounds__(kThreads) k_tcorr(const TA* __restrict__ A, co
     }
 }
 
+// Runtime kernel size (odd k beyond the unrolled instances, k <= kMaxKAny):
+// the same tiles and contract as k_tconv, the taps looped at run time.
+template <bool ROT, typename TI, typename TO>
+__global__ void __launch_bounds__(kThreads) k_tconv_rk(const TI* __restrict__ in, int P, int nch, Tile t, int k,
+                                                       const float* __restrict__ wt, const float* __restrict__ scale,
+                                                       const float* __restrict__ bias, const float* __restrict__ Z,
+                                                       TO* __restrict__ out) {
+    extern __shared__ float lds[];
+    const int R = k / 2, KK = k * k;
+    const int ntile = t.ntx * t.nty;
+    const int g = blockIdx.x / ntile, tile = blockIdx.x - g * ntile;
+    const int ty0 = (tile / t.ntx) * t.TH, tx0 = (tile % t.ntx) * t.TW;
+    const int p0 = g * t.NPB;
+    const int npv = min(t.NPB, P - p0);
+    float* wl = lds;                        // [NPB][KK + 2]: weights, scale, bias
+    float* xs = lds + t.NPB * (KK + 2);     // [NPB][4 NRG + 2R][TW + 2R]
+    for (int f = threadIdx.x; f < npv * (KK + 2); f += kThreads) {
+        const int j = f / (KK + 2), d = f - j * (KK + 2);
+        const int ch = (p0 + j) % nch;
+        float v;
+        if (d < KK) v = wt[ch * KK + (ROT ? KK - 1 - d : d)];
+        else if (d == KK) v = scale[ch];
+        else v = bias ? bias[ch] : 0.f;
+        wl[f] = v;
+    }
+    stage(xs, in, p0, 1, npv, t, ty0, tx0, R);
+    __syncthreads();
+    const int SW = t.TW + 2 * R, RH = 4 * t.NRG + 2 * R;
+    const int total = t.NPB * t.NRG * t.TW;
+    const uint32_t hw = (uint32_t)t.h * t.w;
+    Walk3 it(threadIdx.x, kThreads, t.TW, t.NRG);
+    for (int f = threadIdx.x; f < total; f += kThreads, it.next()) {
+        const int j = it.i2, rg = it.i1, c = it.i0;
+        if (j >= npv) continue;
+        const float* wp = wl + j * (KK + 2);
+        const float* xb = xs + (j * RH + rg * 4) * SW + c;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int ky = 0; ky < k; ++ky)
+            for (int kx = 0; kx < k; ++kx) {
+                const float wv = wp[ky * k + kx];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(wv, xb[(q + ky) * SW + kx], acc[q]);
+            }
+        const float sc = wp[KK], bi = wp[KK + 1];
+        const uint32_t pbase = (uint32_t)(p0 + j) * hw;
+        const int x = tx0 + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = rg * 4 + q, y = ty0 + r;
+            if (r < t.TH && y < t.h && x < t.w) {
+                const uint32_t o = pbase + (uint32_t)(y * t.w + x);
+                float v = fmaf(sc, acc[q], bi);
+                if (Z) v += Z[o];
+                stv(out, o, v);
+            }
+        }
+    }
+}
+
+// Runtime kernel size, weight-gradient correlation: the same contract and
+// tiles as k_tcorr, output-stationary (thread d owns taps d, d + kThreads, ...
+// and the sum slot KK), so no per-thread array of k^2 accumulators.
+template <typename TA, typename TX>
+__global__ void __launch_bounds__(kThreads) k_tcorr_rk(const TA* __restrict__ A, const TX* __restrict__ X, int nb,
+                                                       int nch, Tile t, int k, int nblk, float* __restrict__ part) {
+    extern __shared__ float lds[];
+    const int R = k / 2, KK = k * k;
+    const int ch = blockIdx.x, blk = blockIdx.y;
+    const int b0 = (int)((long)nb * blk / nblk), b1 = (int)((long)nb * (blk + 1) / nblk);
+    const int ARH = 4 * t.NRG, SW = t.TW + 2 * R, RH = 4 * t.NRG + 2 * R;
+    float* as = lds;                            // [NPB][4 NRG][TW]
+    float* xs = lds + t.NPB * ARH * t.TW;       // [NPB][4 NRG + 2R][TW + 2R]
+    constexpr int kMaxPer = (kMaxKAny * kMaxKAny + 1 + kThreads - 1) / kThreads;
+    float acc[kMaxPer];
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) acc[q] = 0.f;
+    for (int bg = b0; bg < b1; bg += t.NPB) {
+        const int npv = min(t.NPB, b1 - bg);
+        for (int tile = 0; tile < t.ntx * t.nty; ++tile) {
+            const int ty0 = (tile / t.ntx) * t.TH, tx0 = (tile % t.ntx) * t.TW;
+            __syncthreads();   // the previous tile's reads are done
+            stage(as, A, bg * nch + ch, nch, npv, t, ty0, tx0, 0);
+            stage(xs, X, bg * nch + ch, nch, npv, t, ty0, tx0, R);
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < kMaxPer; ++q) {
+                const int d = threadIdx.x + q * kThreads;
+                if (d > KK) continue;
+                const int ky = d < KK ? d / k : 0, kx = d < KK ? d - ky * k : 0;
+                float s = 0.f;
+                for (int j = 0; j < npv; ++j)
+                    for (int r = 0; r < ARH; ++r) {
+                        const float* ar = as + (j * ARH + r) * t.TW;
+                        const float* xr = xs + (j * RH + r + ky) * SW + kx;
+                        if (d == KK)
+                            for (int c = 0; c < t.TW; ++c) s += ar[c];
+                        else
+                            for (int c = 0; c < t.TW; ++c) s = fmaf(ar[c], xr[c], s);
+                    }
+                acc[q] += s;
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+        const int d = threadIdx.x + q * kThreads;
+        if (d <= KK) part[((uint32_t)blk * nch + ch) * (KK + 1) + d] = acc[q];
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Large planes (both sides >= kBigSide): 64 x 64 tiles, each thread a 4 x 4
 // block with a register-blocked window (two window rows live, read as 16-byte
@@ -533,30 +643,31 @@ __global__ void __launch_bounds__(kThreads) k_tconv_big(const TI* __restrict__ i
 }
 
 // dW = s * C, ds = sum_d W * C, and (base level) db = sum g, from the partials.
-// One workgroup of 64 lanes per channel, lane d < K*K+1 sums slot d over the
-// partial blocks in a fixed order.
+// One workgroup of 64 lanes per channel; lane l sums slots l, l + 64, ... over
+// the partial blocks in a fixed order.
 __global__ void __launch_bounds__(64) k_corr_finalize(const float* __restrict__ part, int nch, int nblk, int k,
                                                       const float* __restrict__ wt, const float* __restrict__ scale,
                                                       float* __restrict__ dw, float* __restrict__ ds,
                                                       float* __restrict__ db) {
-    const int ch = blockIdx.x, d = threadIdx.x;
+    const int ch = blockIdx.x;
     const int kk = k * k;
-    float cv = 0.f;
-    if (d <= kk) {
+    const size_t stride = (size_t)nch * (kk + 1);
+    float wv = 0.f;
+    for (int d = threadIdx.x; d <= kk; d += 64) {
         const float* pp = part + (size_t)ch * (kk + 1) + d;
-        const size_t stride = (size_t)nch * (kk + 1);
+        float cv = 0.f;
 #pragma unroll 8
         for (int b = 0; b < nblk; ++b) cv += pp[b * stride];
+        if (d < kk) {
+            dw[(size_t)ch * kk + d] = scale[ch] * cv;
+            wv = fmaf(wt[(size_t)ch * kk + d], cv, wv);
+        } else if (db) {
+            db[ch] = cv;
+        }
     }
-    float wv = 0.f;
-    if (d < kk) {
-        dw[(size_t)ch * kk + d] = scale[ch] * cv;
-        wv = wt[(size_t)ch * kk + d] * cv;
-    }
-    if (d == kk && db) db[ch] = cv;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) wv += __shfl_xor(wv, o, 64);
-    if (d == 0) ds[ch] = wv;
+    if (threadIdx.x == 0) ds[ch] = wv;
 }
 
 template <typename T>
@@ -576,7 +687,19 @@ void launch_synthesis(const float* Y, const float* Zd, int P, int h, int w, floa
 // out = scale * conv(in) + bias + Z over P planes of h x w, channel p % nch
 template <int K, typename TI, typename TO>
 void launch_conv(bool rot, const TI* in, int P, int nch, int h, int w, const float* wt, const float* scale,
-                 const float* bias, const float* Z, TO* out, hipStream_t st) {
+                 const float* bias, const float* Z, TO* out, hipStream_t st, int k_rt = K) {
+    if constexpr (K == 0) {
+        // runtime kernel size: the small-tile kernel with the taps looped
+        const Tile t = make_tile(h, w, k_rt, false);
+        const uint32_t grid = (uint32_t)((P + t.NPB - 1) / t.NPB) * (uint32_t)(t.ntx * t.nty);
+        const size_t lds = tile_lds_floats(t, k_rt, false) * sizeof(float);
+        if (rot)
+            hipLaunchKernelGGL((k_tconv_rk<true, TI, TO>), dim3(grid), dim3(kThreads), lds, st, in, P, nch, t, k_rt,
+                               wt, scale, bias, Z, out);
+        else
+            hipLaunchKernelGGL((k_tconv_rk<false, TI, TO>), dim3(grid), dim3(kThreads), lds, st, in, P, nch, t, k_rt,
+                               wt, scale, bias, Z, out);
+    } else {
     if (big_planes(h, w)) {
         const int ntx = (w + kBigTile - 1) / kBigTile, nty = (h + kBigTile - 1) / kBigTile;
         const uint32_t grid = (uint32_t)P * ntx * nty;
@@ -597,6 +720,7 @@ void launch_conv(bool rot, const TI* in, int P, int nch, int h, int w, const flo
     else
         hipLaunchKernelGGL((k_tconv<K, false, TI, TO>), dim3(grid), dim3(kThreads), lds, st, in, P, nch, t, wt,
                            scale, bias, Z, out);
+    }
 }
 
 }  // namespace
@@ -614,8 +738,17 @@ namespace {
 // correlation + finalize of one level (nch channels, nb planes per channel)
 template <int K, typename TA, typename TX>
 void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const float* wt, const float* scale,
-                 float* dw, float* ds, float* db, float* part, hipStream_t st) {
+                 float* dw, float* ds, float* db, float* part, hipStream_t st, int k_rt = K) {
     const int nblk = unfused_corr_blocks(nb, nch, h, w);
+    if constexpr (K == 0) {
+        // runtime kernel size: small tiles for every plane size (blocks beyond
+        // the batch, where the split counts tiles, add zero partials)
+        const Tile t = make_tile(h, w, k_rt, true);
+        const size_t lds = tile_lds_floats(t, k_rt, true) * sizeof(float);
+        hipLaunchKernelGGL((k_tcorr_rk<TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, k_rt,
+                           nblk, part);
+        hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, k_rt, wt, scale, dw, ds, db);
+    } else {
     if (big_planes(h, w)) {
         const int ntx = (w + kBigTile - 1) / kBigTile, nty = (h + kBigTile - 1) / kBigTile;
         hipLaunchKernelGGL((k_tcorr_big<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), 0, st, A, X, nb, nch, h, w,
@@ -628,6 +761,7 @@ void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const 
     }
     hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, K, wt, scale, dw,
                        ds, db);
+    }
 }
 
 template <int K, typename T>
@@ -636,6 +770,7 @@ int fwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const float* w0, 
           const float* zext) {
     const int B = d->B, C = d->C, L = d->L;
     const int P = B * C;
+    const size_t KK = (size_t)d->k * d->k;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     for (int i = 1; i <= L && stage != 2; ++i) {
         if (i == 1)
@@ -647,12 +782,12 @@ int fwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const float* w0, 
     if (stage == 1) return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
     for (int i = 1; i <= L; ++i)
         launch_conv<K, float, float>(false, F(p.s_off[i]), 4 * P, 4 * C, p.h[i], p.w[i],
-                                     wl + (size_t)(i - 1) * 4 * C * K * K, sl + (size_t)(i - 1) * 4 * C, nullptr,
-                                     nullptr, F(p.y_off[i]), st);
+                                     wl + (size_t)(i - 1) * 4 * C * KK, sl + (size_t)(i - 1) * 4 * C, nullptr,
+                                     nullptr, F(p.y_off[i]), st, d->k);
     for (int i = L; i >= 1; --i)
         launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : zext, P, p.h[i], p.w[i], F(p.z_off[i]),
                          p.h[i - 1], p.w[i - 1], st);
-    launch_conv<K, T, T>(false, x, P, C, d->H, d->W, w0, s0, b0, L > 0 ? F(p.z_off[1]) : nullptr, out, st);
+    launch_conv<K, T, T>(false, x, P, C, d->H, d->W, w0, s0, b0, L > 0 ? F(p.z_off[1]) : nullptr, out, st, d->k);
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
@@ -662,6 +797,7 @@ int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const
           char* ws, hipStream_t st, int stage, const float* zext) {
     const int B = d->B, C = d->C, L = d->L;
     const int P = B * C;
+    const size_t KK = (size_t)d->k * d->k;
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
     float* part = F(p.part_off);
     // analysis cascades of g (the adjoint of the synthesis) and of x
@@ -681,21 +817,21 @@ int bwd_t(const wtc_desc* d, const UnfusedPlan& p, const T* x, const T* g, const
     if (stage == 1) return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
     // per level: dS = s * (rot W * dY);  dW, ds from corr(dY, S)
     for (int i = 1; i <= L; ++i) {
-        const float* wli = wl + (size_t)(i - 1) * 4 * C * K * K;
+        const float* wli = wl + (size_t)(i - 1) * 4 * C * KK;
         const float* sli = sl + (size_t)(i - 1) * 4 * C;
         launch_conv<K, float, float>(true, F(p.dt_off[i]), 4 * P, 4 * C, p.h[i], p.w[i], wli, sli, nullptr, nullptr,
-                                     F(p.y_off[i]), st);
+                                     F(p.y_off[i]), st, d->k);
         launch_corr<K, float, float>(F(p.dt_off[i]), F(p.s_off[i]), B, 4 * C, p.h[i], p.w[i], wli, sli,
-                                     dwl + (size_t)(i - 1) * 4 * C * K * K, dsl + (size_t)(i - 1) * 4 * C, nullptr,
-                                     part, st);
+                                     dwl + (size_t)(i - 1) * 4 * C * KK, dsl + (size_t)(i - 1) * 4 * C, nullptr,
+                                     part, st, d->k);
     }
     // adjoint of the analysis: synthesis of dS, deepest first
     for (int i = L; i >= 1; --i)
         launch_synthesis(F(p.y_off[i]), i < L ? F(p.z_off[i + 1]) : zext, P, p.h[i], p.w[i], F(p.z_off[i]),
                          p.h[i - 1], p.w[i - 1], st);
     // base: dx = s0 * (rot W0 * g) + dLL_0;  dW0, ds0, db0 from corr(g, x)
-    launch_conv<K, T, T>(true, g, P, C, d->H, d->W, w0, s0, nullptr, L > 0 ? F(p.z_off[1]) : nullptr, dx, st);
-    launch_corr<K, T, T>(g, x, B, C, d->H, d->W, w0, s0, dw0, ds0, db0, part, st);
+    launch_conv<K, T, T>(true, g, P, C, d->H, d->W, w0, s0, nullptr, L > 0 ? F(p.z_off[1]) : nullptr, dx, st, d->k);
+    launch_corr<K, T, T>(g, x, B, C, d->H, d->W, w0, s0, dw0, ds0, db0, part, st, d->k);
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
@@ -742,7 +878,7 @@ int unfused_forward(const wtc_desc* d, const UnfusedPlan& p, const void* x, cons
         case 3: return fwd_k<3>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
         case 5: return fwd_k<5>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
         case 7: return fwd_k<7>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
-        default: return WTC_ESHAPE;
+        default: return fwd_k<0>(d, p, x, w0, s0, b0, wl, sl, out, ws, st, stage, zext);
     }
 }
 
@@ -755,7 +891,7 @@ int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, con
         case 3: return bwd_k<3>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
         case 5: return bwd_k<5>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
         case 7: return bwd_k<7>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
-        default: return WTC_ESHAPE;
+        default: return bwd_k<0>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
     }
 }
 

@@ -96,6 +96,7 @@ int main(int argc, char** argv) {
         {70, 3, 7, 7, 1, 5, 0, 0},    {2, 3, 224, 224, 3, 5, 0, 0}, {1, 2, 300, 260, 4, 3, 0, 0},
         {1, 2, 257, 129, 9, 5, 0, 0}, {2, 2, 260, 130, 0, 7, 0, 0}, {2, 5, 64, 64, 3, 5, 0, 1},
         {1, 1, 1, 1, 3, 5, 0, 0},     {2, 4, 8, 8, 2, 5, 1, 0},     {1, 2, 600, 40, 2, 5, 0, 0},
+        {2, 3, 33, 20, 2, 31, 0, 0},  {1, 2, 200, 150, 3, 9, 1, 1},
     };
     for (int i = 0; i < ncase; ++i) {
         wtc_desc d;
@@ -104,7 +105,7 @@ int main(int argc, char** argv) {
         d.H = pick({1, 2, 3, 7, 8, 13, 14, 16, 31, 32, 40, 64, 100, 127, 128, 129, 150, 224});
         d.W = pick({1, 2, 5, 7, 8, 14, 17, 32, 33, 36, 64, 72, 100, 128, 130, 200});
         d.L = pick({0, 1, 2, 3, 4, 5, 6, 9});
-        d.k = pick({1, 3, 5, 7});
+        d.k = pick({1, 3, 5, 7, 9, 11});
         d.dtype = pick({0, 1});
         d.layout = (rng() % 8 == 0) ? 1 : 0;
         cases.push_back(d);

@@ -41,7 +41,8 @@ FAKE = ctypes.c_void_p(16)   # never dereferenced: every case below fails valida
     (dict(B=0), binding.WTC_EINVAL), (dict(H=0), binding.WTC_EINVAL), (dict(dtype=7), binding.WTC_EDTYPE),
     (dict(layout=2), binding.WTC_EDTYPE), (dict(layout=1), binding.WTC_EWORKSPACE),
     (dict(H=512, W=512), binding.WTC_EWORKSPACE),
-    (dict(k=9), binding.WTC_ESHAPE),
+    (dict(k=33), binding.WTC_ESHAPE),
+    (dict(k=9), binding.WTC_EWORKSPACE),   # k = 9..31 runs the level-by-level kernels: it needs a workspace
 ])
 def test_forward_rejects(kw, status):
     lib = binding.load_library()
@@ -118,11 +119,11 @@ def test_unfused_workspace_and_limits():
     assert binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k) > want
     # any plane size is accepted (no LDS limit) ...
     assert binding.wtconv_forward_unfused_workspace(1, 1, 512, 512, 2, 5) > 0
-    # ... but not more than 30 levels, k > 7, or tensors beyond 32-bit indexing
+    # ... but not more than 30 levels, k > 31, or tensors beyond 32-bit indexing
     d = _desc(L=31)
     assert lib.wtconv_forward_unfused(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                       1 << 40, None) == binding.WTC_ESHAPE
-    d = _desc(k=9)
+    d = _desc(k=33)
     assert lib.wtconv_forward_unfused(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                       1 << 40, None) == binding.WTC_ESHAPE
     d = _desc(B=4096, C=1024, H=32, W=32)
@@ -184,7 +185,7 @@ def test_large_planes_take_the_peeled_path():
     assert binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=0, direction=0) < \
         binding.wtconv_io_model_bytes(2, 3, 200, 150, 3, 5, impl=1, direction=0)
     # limits that no path lifts
-    assert binding.wtconv_forward_workspace(2, 3, 64, 64, 2, 9) == 0
+    assert binding.wtconv_forward_workspace(2, 3, 64, 64, 2, 33) == 0
 
 
 def test_channels_last_workspace_and_model():
@@ -232,3 +233,19 @@ def test_noalloc_scratch_covers_the_benchmark_shapes():
             need = binding.wtconv_backward_workspace(w.B, w.C, w.H, w.W, L, w.k, w.dtype)
             if w.H <= 128 and w.W <= 128:
                 assert need <= binding.NOALLOC_SCRATCH_BYTES, (w.name, L, need)
+
+
+def test_kernel_sizes_beyond_the_fused_kernels():
+    """k = 9..31 runs the level-by-level kernels through the fused entry points:
+    their workspace queries and I/O model are the level-by-level ones."""
+    for k in (9, 11, 31):
+        for L in (0, 2):
+            for fn, fu in (("wtconv_forward_workspace", "wtconv_forward_unfused_workspace"),
+                           ("wtconv_backward_workspace", "wtconv_backward_unfused_workspace")):
+                a = getattr(binding, fn)(2, 3, 40, 24, L, k)
+                b = getattr(binding, fu)(2, 3, 40, 24, L, k)
+                assert a == b, (k, L, fn)
+            for dr in (0, 1):
+                assert binding.wtconv_io_model_bytes(2, 3, 40, 24, L, k, impl=0, direction=dr) == \
+                    binding.wtconv_io_model_bytes(2, 3, 40, 24, L, k, impl=1, direction=dr)
+    assert binding.wtconv_backward_workspace(2, 3, 40, 24, 2, 33) == 0

@@ -277,6 +277,26 @@ def test_full_size_dwconv(k):
     _full_size(wl_, 0)
 
 
+# Kernel sizes 9..31: no fused kernel holds their k^2 weights and accumulators
+# in registers, so the fused entry points run the level-by-level kernels with
+# the taps looped at run time.  Both entry points, small and large planes (the
+# 64 x 64-tile threshold), bf16, L = 0, a kernel larger than the plane.
+LARGE_K = [
+    (2, 3, 32, 32, 2, 9, 120, "fp32"),
+    (1, 2, 50, 60, 3, 11, 121, "fp32"),
+    (2, 2, 20, 14, 1, 9, 122, "bf16"),
+    (2, 3, 16, 16, 0, 13, 123, "fp32"),
+    (1, 2, 9, 7, 3, 15, 124, "fp32"),
+    (1, 1, 40, 33, 1, 31, 125, "fp32"),
+]
+
+
+@pytest.mark.parametrize("impl", ["fused", "unfused"])
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", LARGE_K)
+def test_large_kernel_sizes(impl, B, C, H, W, L, k, seed, dtype):
+    _case(B, C, H, W, L, k, seed, dtype, impl)
+
+
 # Planes beyond the on-chip pipeline: level 1 and the base conv level by level,
 # the LL band recursively (fused once it fits).
 LARGE = [
