@@ -68,7 +68,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         a.P = partial_len(k, a.Lm);
         a.ppw = 64;
         p->nchunk = (d->B + 63) / 64;
-        p->grid = d->C * p->nchunk;
+        p->grid = 8 * cdiv(d->C * p->nchunk, 8);   // XCD-aware unit order (8 XCDs)
         p->nrec = (long)p->nchunk * d->C;
         p->nthr = 64;
         p->bpq = 1;

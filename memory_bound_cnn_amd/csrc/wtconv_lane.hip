@@ -102,7 +102,16 @@ k_lane(const FusedArgs a) {
     __shared__ float lds[64 * SP];
     __shared__ float red[4 * RL];   // backward: partials per 16-lane row
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int c = blockIdx.x % a.C, chunk = blockIdx.x / a.C;
+    // Units (batch chunk, channel), chunk-major, dealt to the XCDs in
+    // contiguous ranges: workgroup i runs on XCD i % 8 (workgroups are dealt to
+    // the XCDs in turn), so the planes of neighbouring channels -- 196-byte
+    // planes that share cache lines -- pass through one L2 at about the same
+    // time instead of being fetched once per XCD.
+    const int nchunk = (a.B + 63) / 64;
+    const int U = a.C * nchunk, per = (U + 7) / 8;
+    const int k8 = blockIdx.x >> 3, u = (blockIdx.x & 7) * per + k8;
+    if (k8 >= per || u >= U) return;   // whole workgroup, before any barrier
+    const int c = u % a.C, chunk = u / a.C;
     const int b0 = chunk * 64, n = min(64, a.B - b0);
     const ST* srcp = reinterpret_cast<const ST*>(a.src);
     const ST* auxp = reinterpret_cast<const ST*>(a.aux);

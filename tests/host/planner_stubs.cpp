@@ -97,9 +97,8 @@ int launch_tiny(const FusedArgs& a, int dtype, int bwd, int grid, void*) {
 }
 
 int launch_lane(const FusedArgs& a, int dtype, int bwd, int grid, void*) {
-    need(grid % a.C == 0, "lane grid");
-    const int nchunk = grid / a.C;
-    need((long)nchunk * 64 >= a.B, "lane chunks cover the batch");
+    const int nchunk = (a.B + 63) / 64;
+    need(grid % 8 == 0 && grid >= a.C * nchunk && grid < a.C * nchunk + 8, "lane grid");
     rd(a.src, act_bytes(a, dtype));
     if (bwd) rd(a.aux, act_bytes(a, dtype));
     params(a, 5, bwd);
