@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--workload", default=HEADLINE)
     p.add_argument("--level", type=int, default=None, help="override L (sweep workload)")
     p.add_argument("--impl", default="fused", choices=["fused", "unfused"])
+    p.add_argument("--layout", default="nchw", choices=["nchw", "nhwc", "nhwc_inplace"],
+                   help="activation memory layout: nhwc = torch.channels_last tensors through NCHW copies "
+                        "(layout 1), nhwc_inplace = read and written in place (layout 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-summary", action="store_true")
     p.add_argument("--torch-dwconv", action="store_true",
@@ -96,7 +99,7 @@ def kernel_source_hash():
 class Runner:
     """Device buffers for one workload and one implementation."""
 
-    def __init__(self, wl, L, impl, torch, binding, rotate=True):
+    def __init__(self, wl, L, impl, torch, binding, rotate=True, layout="nchw"):
         from memory_bound_cnn_amd.inputs import workload_inputs
         self.torch, self.b = torch, binding
         self.wl, self.L, self.impl = wl, L, impl
@@ -110,10 +113,14 @@ class Runner:
         self.R = R
         x = torch.from_numpy(d["x"]).to(dev).to(sd)
         g = torch.from_numpy(d["g"]).to(dev).to(sd)
+        if layout != "nchw":
+            x = x.contiguous(memory_format=torch.channels_last)
+            g = g.contiguous(memory_format=torch.channels_last)
         self.sets = []
         for r in range(R):
-            xs = x if r == 0 else x.roll(r, dims=0).contiguous()
-            gs = g if r == 0 else g.roll(r, dims=0).contiguous()
+            fmt = torch.channels_last if layout != "nchw" else torch.contiguous_format
+            xs = x if r == 0 else x.roll(r, dims=0).contiguous(memory_format=fmt)
+            gs = g if r == 0 else g.roll(r, dims=0).contiguous(memory_format=fmt)
             self.sets.append(dict(x=xs, g=gs, out=torch.empty_like(x), dx=torch.empty_like(x)))
         f = lambda a: torch.from_numpy(a).to(dev)
         self.w0, self.s0, self.b0 = f(d["w0"]), f(d["s0"]), f(d["b0"])
@@ -125,13 +132,16 @@ class Runner:
                           dwl=torch.empty(L, 4 * C, k, k, **f32) if L > 0 else None,
                           dsl=torch.empty(L, 4 * C, **f32) if L > 0 else None)
         shp = (wl.B, wl.C, wl.H, wl.W, L, k, wl.dtype)
+        lay = {"nchw": 0, "nhwc": 1, "nhwc_inplace": 2}[layout]
+        self.in_place = layout == "nhwc_inplace"
         if impl == "fused":
             self.fwd, self.bwd = binding.wtconv_forward, binding.wtconv_backward
-            wsf, wsb = binding.wtconv_forward_workspace(*shp), binding.wtconv_backward_workspace(*shp)
+            wsf = binding.wtconv_forward_workspace(*shp, layout=lay)
+            wsb = binding.wtconv_backward_workspace(*shp, layout=lay)
         else:
             self.fwd, self.bwd = binding.wtconv_forward_unfused, binding.wtconv_backward_unfused
-            wsf = binding.wtconv_forward_unfused_workspace(*shp)
-            wsb = binding.wtconv_backward_unfused_workspace(*shp)
+            wsf = binding.wtconv_forward_unfused_workspace(*shp, layout=lay)
+            wsb = binding.wtconv_backward_unfused_workspace(*shp, layout=lay)
         self.ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device=dev)
         self.ws_b = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
         self.N, self.e = N, e
@@ -140,14 +150,15 @@ class Runner:
         s = self.sets[i % self.R]
         if ev is not None:
             ev[0].record()
+        kw = {"in_place": True} if self.in_place else {}
         if only != "bwd":
             self.fwd(s["x"], self.w0, self.s0, self.b0, self.wl_, self.sl_, self.L, out=s["out"],
-                     workspace=self.ws_f)
+                     workspace=self.ws_f, **kw)
         if ev is not None:
             ev[1].record()
         if only != "fwd":
             self.bwd(s["x"], s["g"], self.w0, self.s0, self.wl_, self.sl_, self.L, dx=s["dx"], grads=self.grads,
-                     workspace=self.ws_b)
+                     workspace=self.ws_b, **kw)
         if ev is not None:
             ev[2].record()
 
@@ -209,6 +220,27 @@ def dwconv_comparison(wl, torch, binding, with_torch):
                                   "fwd_ms": round(sum(fw) / len(fw), 5), "bwd_ms": round(sum(bw) / len(bw), 5)}
     base = res["dwconv_L0_k7"]["ms"]
     res["wtconv_over_dwconv_k7"] = round(res[f"wtconv_L{wl.L}_k{wl.k}"]["ms"] / base, 3)
+    return res
+
+
+def channels_last_comparison(torch, binding):
+    """Fused forward + backward on channels-last tensors -- through NCHW copies
+    (layout 1) and in place (layout 2) -- against the same workload in NCHW,
+    ms per step."""
+    from memory_bound_cnn_amd.inputs import WORKLOADS
+    res = []
+    for name in ("stage1_b32c96_64x64_L3", "bf16_b64c192_32x32_L3", "odd_b128c384_14x14_L2"):
+        w = WORKLOADS[name]
+        row = {"workload": name, "L": w.L}
+        for layout in ("nchw", "nhwc", "nhwc_inplace"):
+            rr = Runner(w, w.L, "fused", torch, binding, layout=layout)
+            m, mf, mb = rr.time(50, 5)
+            del rr
+            row[layout] = {"ms": round(m, 5), "fwd_ms": round(mf, 5), "bwd_ms": round(mb, 5)}
+        row["nhwc_over_nchw"] = round(row["nhwc"]["ms"] / row["nchw"]["ms"], 3)
+        row["nhwc_inplace_over_nchw"] = round(row["nhwc_inplace"]["ms"] / row["nchw"]["ms"], 3)
+        res.append(row)
+        torch.cuda.empty_cache()
     return res
 
 
@@ -369,7 +401,7 @@ def _pmc_totals(d, counter):
     return acc
 
 
-def pmc_summary(dirs, out_txt, cmd, wl_name, L, source_hash=None):
+def pmc_summary(dirs, out_txt, cmd, wl_name, L, source_hash=None, layout="nchw"):
     """Calibrated HBM bytes per call of each direction from FETCH_SIZE and
     WRITE_SIZE runs (one counter per run) that called only that direction.
     Every library kernel of such a run belongs to the direction; the calls
@@ -401,12 +433,13 @@ def pmc_summary(dirs, out_txt, cmd, wl_name, L, source_hash=None):
                 "write_bytes_per_call": wv[0] * 1024.0 * w_fac / calls_w,
                 "dispatches_per_call": fv[1] / calls_f}
     from memory_bound_cnn_amd import binding
-    model = {"fwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=0),
-             "bwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=1)}
+    lay = {"nchw": 0, "nhwc": 1, "nhwc_inplace": 2}[layout]
+    model = {"fwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=0, layout=lay),
+             "bwd": binding.wtconv_io_model_bytes(*shp, impl=0, direction=1, layout=lay)}
     rec = {"source_hash": source_hash or kernel_source_hash(),
            "calibration": {"copy_kernel": _short(ck), "copy_bytes_each_way": copy_bytes,
                            "fetch_factor": f_fac, "write_factor": w_fac},
-           "workloads": {f"{wl_name}_L{L}": {"fwd_bytes": tot["fwd"], "bwd_bytes": tot["bwd"],
+           "workloads": {f"{wl_name}_L{L}" + ("" if layout == "nchw" else "_" + layout): {"fwd_bytes": tot["fwd"], "bwd_bytes": tot["bwd"],
                                              "model_fwd_bytes": model["fwd"], "model_bwd_bytes": model["bwd"],
                                              "command": cmd, "kernels": per_kernel}}}
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
@@ -425,7 +458,7 @@ def pmc_summary(dirs, out_txt, cmd, wl_name, L, source_hash=None):
              f"copy probe: {_short(ck)} moving {copy_bytes:.0f} B each way; FETCH_SIZE reads "
              f"{cf[ck][0] / cf[ck][1]:.1f} KiB -> factor {f_fac:.4f}; WRITE_SIZE reads "
              f"{cw[ck][0] / cw[ck][1]:.1f} KiB -> factor {w_fac:.4f}",
-             f"workload {wl_name} L={L}", ""]
+             f"workload {wl_name} L={L} layout {layout}", ""]
     for k, v in per_kernel.items():
         lines.append(f"{k:104s} x{v['dispatches_per_call']:.0f}/call: read {v['read_bytes_per_call'] / 1e6:9.2f} MB, "
                      f"write {v['write_bytes_per_call'] / 1e6:9.2f} MB")
@@ -436,9 +469,9 @@ def pmc_summary(dirs, out_txt, cmd, wl_name, L, source_hash=None):
     print("\n".join(lines))
 
 
-def traffic_from_profiles(wl, L):
-    """HBM bytes per backward launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources."""
+def traffic_from_profiles(wl, L, layout="nchw"):
+    """HBM bytes per call (fwd_bytes, bwd_bytes) from the committed rocprofv3
+    counter summary, if it was taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(p):
         return None
@@ -446,7 +479,7 @@ def traffic_from_profiles(wl, L):
         rec = json.load(open(p))
     except ValueError:
         return None
-    key = f"{wl.name}_L{L}"
+    key = f"{wl.name}_L{L}" + ("" if layout == "nchw" else "_" + layout)
     r = rec.get("workloads", {}).get(key)
     if not r or rec.get("source_hash") != kernel_source_hash():
         return None
@@ -469,11 +502,12 @@ def main():
         stats_summary(a.stats_summary[0], a.stats_summary[1], a.cmd)
         return
     if a.pmc_summary:
-        pmc_summary(a.pmc_summary[:6], a.pmc_summary[6], a.cmd, wl.name, L, a.source_hash)
+        pmc_summary(a.pmc_summary[:6], a.pmc_summary[6], a.cmd, wl.name, L, a.source_hash, a.layout)
         return
     shp = (wl.B, wl.C, wl.H, wl.W, L, wl.k, wl.dtype)
-    io_f = binding.wtconv_io_model_bytes(*shp, impl=0, direction=0)
-    io_b = binding.wtconv_io_model_bytes(*shp, impl=0, direction=1)
+    lay = {"nchw": 0, "nhwc": 1, "nhwc_inplace": 2}[a.layout]
+    io_f = binding.wtconv_io_model_bytes(*shp, impl=0, direction=0, layout=lay)
+    io_b = binding.wtconv_io_model_bytes(*shp, impl=0, direction=1, layout=lay)
 
     # The CPU baseline runs first, before this process touches the GPU.
     cpu = None
@@ -498,15 +532,15 @@ def main():
         return
 
     if a.profile_steps is not None:
-        r = Runner(wl, L, a.impl, torch, binding)
+        r = Runner(wl, L, a.impl, torch, binding, layout=a.layout)
         for i in range(a.profile_steps):
             r.step(i, only=a.profile_only)
         torch.cuda.synchronize()
         print(json.dumps({"profile_run": wl.name, "L": L, "impl": a.impl, "calls": a.profile_steps,
-                          "only": a.profile_only, "source_hash": kernel_source_hash()}))
+                          "only": a.profile_only, "layout": a.layout, "source_hash": kernel_source_hash()}))
         return
 
-    r = Runner(wl, L, a.impl, torch, binding)
+    r = Runner(wl, L, a.impl, torch, binding, layout=a.layout)
     ms, fwd_ms, bwd_ms = r.time(a.steps, a.warmup)
     fl_f = binding.wtconv_flops(*shp, direction=0)
     fl_b = binding.wtconv_flops(*shp, direction=1)
@@ -527,7 +561,7 @@ def main():
         "dtype": "f32" if wl.dtype == "fp32" else "bf16-storage/f32-compute",
         "data": "synthetic (seeded N(0,1) inputs and gradients, N(0,1/k^2) weights, U[0.05,0.5] scales)",
         "config": {"workload": wl.name, "B": wl.B, "C": wl.C, "H": wl.H, "W": wl.W, "L": L, "k": wl.k,
-                   "storage": wl.dtype, "impl": a.impl},
+                   "storage": wl.dtype, "impl": a.impl, "layout": a.layout},
         "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "fwd_ms": round(fwd_ms, 5),
         "bwd_ms": round(bwd_ms, 5),
@@ -535,7 +569,7 @@ def main():
         "flops": {"fwd": fl_f, "bwd": fl_b},
         "buffer_sets_rotated": r.R,
     }
-    tr = traffic_from_profiles(wl, L)
+    tr = traffic_from_profiles(wl, L, a.layout)
     # dominant call: wtconv_backward; algorithmic bytes per call = 3 e N
     alg_b = 3.0 * r.e * r.N
     alg_f = 2.0 * r.e * r.N
@@ -609,6 +643,7 @@ def main():
                 summary.append(row)
         line["per_workload"] = summary
         line["dwconv_comparison"] = dwconv_comparison(wl, torch, binding, a.torch_dwconv)
+        line["channels_last_comparison"] = channels_last_comparison(torch, binding)
         line["training_step_memory"] = memory_comparison(wl, L, torch, binding)
 
     if cpu is not None:

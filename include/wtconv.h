@@ -28,12 +28,19 @@
  *     library never allocates, frees or synchronises on these paths; calls
  *     are asynchronous on `stream` (a hipStream_t; NULL = default stream).
  *   - x, out, g (= d loss / d out) and dx are [B, C, H, W], NCHW contiguous
- *     (layout 0) or channels-last [B, H, W, C] contiguous (layout 1), stored as
- *     float32 (dtype WTC_FP32) or bfloat16 bits (WTC_BF16; out and dx are
- *     rounded to nearest even).  All arithmetic is float32.  Channels-last
- *     tensors are transposed into NCHW copies at the front of the workspace,
- *     computed there and transposed back (two extra tensors of workspace
- *     forward, three backward; four and six extra tensor passes of traffic).
+ *     (layout 0) or channels-last [B, H, W, C] contiguous (layouts 1 and 2),
+ *     stored as float32 (dtype WTC_FP32) or bfloat16 bits (WTC_BF16; out and
+ *     dx are rounded to nearest even).  All arithmetic is float32.
+ *     Layout 1 (channels-last, fastest): the tensors are transposed into NCHW
+ *     copies at the front of the workspace, computed there and transposed
+ *     back (two extra tensors of workspace forward, three backward; four and
+ *     six extra tensor passes of traffic).
+ *     Layout 2 (channels-last, in place): the fused kernels read and write
+ *     the tensors where they are -- no copies, no extra workspace, HBM
+ *     traffic as for NCHW -- for every plane the on-chip pipeline holds (about
+ *     128 x 128 at k = 5, k <= 7); slower than layout 1, because each pixel of
+ *     a channel is a separate cache-line request.  Beyond those planes layout
+ *     2 is adapted like layout 1.  The level-by-level entry points adapt both.
  *   - Parameters and their gradients are float32:
  *       w0 [C, k, k] (PyTorch depthwise [C,1,k,k] order), s0 [C], b0 [C],
  *       wl [L, 4C, k, k] with flat index ((l*C + c)*4 + u)*k*k + ky*k + kx,
@@ -58,7 +65,7 @@ typedef enum {
     WTC_OK = 0,
     WTC_EINVAL = -1,     /* null pointer, k even or < 1, L < 0, B/C/H/W < 1, bad impl/dir */
     WTC_ESHAPE = -2,     /* k > 31, or a tensor of 2^31 elements or more */
-    WTC_EDTYPE = -3,     /* dtype or layout not supported (layout > 1) */
+    WTC_EDTYPE = -3,     /* dtype or layout not supported (layout > 2) */
     WTC_EWORKSPACE = -4, /* workspace NULL or smaller than the queried size */
     WTC_EHIP = -5,       /* a HIP launch or runtime call failed */
     WTC_ESCRATCH = -6    /* wtconv_backward_noalloc: the call needs more than
@@ -72,7 +79,7 @@ typedef struct {
     int L;          /* wavelet levels (>= 0)                                  */
     int k;          /* kernel size: odd, 1..31 (fused kernels for k <= 7)     */
     int dtype;      /* wtc_dtype: storage type of x / out / g / dx           */
-    int layout;     /* 0 = NCHW, 1 = channels-last (NHWC)                     */
+    int layout;     /* 0 = NCHW, 1 = channels-last, 2 = channels-last in place */
 } wtc_desc;
 
 /* Bytes of device workspace wtconv_forward needs (0: none).  It is 0 for every
@@ -130,8 +137,8 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g,
  * Runs on the device current at the call (the one of `stream` and the
  * tensors).  A call whose wtconv_backward_workspace(d) exceeds the array
  * returns WTC_ESCRATCH before any HIP call: planes beyond the on-chip
- * pipeline (above about 128 x 128 at k = 5) and channels-last tensors need
- * far more.  Nothing in the array has to start at zero (every record is
+ * pipeline (above about 128 x 128 at k = 5) and channels-last tensors through
+ * NCHW copies (layout 1) need far more; layout 2 fits.  Nothing in the array has to start at zero (every record is
  * written before it is read), but all calls on one GPU share it: calls that
  * overlap in time on one GPU (two streams, or two threads) race and must be
  * serialised by the caller.  The first call on a device also looks up the

@@ -85,7 +85,8 @@ def wtconv_status_string(status):
 
 
 def make_desc(B, C, H, W, L, k, dtype="fp32", layout=0):
-    """layout 0: NCHW; 1: channels-last (NHWC), adapted by transposes in the library."""
+    """layout 0: NCHW; 1: channels-last (through NCHW copies in the workspace);
+    2: channels-last read and written in place (no copies)."""
     dt = {"fp32": WTC_FP32, "bf16": WTC_BF16, torch.float32: WTC_FP32, torch.bfloat16: WTC_BF16}[dtype]
     return wtc_desc(int(B), int(C), int(H), int(W), int(L), int(k), dt, int(layout))
 
@@ -124,9 +125,10 @@ def _check_tensor(t, name, dtypes, device, shape=None, layout=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
-def _desc_of(x, L, k):
+def _desc_of(x, L, k, in_place=False):
     B, C, H, W = x.shape
-    return make_desc(B, C, H, W, L, k, x.dtype, _layout_of(x))
+    lay = _layout_of(x)
+    return make_desc(B, C, H, W, L, k, x.dtype, 2 if (lay == 1 and in_place) else lay)
 
 
 def _check_params(x, w0, s0, b0, wl, sl, L):
@@ -162,10 +164,10 @@ def _workspace(nbytes, device, workspace):
     return ws, nbytes
 
 
-def _fwd_common(fn_name, ws_name, x, w0, s0, b0, wl, sl, L, out, workspace):
+def _fwd_common(fn_name, ws_name, x, w0, s0, b0, wl, sl, L, out, workspace, in_place=False):
     k = _check_params(x, w0, s0, b0, wl, sl, L)
     lib = load_library()
-    d = _desc_of(x, L, k)
+    d = _desc_of(x, L, k, in_place)
     if out is None:
         out = torch.empty_like(x)
     _check_tensor(out, "out", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
@@ -201,11 +203,11 @@ def _grad_buffers(x, L, k, grads):
     return out
 
 
-def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace):
+def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace, in_place=False):
     k = _check_params(x, w0, s0, None, wl, sl, L)
     _check_tensor(g, "g", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
     lib = load_library()
-    d = _desc_of(x, L, k)
+    d = _desc_of(x, L, k, in_place)
     if dx is None:
         dx = torch.empty_like(x)
     _check_tensor(dx, "dx", (x.dtype,), x.device, x.shape, layout=_layout_of(x))
@@ -227,9 +229,12 @@ def _bwd_common(fn_name, ws_name, x, g, w0, s0, wl, sl, L, dx, grads, workspace)
     return out
 
 
-def wtconv_forward(x, w0, s0, b0, wl, sl, L, out=None, workspace=None):
-    """out = WTConv(x) on the current stream (fused kernels)."""
-    return _fwd_common("wtconv_forward", "wtconv_forward_workspace", x, w0, s0, b0, wl, sl, L, out, workspace)
+def wtconv_forward(x, w0, s0, b0, wl, sl, L, out=None, workspace=None, in_place=False):
+    """out = WTConv(x) on the current stream (fused kernels).  in_place: a
+    channels-last x is read (and out written) where it is, without NCHW copies
+    (layout 2; slower, no extra workspace)."""
+    return _fwd_common("wtconv_forward", "wtconv_forward_workspace", x, w0, s0, b0, wl, sl, L, out, workspace,
+                       in_place)
 
 
 def wtconv_forward_unfused(x, w0, s0, b0, wl, sl, L, out=None, workspace=None):
@@ -238,17 +243,19 @@ def wtconv_forward_unfused(x, w0, s0, b0, wl, sl, L, out=None, workspace=None):
                        out, workspace)
 
 
-def wtconv_backward(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None):
-    """Returns dict(dx, dw0, ds0, db0, dwl, dsl) for upstream gradient g (fused kernels)."""
+def wtconv_backward(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None, in_place=False):
+    """Returns dict(dx, dw0, ds0, db0, dwl, dsl) for upstream gradient g (fused
+    kernels).  in_place: as for :func:`wtconv_forward`."""
     return _bwd_common("wtconv_backward", "wtconv_backward_workspace", x, g, w0, s0, wl, sl, L, dx, grads,
-                       workspace)
+                       workspace, in_place)
 
 
-def wtconv_backward_noalloc(x, g, w0, s0, wl, sl, L, dx=None, grads=None):
+def wtconv_backward_noalloc(x, g, w0, s0, wl, sl, L, dx=None, grads=None, in_place=False):
     """:func:`wtconv_backward` without a workspace: the library allocates
     nothing (its scratch is a fixed per-GPU array of NOALLOC_SCRATCH_BYTES).
-    Pass dx and grads to have no allocation on this side either."""
-    return _bwd_common("wtconv_backward_noalloc", None, x, g, w0, s0, wl, sl, L, dx, grads, None)
+    Pass dx and grads to have no allocation on this side either.  Channels-last
+    tensors need in_place=True (NCHW copies would not fit the scratch)."""
+    return _bwd_common("wtconv_backward_noalloc", None, x, g, w0, s0, wl, sl, L, dx, grads, None, in_place)
 
 
 def wtconv_backward_unfused(x, g, w0, s0, wl, sl, L, dx=None, grads=None, workspace=None):

@@ -180,6 +180,10 @@ struct FusedArgs {
     int vec;           // W % 4 == 0: 4-pixel vector global accesses
     int pf_on;         // prefetch the next planes into registers
     int nobase;        // skip the base conv: the LL problem of a peeled plane (its scale and bias are 0)
+    int units;         // 1: one (batch chunk, channel) unit per workgroup, dealt to the XCDs in
+                       //    contiguous ranges; records [chunk][channel] (finalize in chunk mode)
+    int nchunk;        // units: batch chunks per channel (of ppw entries)
+    int nhwc;          // x, g, out, dx are channels-last [B, H, W, C] (the kernel's kNHWC)
     Layout lay;
     int wts_off;       // folded weights (per workgroup)
     int red_off;       // reduction scratch (backward)

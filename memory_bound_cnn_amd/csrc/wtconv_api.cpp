@@ -24,8 +24,8 @@ int check_desc(const wtc_desc* d) {
     if (d->B < 1 || d->C < 1 || d->H < 1 || d->W < 1 || d->L < 0) return WTC_EINVAL;
     if (d->k < 1 || d->k % 2 == 0) return WTC_EINVAL;
     if (d->dtype != WTC_FP32 && d->dtype != WTC_BF16) return WTC_EDTYPE;
-    if (d->layout != 0 && d->layout != 1) return WTC_EDTYPE;
-    if (d->layout == 1 && d->B > 65535) return WTC_ESHAPE;   // transpose grid
+    if (d->layout < 0 || d->layout > 2) return WTC_EDTYPE;
+    if (d->layout != 0 && d->B > 65535) return WTC_ESHAPE;   // transpose grid
     return WTC_OK;
 }
 
@@ -61,8 +61,13 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     a.nqx = a.Wq / 8;
     a.qpp = (a.Hq / 8) * a.nqx;
     a.vec = (d->W % 4 == 0) ? 1 : 0;
+    // channels-last tensors: the plane pipeline reads and writes them in place,
+    // one (batch chunk, channel) unit per workgroup, the units of neighbouring
+    // channels -- which share every cache line -- on one XCD at a time
+    a.nhwc = d->layout != 0 ? 1 : 0;
+    a.units = a.nhwc;
     p->tiny = 0;
-    if (lane_supported(k, d->H, d->W, d->L, a.Lm)) {
+    if (!a.nhwc && lane_supported(k, d->H, d->W, d->L, a.Lm)) {
         // one plane per lane, one wave per 64 batch entries of a channel
         p->tiny = 2;
         a.P = partial_len(k, a.Lm);
@@ -76,7 +81,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         return WTC_OK;
     }
     const long esize = d->dtype == WTC_BF16 ? 2 : 4;
-    if (tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm) &&
+    if (!a.nhwc && tiny_supported(k, a.Hq, a.Wq, d->L, a.Lm) &&
         ((long)d->B + 16) * d->C * d->H * d->W * esize < (1L << 31)) {   // 32-bit buffer offsets
         // one wave per workgroup: 16 consecutive channels, ppw batch entries (one
         // pass per entry); one resident round of waves (registers allow 3 per
@@ -144,7 +149,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     // planes; the bf16 forward measured faster staging through registers (54 us
     // against 70 us on 32x32 planes).  Tried first, so it wins ties.
     const int esz = d->dtype == WTC_BF16 ? 2 : 4;
-    const bool dl_ok = a.vec && a.qpp <= 128 && (bwd || d->dtype == WTC_FP32);
+    const bool dl_ok = a.vec && a.qpp <= 128 && (bwd || d->dtype == WTC_FP32) && !(a.nhwc && d->dtype == WTC_BF16);
     // The backward takes direct loads whenever one plane fills a wave, even where
     // the larger slot (it holds a plane of x too) leaves fewer workgroups resident
     // (32x32 fp32: 7 instead of 8 per CU).
@@ -209,6 +214,28 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     p->nchunk = grid;
     p->grid = grid;
     p->nrec = 2L * grid;
+    if (a.units) {
+        // (batch chunk, channel) units of ppw planes: the chunk length (a whole
+        // number of plane groups) that minimises rounds x chunk length
+        long best_t = -1;
+        int best_ppw = 1;
+        for (int nc = 1; nc <= d->B; ++nc) {
+            const int pp = std::min(d->B, round_up(cdiv(d->B, nc), NP));
+            const long units = (long)d->C * cdiv(d->B, pp);
+            const long t = (units + slots - 1) / slots * pp;
+            if (best_t < 0 || t < best_t) {
+                best_t = t;
+                best_ppw = pp;
+            }
+        }
+        a.ppw = best_ppw;
+        a.nchunk = cdiv(d->B, a.ppw);
+        const long units = (long)d->C * a.nchunk;
+        if (8 * cdiv((int)std::min<long>(units, 1L << 28), 8) < units) return WTC_ESHAPE;
+        p->nchunk = a.nchunk;
+        p->grid = 8 * cdiv((int)units, 8);   // the units dealt to the 8 XCDs in contiguous ranges
+        p->nrec = units;
+    }
     p->nthr = nthr;
     p->bpq = bpq;
     return WTC_OK;
@@ -386,7 +413,7 @@ int fused_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* 
         f.w0 = w0; f.s0 = s0; f.wl = wl; f.sl = sl;
         f.dw0 = dw0; f.ds0 = ds0; f.db0 = db0; f.dwl = dwl; f.dsl = dsl;
         f.C = d->C; f.B = d->B; f.L = d->L; f.Lm = a.Lm; f.k = d->k; f.ppw = a.ppw; f.P = a.P;
-        f.chunks = p.tiny ? p.nchunk : 0;
+        f.chunks = (p.tiny || a.units) ? p.nchunk : 0;
         e = launch_finalize(f, stream);
         return e == 0 ? WTC_OK : WTC_EHIP;
     }
@@ -453,6 +480,15 @@ int unf_bwd_run(const wtc_desc* d, const void* x, const void* g, const float* w0
 // Channels-last (NHWC) tensors: transposed into NCHW copies at the front of
 // the workspace, computed there, the result transposed back.
 // ---------------------------------------------------------------------------
+// Channels-last tensors read and written in place (layout 2): planes the
+// on-chip pipeline holds, k <= kMaxK.  Layout 1, and layout 2 anywhere else,
+// is adapted through NCHW copies.
+bool nhwc_native(const wtc_desc* d, bool bwd) {
+    if (d->layout != 2 || beyond_fused_k(d)) return false;
+    FusedPlan p;
+    return plan_fused(d, bwd, &p) == WTC_OK;
+}
+
 size_t nhwc_tensor_bytes(const wtc_desc* d) {
     return al256((size_t)d->B * d->C * d->H * d->W * (d->dtype == WTC_BF16 ? 2 : 4));
 }
@@ -626,11 +662,12 @@ const char* wtconv_status_string(int s) {
 
 size_t wtconv_forward_workspace(const wtc_desc* d) {
     if (check_desc(d) != WTC_OK) return 0;
+    if (nhwc_native(d, false)) return 0;
     const wtc_desc n = nchw_of(d);
     int st = WTC_OK;
     const size_t inner = fused_fwd_ws(&n, 0, &st);
     if (st != WTC_OK) return 0;
-    return d->layout == 1 ? 2 * nhwc_tensor_bytes(d) + inner : inner;
+    return d->layout != 0 ? 2 * nhwc_tensor_bytes(d) + inner : inner;
 }
 
 int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const float* s0,
@@ -640,7 +677,7 @@ int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const floa
     if (st != WTC_OK) return st;
     if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
-    if (d->layout == 1)
+    if (d->layout != 0 && !nhwc_native(d, false))
         return nhwc_forward(d, false, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes,
                             stream);
     return fused_fwd_run(d, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes, stream, 0);
@@ -648,11 +685,15 @@ int wtconv_forward(const wtc_desc* d, const void* x, const float* w0, const floa
 
 size_t wtconv_backward_workspace(const wtc_desc* d) {
     if (check_desc(d) != WTC_OK) return 0;
+    if (nhwc_native(d, true)) {
+        int st = WTC_OK;
+        return fused_bwd_ws(d, 0, &st);
+    }
     const wtc_desc n = nchw_of(d);
     int st = WTC_OK;
     const size_t inner = fused_bwd_ws(&n, 0, &st);
     if (st != WTC_OK) return 0;
-    return d->layout == 1 ? 3 * nhwc_tensor_bytes(d) + inner : inner;
+    return d->layout != 0 ? 3 * nhwc_tensor_bytes(d) + inner : inner;
 }
 
 int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -661,7 +702,7 @@ int wtconv_backward(const wtc_desc* d, const void* x, const void* g, const float
                     size_t workspace_bytes, void* stream) {
     const int st = backward_check(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl);
     if (st != WTC_OK) return st;
-    if (d->layout == 1)
+    if (d->layout != 0 && !nhwc_native(d, true))
         return nhwc_backward(d, false, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
                              static_cast<char*>(workspace), workspace_bytes, stream);
     return fused_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, static_cast<char*>(workspace),
@@ -676,7 +717,7 @@ size_t wtconv_forward_unfused_workspace(const wtc_desc* d) {
     const wtc_desc n = nchw_of(d);
     UnfusedPlan p;
     if (unfused_plan(&n, 0, &p) != WTC_OK) return 0;
-    return d->layout == 1 ? 2 * nhwc_tensor_bytes(d) + p.total : p.total;
+    return d->layout != 0 ? 2 * nhwc_tensor_bytes(d) + p.total : p.total;
 }
 
 int wtconv_forward_unfused(const wtc_desc* d, const void* x, const float* w0, const float* s0,
@@ -686,7 +727,7 @@ int wtconv_forward_unfused(const wtc_desc* d, const void* x, const float* w0, co
     if (st != WTC_OK) return st;
     if (!x || !w0 || !s0 || !b0 || !out) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl)) return WTC_EINVAL;
-    if (d->layout == 1)
+    if (d->layout != 0)
         return nhwc_forward(d, true, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes,
                             stream);
     return unf_fwd_run(d, x, w0, s0, b0, wl, sl, out, static_cast<char*>(workspace), workspace_bytes, stream);
@@ -697,7 +738,7 @@ size_t wtconv_backward_unfused_workspace(const wtc_desc* d) {
     const wtc_desc n = nchw_of(d);
     UnfusedPlan p;
     if (unfused_plan(&n, 1, &p) != WTC_OK) return 0;
-    return d->layout == 1 ? 3 * nhwc_tensor_bytes(d) + p.total : p.total;
+    return d->layout != 0 ? 3 * nhwc_tensor_bytes(d) + p.total : p.total;
 }
 
 int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g, const float* w0,
@@ -708,7 +749,7 @@ int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g, con
     if (st != WTC_OK) return st;
     if (!x || !g || !w0 || !s0 || !dx || !dw0 || !ds0 || !db0) return WTC_EINVAL;
     if (d->L > 0 && (!wl || !sl || !dwl || !dsl)) return WTC_EINVAL;
-    if (d->layout == 1)
+    if (d->layout != 0)
         return nhwc_backward(d, true, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl,
                              static_cast<char*>(workspace), workspace_bytes, stream);
     return unf_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, static_cast<char*>(workspace),
@@ -738,6 +779,7 @@ double wtconv_flops(const wtc_desc* d, int dir) {
 
 double wtconv_io_model_bytes(const wtc_desc* d, int impl, int dir) {
     if (check_desc(d) != WTC_OK || (dir != 0 && dir != 1) || (impl != 0 && impl != 1)) return -1.0;
+    if (impl == 0 && nhwc_native(d, dir == 1)) return io_fused(d, dir, 0);   // read and written in place
     const wtc_desc n = nchw_of(d);
     const double t = impl == 0 ? io_fused(&n, dir, 0) : io_unfused(&n, dir);
     if (t < 0 || d->layout == 0) return t;

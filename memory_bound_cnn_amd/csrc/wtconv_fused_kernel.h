@@ -252,6 +252,27 @@ __device__ __forceinline__ void load_w4(const float* p, float (&w)[K * K]) {
     for (int t = 0; t < KK; ++t) w[t] = v[ROT ? (KK - 1 - t) : t];
 }
 
+// Four pixels of one row at pixel stride ps: consecutive (load4 / store4) in
+// NCHW planes, ps = C elements apart in channels-last tensors.
+template <bool NHWC, typename ST>
+__device__ __forceinline__ void gload4(const ST* p, size_t ps, float (&v)[4]) {
+    if constexpr (NHWC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = to_f32(p[i * ps]);
+    } else {
+        load4(p, v);
+    }
+}
+template <bool NHWC, typename ST>
+__device__ __forceinline__ void gstore4(ST* p, size_t ps, const float (&v)[4]) {
+    if constexpr (NHWC) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) from_f32(p[i * ps], v[i]);
+    } else {
+        store4(p, v);
+    }
+}
+
 // Pixel (y, x) of a plane, zero outside [0,H) x [0,W).
 template <typename ST>
 __device__ __forceinline__ float ld_px(const ST* plane, int y, int x, int H, int W) {
@@ -260,17 +281,17 @@ __device__ __forceinline__ float ld_px(const ST* plane, int y, int x, int H, int
 
 // Four pixels starting at `rowp` (= image pixel (y, x), x % 4 == 0); zero where
 // the row is outside the image (row_ok false) or a column is >= W.
-template <bool VEC, typename ST>
-__device__ __forceinline__ void ld_row4(const ST* rowp, bool row_ok, int x, int W, float (&v)[4]) {
+template <bool VEC, bool NHWC = false, typename ST>
+__device__ __forceinline__ void ld_row4(const ST* rowp, bool row_ok, int x, int W, float (&v)[4], size_t ps = 1) {
     if constexpr (VEC) {
         if (row_ok && x < W) {
-            load4(rowp, v);
+            gload4<NHWC>(rowp, ps, v);
         } else {
             v[0] = v[1] = v[2] = v[3] = 0.f;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (row_ok && x + i < W) ? to_f32(rowp[i]) : 0.f;
+        for (int i = 0; i < 4; ++i) v[i] = (row_ok && x + i < W) ? to_f32(rowp[NHWC ? i * ps : i]) : 0.f;
     }
 }
 
@@ -309,9 +330,10 @@ __device__ __forceinline__ float row_sum(float v) {
 // runtime-geometry kernel is compiled for Lm <= 3 (one set) and for any Lm,
 // so that the common shallow plans keep 20 registers free.
 // ---------------------------------------------------------------------------
-template <bool DLM, int LMX>
+template <bool DLM, int LMX, bool NHWC = false>
 struct RtGeom {
     static constexpr bool kDL = DLM;     // planes by DMA (layout mode 1) or staged through registers
+    static constexpr bool kNHWC = NHWC;  // activations channels-last: pixel stride C
     static constexpr bool kXSeg = false;
     static constexpr bool kFixed = false;
     static constexpr bool kNoLevels = false;
@@ -350,10 +372,12 @@ struct RtGeom {
     __device__ int P() const { return a.P; }
 };
 
-template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, int MODE, int ESZ>
+template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, int MODE, int ESZ,
+          bool NHWC = false>
 struct CtGeom {
     static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, MODE, ESZ);
     static constexpr bool kDL = MODE == 1;
+    static constexpr bool kNHWC = NHWC;
     // direct loads may run ahead into the next channel segment: the backward
     // reduction scratch (from offset 0) ends before the first copy target
     static constexpr bool kXSeg =
@@ -484,12 +508,35 @@ wtc_fused_kernel(const FusedArgs a) {
     // This workgroup's planes: [q0, q1) in channel-major order (q = c*B + b),
     // at most two channel segments.
     const long qtot = (long)a.C * a.B;
-    const long q0 = (long)blockIdx.x * a.ppw;
-    const long q1 = min(q0 + (long)a.ppw, qtot);
+    long q0, q1;
+    int unit = 0;
+    if (a.units) {
+        // one (batch chunk, channel) unit, chunk-major, the units dealt to the
+        // XCDs in contiguous ranges (workgroup i runs on XCD i % 8): the planes
+        // of neighbouring channels, which share cache lines (channels-last
+        // tensors, small odd planes), go through one L2 at about the same time
+        const int U = a.C * a.nchunk, per = (U + 7) / 8, k8 = blockIdx.x >> 3;
+        unit = (blockIdx.x & 7) * per + k8;
+        if (k8 >= per || unit >= U) return;   // whole workgroup, before any barrier
+        const int cu = unit % a.C, chunk = unit / a.C;
+        q0 = (long)cu * a.B + (long)chunk * a.ppw;
+        q1 = min(q0 + (long)a.ppw, (long)(cu + 1) * a.B);
+    } else {
+        q0 = (long)blockIdx.x * a.ppw;
+        q1 = min(q0 + (long)a.ppw, qtot);
+    }
     const int c_first = (int)(q0 / a.B);
     const int Lm = g.Lm();
     const bool tail = a.L > Lm;
     const size_t plane_sz = (size_t)a.H * a.W;
+    // global addressing: plane (b, c) starts at b C H W + c (channels-last) or
+    // (b C + c) H W (NCHW); pixel (y, x) of a plane is (y W + x) ps further
+    constexpr bool NHWC = G::kNHWC;
+    static_assert(!(NHWC && DL && sizeof(ST) == 2), "channels-last bf16 planes are staged through registers");
+    const size_t ps = NHWC ? (size_t)a.C : 1;
+    auto plane_at = [&](const ST* base, long b, int ch) {
+        return base + (size_t)b * a.C * plane_sz + (NHWC ? (size_t)ch : (size_t)ch * plane_sz);
+    };
     const FastDiv dqpp = make_div(g.qpp()), dnqx = make_div(g.nqx());
 
     // Per-thread roles.  Recomputed at the top of every plane iteration from an
@@ -562,7 +609,7 @@ wtc_fused_kernel(const FusedArgs a) {
             if (e < g.NP() * per) {
                 const int s2 = fdiv(e, dper), m = e - s2 * per;
                 const int y = fdiv(m, dwv), xq = m - y * wv;
-                pf_goff[k] = s2 * cplane + y * a.W + xq * UW;
+                pf_goff[k] = s2 * cplane + (y * a.W + xq * UW) * (NHWC ? a.C : 1);
                 pf_lds[k] = (s2 << 16) | (s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW);
             }
         }
@@ -570,16 +617,16 @@ wtc_fused_kernel(const FusedArgs a) {
     // issue the global loads of the NP planes starting at batch index bbn
     auto pf_issue = [&](int bbn) {
         if constexpr (VEC) {
-            const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
+            const ST* base = plane_at(srcp, bbn, c);
 #pragma unroll
             for (int k = 0; k < PFU; ++k)
-                if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) load4(base + pf_goff[k], pf[k]);
+                if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) gload4<NHWC>(base + pf_goff[k], ps, pf[k]);
         } else if constexpr (G::kFixed) {
             // unit k: plane k % NP, in-plane pixel tid + (k / NP) * nthr, so one
             // row/column decode serves the NP planes (NP is a constant here; the
             // planner prefetches only when NP * ceil(H W / nthr) units fit)
             constexpr int NPc = G::NP(), NJ = (PFU + NPc - 1) / NPc;
-            const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
+            const ST* base = plane_at(srcp, bbn, c);
 #pragma unroll
             for (int jj = 0; jj < NJ; ++jj) {
                 const int m = tid + jj * nthr;
@@ -591,13 +638,13 @@ wtc_fused_kernel(const FusedArgs a) {
                     if (k >= PFU) continue;
                     pf_dst[k] = -1;
                     if (m < per && bbn + s2 < b_end) {
-                        pf[k][0] = to_f32(base[s2 * cplane + m]);
+                        pf[k][0] = to_f32(base[s2 * cplane + m * ps]);
                         pf_dst[k] = s2 * g.slot() + dst0;
                     }
                 }
             }
         } else {
-            const ST* base = srcp + ((size_t)bbn * a.C + c) * plane_sz;
+            const ST* base = plane_at(srcp, bbn, c);
 #pragma unroll
             for (int k = 0; k < PFU; ++k) {
                 const int e = tid + k * nthr;
@@ -605,7 +652,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 if (e < g.NP() * per) {
                     const int s2 = fdiv(e, dper), m = e - s2 * per;
                     if (bbn + s2 < b_end) {
-                        pf[k][0] = to_f32(base[s2 * cplane + m]);
+                        pf[k][0] = to_f32(base[s2 * cplane + m * ps]);
                         const int y = fdiv(m, dwv), xq = m - y * wv;
                         pf_dst[k] = s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq;
                     }
@@ -652,7 +699,7 @@ wtc_fused_kernel(const FusedArgs a) {
                     if (!decltype(full)::value && r >= a.H) continue;
                     if (NPc > 1 && bbn + s2 >= bend) continue;
                     __builtin_amdgcn_global_load_lds(
-                        (const void*)(base + ((size_t)(bbn + s2) * a.C + ch) * plane_sz + (size_t)r * a.W + lane),
+                        (const void*)(plane_at(base, bbn + s2, ch) + ((size_t)r * a.W + lane) * ps),
                         (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc),
                         4, 0, 0);
                 }
@@ -669,13 +716,13 @@ wtc_fused_kernel(const FusedArgs a) {
             // (lane from an opaque copy: no per-lane address is kept live across the plane loop)
             const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = opaque(tid0) & 63;
             const int nw = nthr >> 6;
-            const ST* pb = base + ((size_t)bbn * a.C + ch) * plane_sz;
+            const ST* pb = plane_at(base, bbn, ch);
             float* lb = lds + roff + rr * rS + rc;
             for (int c0 = 0; c0 < a.W; c0 += 64) {
                 if (c0 + lane >= a.W) break;
-                const ST* src = pb + (size_t)wave * a.W + c0 + lane;
+                const ST* src = pb + ((size_t)wave * a.W + c0 + lane) * ps;
                 float* dst = lb + wave * rS + c0;
-                for (int r = wave; r < a.H; r += nw, src += (size_t)nw * a.W, dst += nw * rS)
+                for (int r = wave; r < a.H; r += nw, src += (size_t)nw * a.W * ps, dst += nw * rS)
                     __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
                                                      4, 0, 0);
             }
@@ -799,7 +846,7 @@ wtc_fused_kernel(const FusedArgs a) {
         const int b = bb + slot;
         const bool pok = (slot < g.NP()) && (b < b_end);
         float* S = lds + (slot < g.NP() ? slot : 0) * g.slot();
-        const size_t poff = ((size_t)b * a.C + c) * plane_sz;
+        const size_t poff = (size_t)b * a.C * plane_sz + (NHWC ? (size_t)c : (size_t)c * plane_sz);
 
         if constexpr (DL) {
             // this plane's direct loads have landed (every wave's), and the
@@ -838,11 +885,11 @@ wtc_fused_kernel(const FusedArgs a) {
                 const int s2 = fdiv(e, dper), m = e - s2 * per;
                 if (bb + s2 >= b_end) continue;
                 const int y = fdiv(m, dwv), xq = m - y * wv;
-                const ST* pl = srcp + ((size_t)(bb + s2) * a.C + c) * plane_sz + (size_t)y * a.W + xq * UW;
+                const ST* pl = plane_at(srcp, bb + s2, c) + ((size_t)y * a.W + xq * UW) * ps;
                 float* d = lds + s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW;
                 if constexpr (VEC) {
                     float v[4];
-                    load4(pl, v);
+                    gload4<NHWC>(pl, ps, v);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) d[i] = v[i];
                 } else {
@@ -910,9 +957,10 @@ wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lds_row<4, 4>(xr + i * g.xp_S(), xo[i]);
             } else if constexpr (BWD) {
-                const ST* xp = auxp + poff + opaque(py0 * a.W + px0);
+                const ST* xp = auxp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) ld_row4<VEC>(xp + i * a.W, py0 + i < a.H, px0, a.W, xo[i]);
+                for (int i = 0; i < 4; ++i)
+                    ld_row4<VEC, NHWC>(xp + (size_t)i * a.W * ps, py0 + i < a.H, px0, a.W, xo[i], ps);
                 if constexpr (XQB) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -1044,7 +1092,7 @@ wtc_fused_kernel(const FusedArgs a) {
             if constexpr (BWD) {
                 // x over the quad's 8x8 block -> band t (and LL) at levels 1, 2, 3
                 float ll1[4][4];
-                const ST* xp = auxp + poff + opaque(8 * qy * a.W + 8 * qx);
+                const ST* xp = auxp + poff + (size_t)opaque(8 * qy * a.W + 8 * qx) * ps;
 #pragma unroll
                 for (int jy = 0; jy < 4; ++jy) {
                     float r0[2][4], r1[2][4];
@@ -1061,11 +1109,11 @@ wtc_fused_kernel(const FusedArgs a) {
                         if (jy == 2) quad_rows<2>(xkeep, r0, r1);
                         if (jy == 3) quad_rows<3>(xkeep, r0, r1);
                     } else {
-                    const ST* p0r = xp + (2 * jy) * a.W;
-                    ld_row4<VEC>(p0r, y0 < a.H, 8 * qx, a.W, r0[0]);
-                    ld_row4<VEC>(p0r + 4, y0 < a.H, 8 * qx + 4, a.W, r0[1]);
-                    ld_row4<VEC>(p0r + a.W, y0 + 1 < a.H, 8 * qx, a.W, r1[0]);
-                    ld_row4<VEC>(p0r + a.W + 4, y0 + 1 < a.H, 8 * qx + 4, a.W, r1[1]);
+                    const ST* p0r = xp + (size_t)(2 * jy) * a.W * ps;
+                    ld_row4<VEC, NHWC>(p0r, y0 < a.H, 8 * qx, a.W, r0[0], ps);
+                    ld_row4<VEC, NHWC>(p0r + 4 * ps, y0 < a.H, 8 * qx + 4, a.W, r0[1], ps);
+                    ld_row4<VEC, NHWC>(p0r + (size_t)a.W * ps, y0 + 1 < a.H, 8 * qx, a.W, r1[0], ps);
+                    ld_row4<VEC, NHWC>(p0r + (size_t)(a.W + 4) * ps, y0 + 1 < a.H, 8 * qx + 4, a.W, r1[1], ps);
                     }
 #pragma unroll
                     for (int jx = 0; jx < 4; ++jx) {
@@ -1284,11 +1332,17 @@ wtc_fused_kernel(const FusedArgs a) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[s][i][j] = fmaf(wbase[KK + 1], acc[s][i][j], z[i][j]);
-            ST* op = dstp + poff + opaque(py0 * a.W + px0);
+            ST* op = dstp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
             if constexpr (VEC) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (py0 + i < a.H && px0 < a.W) store4(op + i * a.W, acc[s][i]);
+                    if (py0 + i < a.H && px0 < a.W) gstore4<NHWC>(op + (size_t)i * a.W * ps, ps, acc[s][i]);
+            } else if (NHWC) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (py0 + i < a.H && px0 + j < a.W) from_f32(op[((size_t)i * a.W + j) * ps], acc[s][i][j]);
             } else if ((a.W & 1) == 0) {
                 // even width: pixel pairs
 #pragma unroll
@@ -1363,7 +1417,7 @@ wtc_fused_kernel(const FusedArgs a) {
                     for (int kx = 0; kx < K; ++kx) dred[(q * droles + drole) * K + kx] = cdeep[q][kx];
         }
         lds_barrier();
-        float* rec = a.partials + ((size_t)blockIdx.x * 2 + seg) * g.P();
+        float* rec = a.partials + (a.units ? (size_t)unit : (size_t)blockIdx.x * 2 + seg) * g.P();
         for (int e = tid; e < g.P(); e += nthr) {
             float v = 0.f;
             if (e < KK) {
@@ -1403,29 +1457,29 @@ hipError_t launch_t(const FusedArgs& a, int nthr, size_t lds, int grid, hipStrea
     return hipGetLastError();
 }
 
-// Runtime-geometry kernel for any plane the LDS pipeline holds.  Plans of
-// layout mode 1 copy their planes by DMA (4-pixel rows, one block per quad,
-// one plane per workgroup; fp32, or a bf16 backward); everything else is
-// staged through registers.  The backward comes in two deep-level classes
-// (Lm <= 3, any Lm).
-template <int K>
-hipError_t launch_rt(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
-                     hipStream_t st) {
+// Runtime-geometry kernel of one activation layout (NH: channels-last).
+template <int K, bool NH>
+hipError_t launch_rt_l(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
+                       hipStream_t st) {
     if (a.Lm > kMaxLm) return hipErrorInvalidValue;
     const bool shallow = a.Lm <= 3;
     if (a.lay.dl) {
         if (!a.vec || bpq != 1 || a.NP != 1 || (dtype == WTC_BF16 && !bwd)) return hipErrorInvalidValue;
-        if (!bwd) return launch_t<K, float, false, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
+        if (!bwd) return launch_t<K, float, false, 1, true, RtGeom<true, kMaxLm, NH>>(a, nthr, lds, grid, st);
         if (dtype == WTC_BF16) {
-            if (shallow) return launch_t<K, bf16_t, true, 1, true, RtGeom<true, 3>>(a, nthr, lds, grid, st);
-            return launch_t<K, bf16_t, true, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
+            if constexpr (NH) {
+                return hipErrorInvalidValue;   // channels-last bf16 planes are staged through registers
+            } else {
+                if (shallow) return launch_t<K, bf16_t, true, 1, true, RtGeom<true, 3>>(a, nthr, lds, grid, st);
+                return launch_t<K, bf16_t, true, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
+            }
         }
-        if (shallow) return launch_t<K, float, true, 1, true, RtGeom<true, 3>>(a, nthr, lds, grid, st);
-        return launch_t<K, float, true, 1, true, RtGeom<true, kMaxLm>>(a, nthr, lds, grid, st);
+        if (shallow) return launch_t<K, float, true, 1, true, RtGeom<true, 3, NH>>(a, nthr, lds, grid, st);
+        return launch_t<K, float, true, 1, true, RtGeom<true, kMaxLm, NH>>(a, nthr, lds, grid, st);
     }
 #define WTC_RT(ST_, BWD_, LMX_)                                                                           \
     do {                                                                                                 \
-        using G_ = RtGeom<false, LMX_>;                                                                  \
+        using G_ = RtGeom<false, LMX_, NH>;                                                              \
         if (a.vec) {                                                                                     \
             if (bpq == 1) return launch_t<K, ST_, BWD_, 1, true, G_>(a, nthr, lds, grid, st);            \
             return launch_t<K, ST_, BWD_, 2, true, G_>(a, nthr, lds, grid, st);                          \
@@ -1444,6 +1498,18 @@ hipError_t launch_rt(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, 
 #undef WTC_RT
 }
 
+// Runtime-geometry kernel for any plane the LDS pipeline holds.  Plans of
+// layout mode 1 copy their planes by DMA (4-pixel rows, one block per quad,
+// one plane per workgroup; fp32, or a bf16 backward of NCHW tensors);
+// everything else is staged through registers.  The backward comes in two
+// deep-level classes (Lm <= 3, any Lm).  NCHW and channels-last tensors.
+template <int K>
+hipError_t launch_rt(const FusedArgs& a, int dtype, int bwd, int bpq, int nthr, size_t lds, int grid,
+                     hipStream_t st) {
+    return a.nhwc ? launch_rt_l<K, true>(a, dtype, bwd, bpq, nthr, lds, grid, st)
+                  : launch_rt_l<K, false>(a, dtype, bwd, bpq, nthr, lds, grid, st);
+}
+
 }  // namespace fused_detail
 }  // namespace wtc
 
@@ -1452,14 +1518,16 @@ namespace fused_detail {
 
 // Launch the fixed-geometry instantiation if the plan matches it exactly.
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
-          int NTHR, int BOVL, int MODE = 0>
+          int NTHR, int BOVL, int MODE = 0, bool NH = false>
 bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
                 hipError_t* err) {
     if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
-        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || a.lay.mode != MODE)
+        nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || a.lay.mode != MODE ||
+        (a.nhwc != 0) != NH)
         return false;
-    *err = launch_t<K, ST, BWD, BPQ, VEC, CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST)>>(
-        a, nthr, lds, grid, st);
+    *err = launch_t<K, ST, BWD, BPQ, VEC,
+                    CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST), NH>>(a, nthr, lds, grid,
+                                                                                                 st);
     return true;
 }
 

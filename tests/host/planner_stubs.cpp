@@ -51,13 +51,14 @@ int launch_fused(const FusedArgs& a, int k, int dtype, int bwd, int bpq, int nth
     need(bpq == 1 || bpq == 2, "blocks per quad");
     need(lds_bytes <= 160 * 1024, "LDS");
     need(grid >= 1 && (long)grid * a.ppw >= (long)a.B * a.C, "grid covers every plane");
+    need(!a.units || (grid % 8 == 0 && (long)a.nchunk * a.ppw >= a.B && grid >= a.C * a.nchunk), "unit grid");
     need(a.NP >= 1 && a.Lm <= kMaxLm && a.Hq % 8 == 0 && a.Wq % 8 == 0, "plane geometry");
     need((size_t)(a.NP * a.lay.slot) * 4 <= lds_bytes, "plane slots fit");
     rd(a.src, act_bytes(a, dtype));
     if (bwd) rd(a.aux, act_bytes(a, dtype));
     params(a, k, bwd);
     wr(a.dst, act_bytes(a, dtype));
-    if (bwd) wr(a.partials, sizeof(float) * 2 * (size_t)grid * a.P);
+    if (bwd) wr(a.partials, sizeof(float) * (a.units ? (size_t)a.C * a.nchunk : 2 * (size_t)grid) * a.P);
     return 0;
 }
 

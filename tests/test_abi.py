@@ -39,7 +39,8 @@ FAKE = ctypes.c_void_p(16)   # never dereferenced: every case below fails valida
 @pytest.mark.parametrize("kw,status", [
     (dict(k=4), binding.WTC_EINVAL), (dict(k=0), binding.WTC_EINVAL), (dict(L=-1), binding.WTC_EINVAL),
     (dict(B=0), binding.WTC_EINVAL), (dict(H=0), binding.WTC_EINVAL), (dict(dtype=7), binding.WTC_EDTYPE),
-    (dict(layout=2), binding.WTC_EDTYPE), (dict(layout=1), binding.WTC_EWORKSPACE),
+    (dict(layout=3), binding.WTC_EDTYPE),
+    (dict(layout=1, H=512, W=512), binding.WTC_EWORKSPACE),   # channels-last beyond the pipeline: adapted
     (dict(H=512, W=512), binding.WTC_EWORKSPACE),
     (dict(k=33), binding.WTC_ESHAPE),
     (dict(k=9), binding.WTC_EWORKSPACE),   # k = 9..31 runs the level-by-level kernels: it needs a workspace
@@ -189,63 +190,35 @@ def test_large_planes_take_the_peeled_path():
 
 
 def test_channels_last_workspace_and_model():
-    """Channels-last tensors are transposed into NCHW copies at the front of
-    the workspace: forward two tensors, backward three, on top of the NCHW needs."""
+    """Channels-last tensors: layout 1 goes through NCHW copies at the front of
+    the workspace (forward two tensors, backward three; four / six extra
+    tensor passes of traffic); layout 2 reads and writes them in place for
+    planes the on-chip pipeline holds (the NCHW workspace -- none forward, the
+    partial records backward -- and the NCHW traffic), and is adapted like
+    layout 1 beyond them.  The level-by-level baseline always adapts."""
     B, C, H, W, L, k = 4, 6, 64, 64, 3, 5
     t = B * C * H * W * 4
-    assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=1) == \
-        2 * t + binding.wtconv_forward_workspace(B, C, H, W, L, k)
-    assert binding.wtconv_backward_workspace(B, C, H, W, L, k, layout=1) == \
-        3 * t + binding.wtconv_backward_workspace(B, C, H, W, L, k)
-    assert binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16", layout=1) == \
-        3 * (t // 2) + binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16")
-    for direction, extra in ((0, 4), (1, 6)):
-        assert binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction, layout=1) == \
-            binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction) + extra * t
+    for Hx, Wx in ((H, W), (200, 200)):
+        tx = B * C * Hx * Wx * 4
+        assert binding.wtconv_forward_workspace(B, C, Hx, Wx, L, k, layout=1) == \
+            2 * tx + binding.wtconv_forward_workspace(B, C, Hx, Wx, L, k)
+        assert binding.wtconv_backward_workspace(B, C, Hx, Wx, L, k, layout=1) == \
+            3 * tx + binding.wtconv_backward_workspace(B, C, Hx, Wx, L, k)
+        for direction, extra in ((0, 4), (1, 6)):
+            assert binding.wtconv_io_model_bytes(B, C, Hx, Wx, L, k, impl=0, direction=direction, layout=1) == \
+                binding.wtconv_io_model_bytes(B, C, Hx, Wx, L, k, impl=0, direction=direction) + extra * tx
+    # in place
     assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=2) == 0
-
-
-def test_noalloc_checks_before_any_hip_call():
-    """wtconv_backward_noalloc: argument checks, then the scratch limit, both
-    before any HIP call (so they hold on a host without a GPU)."""
-    lib = binding.load_library()
-    d = _desc(k=4)
-    args = [FAKE] * 12 + [None]
-    assert lib.wtconv_backward_noalloc(ctypes.byref(d), *args) == binding.WTC_EINVAL
-    d = _desc()
-    assert lib.wtconv_backward_noalloc(ctypes.byref(d), None, *args[1:]) == binding.WTC_EINVAL
-    # a plane beyond the on-chip pipeline needs far more than the fixed array
-    d = _desc(B=8, C=64, H=224, W=224, L=3)
-    assert lib.wtconv_backward_workspace(ctypes.byref(d)) > binding.NOALLOC_SCRATCH_BYTES
-    assert lib.wtconv_backward_noalloc(ctypes.byref(d), *args) == binding.WTC_ESCRATCH
-    # channels-last needs three tensor copies of workspace
-    d = _desc(B=32, C=96, H=64, W=64, L=3, layout=1)
-    assert lib.wtconv_backward_noalloc(ctypes.byref(d), *args) == binding.WTC_ESCRATCH
-    assert binding.wtconv_status_string(binding.WTC_ESCRATCH) != binding.wtconv_status_string(42)
-
-
-def test_noalloc_scratch_covers_the_benchmark_shapes():
-    """The fixed scratch holds the backward partial records of every benchmark
-    workload whose planes the on-chip pipeline holds."""
-    from memory_bound_cnn_amd.inputs import WORKLOADS
-    for w in WORKLOADS.values():
-        for L in (w.sweep or (w.L,)):
-            need = binding.wtconv_backward_workspace(w.B, w.C, w.H, w.W, L, w.k, w.dtype)
-            if w.H <= 128 and w.W <= 128:
-                assert need <= binding.NOALLOC_SCRATCH_BYTES, (w.name, L, need)
-
-
-def test_kernel_sizes_beyond_the_fused_kernels():
-    """k = 9..31 runs the level-by-level kernels through the fused entry points:
-    their workspace queries and I/O model are the level-by-level ones."""
-    for k in (9, 11, 31):
-        for L in (0, 2):
-            for fn, fu in (("wtconv_forward_workspace", "wtconv_forward_unfused_workspace"),
-                           ("wtconv_backward_workspace", "wtconv_backward_unfused_workspace")):
-                a = getattr(binding, fn)(2, 3, 40, 24, L, k)
-                b = getattr(binding, fu)(2, 3, 40, 24, L, k)
-                assert a == b, (k, L, fn)
-            for dr in (0, 1):
-                assert binding.wtconv_io_model_bytes(2, 3, 40, 24, L, k, impl=0, direction=dr) == \
-                    binding.wtconv_io_model_bytes(2, 3, 40, 24, L, k, impl=1, direction=dr)
-    assert binding.wtconv_backward_workspace(2, 3, 40, 24, 2, 33) == 0
+    nb = binding.wtconv_backward_workspace(B, C, H, W, L, k, layout=2)
+    assert 0 < nb < t
+    for direction in (0, 1):
+        assert binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction, layout=2) <= \
+            binding.wtconv_io_model_bytes(B, C, H, W, L, k, impl=0, direction=direction) * 1.01
+    tb = B * C * 200 * 200 * 4   # beyond the pipeline: adapted
+    assert binding.wtconv_forward_workspace(B, C, 200, 200, L, k, layout=2) == \
+        2 * tb + binding.wtconv_forward_workspace(B, C, 200, 200, L, k)
+    # the baseline adapts every layout
+    for lay in (1, 2):
+        assert binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16", layout=lay) == \
+            3 * (t // 2) + binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16")
+    assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=3) == 0

@@ -314,25 +314,40 @@ def test_large_planes(B, C, H, W, L, k, seed, dtype):
     _case(B, C, H, W, L, k, seed, dtype)
 
 
-# Channels-last (NHWC) tensors: transposed into NCHW copies in the workspace by
-# the library, results transposed back; values identical to the NCHW call.
+# Channels-last (NHWC) tensors: through NCHW copies in the workspace (layout 1,
+# both implementations), or read and written in place by the fused plane
+# pipeline for every plane it holds (layout 2: one (batch chunk, channel) unit
+# per workgroup; planes beyond it are adapted).  Every staging path of the pipeline: DMA rows
+# (fp32, fixed and runtime geometry), register prefetch and synchronous
+# staging (bf16, rows not a multiple of 4 pixels), two blocks per quad.
 CHANNELS_LAST = [
-    (2, 6, 64, 64, 3, 5, 90, "fp32"),
-    (2, 5, 32, 32, 3, 5, 91, "bf16"),
-    (3, 7, 14, 14, 2, 5, 92, "fp32"),
-    (5, 20, 7, 7, 1, 5, 93, "fp32"),       # register-resident small-plane kernel
-    (1, 3, 200, 150, 2, 5, 94, "fp32"),    # peeled plane
+    (2, 6, 64, 64, 3, 5, 90, "fp32"),      # fixed geometry, DMA rows
+    (2, 5, 32, 32, 3, 5, 91, "bf16"),      # bf16: staged through registers
+    (3, 7, 14, 14, 2, 5, 92, "fp32"),      # several planes per workgroup, rows of 14 pixels
+    (5, 20, 7, 7, 1, 5, 93, "fp32"),       # the 7 x 7 class in the plane pipeline
+    (1, 3, 200, 150, 2, 5, 94, "fp32"),    # peeled plane: adapted through NCHW copies
+    (3, 4, 48, 48, 3, 5, 96, "fp32"),      # runtime geometry, DMA rows
+    (2, 3, 13, 10, 3, 3, 97, "fp32"),      # ragged, k = 3
+    (1, 2, 128, 128, 2, 5, 98, "fp32"),    # two blocks per quad
+    (2, 4, 64, 64, 2, 5, 99, "bf16"),      # bf16 64 x 64
+    (4, 3, 24, 24, 0, 7, 100, "fp32"),     # L = 0, k = 7
+    (35, 17, 8, 8, 2, 5, 101, "fp32"),     # many units, odd channel count
 ]
 
 
-@pytest.mark.parametrize("impl", ["fused", "unfused"])
+@pytest.mark.parametrize("impl", ["fused", "fused_in_place", "unfused"])
 @pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", CHANNELS_LAST)
 def test_channels_last(impl, B, C, H, W, L, k, seed, dtype):
     d = inputs(B, C, H, W, L, k, seed, dtype)
     t = to_dev(d, dtype, L)
     for key in ("x", "g"):
         t[key] = t[key].contiguous(memory_format=torch.channels_last)
-    out, gr = run_fused(t, L, impl)
+    if impl == "fused_in_place":
+        out = binding.wtconv_forward(t["x"], t["w0"], t["s0"], t["b0"], t["wl"], t["sl"], L, in_place=True)
+        gr = binding.wtconv_backward(t["x"], t["g"], t["w0"], t["s0"], t["wl"], t["sl"], L, in_place=True)
+        torch.cuda.synchronize()
+    else:
+        out, gr = run_fused(t, L, impl)
     if C > 1 and H * W > 1:
         assert not out.is_contiguous() and out.is_contiguous(memory_format=torch.channels_last)
     ref_out, ref_gr = oracle_ref(d, L)
@@ -345,3 +360,29 @@ def test_mixed_layouts_rejected():
     g_cl = t["g"].contiguous(memory_format=torch.channels_last)
     with pytest.raises(ValueError):
         binding.wtconv_backward(t["x"], g_cl, t["w0"], t["s0"], t["wl"], t["sl"], 1)
+
+
+def test_channels_last_full_size():
+    """The 32 x 96 x 64 x 64, L = 3 block in channels-last at full size, through
+    NCHW copies and in place: out and dx bit-identical to the NCHW call (same
+    arithmetic per plane, only the addressing differs), weight gradients
+    against the whole-batch oracle."""
+    wl_ = WORKLOADS["stage1_b32c96_64x64_L3"]
+    L = wl_.L
+    d = workload_inputs(wl_)
+    ref_w, sha = _golden(f"{wl_.name}_L{L}")
+    assert _inputs_sha256(d, L) == sha
+    t = to_dev(d, wl_.dtype, L)
+    out_n, gr_n = run_fused(t, L)
+    tc = dict(t)
+    for key in ("x", "g"):
+        tc[key] = t[key].contiguous(memory_format=torch.channels_last)
+    for in_place in (False, True):
+        out_c = binding.wtconv_forward(tc["x"], t["w0"], t["s0"], t["b0"], t["wl"], t["sl"], L, in_place=in_place)
+        gr_c = binding.wtconv_backward(tc["x"], tc["g"], t["w0"], t["s0"], t["wl"], t["sl"], L, in_place=in_place)
+        torch.cuda.synchronize()
+        assert out_c.is_contiguous(memory_format=torch.channels_last)
+        assert torch.equal(out_c.contiguous(), out_n), in_place
+        assert torch.equal(gr_c["dx"].contiguous(), gr_n["dx"]), in_place
+        errs = {k: rel_err(host(gr_c[k]), ref) for k, ref in ref_w.items()}
+        assert all(v <= 1e-4 for v in errs.values()), (in_place, errs)
