@@ -191,6 +191,14 @@ struct FusedArgs {
     int P;             // partial record length (floats)
 };
 
+// Floats of the per-row base-correlation accumulators (after the weights) of
+// the backward kernel with two blocks per quad and three levels or more: it
+// adds each plane's C_0 into them (one 16-lane row per slot set) instead of
+// holding 25 accumulators per lane across the plane, which spilled.
+constexpr int flush_len(bool bwd, int bpq, int nthr, int k, int Lm) {
+    return (bwd && bpq > 1 && Lm >= 3) ? (nthr / 16) * k * k : 0;
+}
+
 // Waves per SIMD the fused kernels are compiled for (register budget 512 /
 // waves): 3 forward, 2 backward or with two blocks per quad; the
 // fixed-geometry kernels without wavelet levels (a plain depthwise conv) are

@@ -126,7 +126,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     auto consider = [&](const Layout& lay, int NP, int nthr, int bpq) {
         const int dsub = std::max(1, nthr / (4 * k));
         const int red_n = red_len(nthr, k, a.Lm, dsub);
-        const size_t lds = (size_t)std::max(NP * lay.slot + wts_n, bwd ? red_n : 0) * 4;
+        const size_t lds = (size_t)std::max(NP * lay.slot + wts_n + flush_len(bwd, bpq, nthr, k, a.Lm), bwd ? red_n : 0) * 4;
         if (lds > kLdsLimit || NP * per_units >= 65536) return;   // fast in-kernel division range
         // plain depthwise conv (no levels) on a plane class with fixed-geometry
         // direct-load instances: those are compiled for more waves per SIMD
@@ -197,7 +197,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     // reduction scratch reuses the plane slots after the last plane
     a.red_off = 0;
     const int red_n = red_len(nthr, k, a.Lm, a.dsub);
-    size_t lds_floats = (size_t)std::max(NP * slot + wts_n, bwd ? red_n : 0);
+    size_t lds_floats = (size_t)std::max(NP * slot + wts_n + flush_len(bwd, bpq, nthr, k, a.Lm), bwd ? red_n : 0);
     p->lds = lds_floats * 4;
     if (p->lds > kLdsLimit) return WTC_ESHAPE;
 

@@ -817,6 +817,13 @@ wtc_fused_kernel(const FusedArgs a) {
         wbase[KK] = BWD ? 0.f : a.b0[c];
         wbase[KK + 1] = a.s0[c];
     }
+    // two blocks per quad, backward, three levels or more (where 25 persistent
+    // accumulators spilled): per-row C_0 accumulators after the weights (rows
+    // of 16 lanes; each slot has one writer, lane 15 of its row)
+    const bool flush0 = BWD && BPQ > 1 && Lm >= 3;
+    float* c0acc = wts + ((KKP * 4 * a.L + KK + 4 + 3) & ~3);
+    if (flush0)
+        for (int e = tid; e < (nthr >> 4) * KK; e += nthr) c0acc[e] = 0.f;
 
     lds_barrier();
     // tail levels (1x1 grids): kappa = sum of their folded centre taps
@@ -1017,6 +1024,20 @@ wtc_fused_kernel(const FusedArgs a) {
                 // every level is a 1x1 grid: the tail term enters at pixel (0, 0)
                 S[g.tail_off()] = ctr[0][0] * kappa;
                 if constexpr (BWD) tailc = fmaf(ctr[0][0], xo[0][0], tailc);
+            }
+        }
+        if (flush0) {
+            // this plane's C_0 into the row accumulators: the 25 accumulators
+            // are live through phase 2 only, not across the levels.  A
+            // no-return LDS add per value; each slot has a single writer, so
+            // the order of the sums is fixed.
+            const int crow = tid >> 4;
+#pragma unroll
+            for (int q = 0; q < KK; ++q) {
+                const float v = row_sum(corr0[q]);
+                if ((tid & 15) == 15)
+                    __hip_atomic_fetch_add(c0acc + crow * KK + q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                corr0[q] = 0.f;
             }
         }
         if (g.bovl() >= 1 && g.bovl() <= Lm) {
@@ -1404,7 +1425,7 @@ wtc_fused_kernel(const FusedArgs a) {
             }
             if (u == 3) {
 #pragma unroll
-                for (int q = 0; q < KK; ++q) r0[row * KK + (KK - 1 - q)] = corr0[q];
+                for (int q = 0; q < KK; ++q) r0[row * KK + (KK - 1 - q)] = flush0 ? c0acc[row * KK + q] : corr0[q];
                 rs[row] = sumg;
                 rt[row] = tailc;
             }
