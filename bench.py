@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--profile-only", default="both", choices=["both", "fwd", "bwd"],
                    help="with --profile-steps: call only the forward or only the backward entry point, so "
                         "that every library kernel of the run belongs to that direction")
+    p.add_argument("--corr-calls", type=int, default=None,
+                   help="run only the base-correlation comparison with this many calls per path (kernel traces)")
     p.add_argument("--copy-probe-mib", type=int, default=None,
                    help="run a plain device copy (read N + write N bytes) 3 times, to calibrate "
                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known traffic")
@@ -241,6 +243,42 @@ def channels_last_comparison(torch, binding):
         row["nhwc_inplace_over_nchw"] = round(row["nhwc_inplace"]["ms"] / row["nchw"]["ms"], 3)
         res.append(row)
         torch.cuda.empty_cache()
+    return res
+
+
+def base_correlation_comparison(torch, binding, calls=50, profile=False):
+    """The base level's weight-gradient correlation on its own, on the bf16
+    workload's shape (64 x 192 planes of 32 x 32, k = 5): the vector-unit
+    correlation tiles of the level-by-level path against the matrix-core
+    kernel, us per call and the rate of reading x and g once.  profile: just
+    run the calls (for a kernel trace)."""
+    from memory_bound_cnn_amd.inputs import WORKLOADS
+    w = WORKLOADS["bf16_b64c192_32x32_L3"]
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    x = torch.randn(w.B, w.C, w.H, w.W, device="cuda", generator=gen).to(torch.bfloat16)
+    g = torch.randn(w.B, w.C, w.H, w.W, device="cuda", generator=gen).to(torch.bfloat16)
+    res = {"shape": {"B": w.B, "C": w.C, "H": w.H, "W": w.W, "k": w.k, "storage": "bf16"},
+           "bytes_per_call": 2 * x.numel() * 2}
+    outs = {}
+    for label, impl in (("valu", binding.CORR_VALU), ("mfma", binding.CORR_MFMA)):
+        out = torch.empty(w.C, w.k, w.k, device="cuda")
+        ws = torch.empty(binding.wtconv_base_correlation_workspace(w.B, w.C, w.H, w.W, w.k, "bf16", impl),
+                         dtype=torch.uint8, device="cuda")
+        for _ in range(3 if not profile else 0):
+            binding.wtconv_base_correlation(x, g, w.k, impl, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(calls):
+            binding.wtconv_base_correlation(x, g, w.k, impl, out=out, workspace=ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) / calls * 1e3
+        res[label] = {"us": round(us, 2), "gbps": round(res["bytes_per_call"] / (us * 1e-6) / 1e9, 1)}
+        outs[label] = out
+    ref = outs["valu"]
+    res["mfma_over_valu_max_rel_diff"] = float((outs["mfma"] - ref).abs().max() / ref.pow(2).mean().sqrt())
+    res["mfma_speedup"] = round(res["valu"]["us"] / res["mfma"]["us"], 2)
     return res
 
 
@@ -511,13 +549,18 @@ def main():
 
     # The CPU baseline runs first, before this process touches the GPU.
     cpu = None
-    if not a.no_cpu_baseline and a.profile_steps is None and a.copy_probe_mib is None:
+    if not a.no_cpu_baseline and a.profile_steps is None and a.copy_probe_mib is None and a.corr_calls is None:
         cpu = cpu_baseline(wl, L, (io_f + io_b) / wl.B)
         cpu["value"] = round(cpu["value"], 4)
 
     import torch
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
+
+    if a.corr_calls is not None:
+        print(json.dumps({"base_correlation_comparison":
+                          base_correlation_comparison(torch, binding, calls=a.corr_calls, profile=True)}))
+        return
 
     if a.copy_probe_mib is not None:
         if a.copy_probe_mib != COPY_PROBE_MIB:
@@ -644,6 +687,7 @@ def main():
         line["per_workload"] = summary
         line["dwconv_comparison"] = dwconv_comparison(wl, torch, binding, a.torch_dwconv)
         line["channels_last_comparison"] = channels_last_comparison(torch, binding)
+        line["base_correlation_comparison"] = base_correlation_comparison(torch, binding)
         line["training_step_memory"] = memory_comparison(wl, L, torch, binding)
 
     if cpu is not None:

@@ -150,6 +150,29 @@ int wtconv_backward_noalloc(const wtc_desc* d, const void* x, const void* g,
                             void* dx, float* dw0, float* ds0, float* db0,
                             float* dwl, float* dsl, void* stream);
 
+/* The base level's weight-gradient correlation on its own,
+ *   c0[c][ky][kx] = sum_{b,p} g[b,c,p] * x[b,c,p + (ky - k/2, kx - k/2)]   (x zero outside),
+ * so that dW0 = s0 * c0 (the correlation the backward pass reduces for the base
+ * depthwise convolution of the operator; "Fast and Memory-Efficient Wavelet
+ * Convolutions via I/O-Aware Reformulation", arXiv 2608.10805, Abstract).  Two
+ * implementations of the same sum, for comparing the vector units with the
+ * matrix cores (the windowed batched-matmul formulation of a depthwise
+ * convolution: "WBMM: Windowed Batch Matrix Multiplication ..." review,
+ * core claim):
+ *   impl 0: the level-by-level baseline's register-blocked correlation tiles
+ *           on the vector units (any dtype, k <= 31);
+ *   impl 1: the gfx950 matrix cores, one 16 x 16 x 32 bf16 product per
+ *           32-pixel segment of J rows (J = 16, 5, 3, 2 for k = 1, 3, 5, 7)
+ *           accumulating every tap (dtype WTC_BF16 -- exact products --,
+ *           k <= 7, H and W <= 64).
+ * NCHW only (layout 0).  x, g device tensors as in wtconv_backward; c0
+ * [C, k, k] float32, overwritten; the workspace (partial sums) is queried per
+ * impl.  Deterministic.  WTC_EDTYPE / WTC_ESHAPE outside a path's limits,
+ * WTC_EINVAL for another impl. */
+size_t wtconv_base_correlation_workspace(const wtc_desc* d, int impl);
+int wtconv_base_correlation(const wtc_desc* d, const void* x, const void* g, float* c0, int impl,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Level-by-level baseline: one kernel per step, every intermediate (bands,
  * convolved bands, partial syntheses) a float32 tensor in the workspace.
  * Same arguments and results as above.  It accepts any plane size but

@@ -71,6 +71,10 @@ def load_library(path=None):
         f.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.wtconv_backward_noalloc.restype = ctypes.c_int
     lib.wtconv_backward_noalloc.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.wtconv_base_correlation_workspace.restype = _SZ
+    lib.wtconv_base_correlation_workspace.argtypes = [_D, ctypes.c_int]
+    lib.wtconv_base_correlation.restype = ctypes.c_int
+    lib.wtconv_base_correlation.argtypes = [_D, _P, _P, _P, ctypes.c_int, _P, _SZ, _P]
     lib.wtconv_io_model_bytes.restype = ctypes.c_double
     lib.wtconv_io_model_bytes.argtypes = [_D, ctypes.c_int, ctypes.c_int]
     lib.wtconv_flops.restype = ctypes.c_double
@@ -262,6 +266,36 @@ def wtconv_backward_unfused(x, g, w0, s0, wl, sl, L, dx=None, grads=None, worksp
     """Level-by-level baseline of :func:`wtconv_backward`."""
     return _bwd_common("wtconv_backward_unfused", "wtconv_backward_unfused_workspace", x, g, w0, s0, wl, sl, L,
                        dx, grads, workspace)
+
+
+CORR_VALU, CORR_MFMA = 0, 1
+
+
+def wtconv_base_correlation(x, g, k, impl=CORR_VALU, out=None, workspace=None):
+    """c0[c, ky, kx] = sum over batch and pixels of g * x shifted by
+    (ky - k//2, kx - k//2) (x zero outside): the base level's weight-gradient
+    correlation alone.  impl CORR_VALU: vector-unit tiles; CORR_MFMA: matrix
+    cores (bf16 NCHW planes, k <= 7, H and W <= 64)."""
+    dev = x.device
+    _check_tensor(x, "x", (torch.float32, torch.bfloat16), dev, layout=0)
+    _check_tensor(g, "g", (x.dtype,), dev, x.shape, layout=0)
+    B, C, H, W = x.shape
+    lib = load_library()
+    d = make_desc(B, C, H, W, 0, k, x.dtype, 0)
+    if out is None:
+        out = torch.empty((C, k, k), dtype=torch.float32, device=dev)
+    _check_tensor(out, "out", (torch.float32,), dev, (C, k, k))
+    ws, wsb = _workspace(lib.wtconv_base_correlation_workspace(ctypes.byref(d), int(impl)), dev, workspace)
+    st = lib.wtconv_base_correlation(ctypes.byref(d), _ptr(x), _ptr(g), _ptr(out), int(impl), _ptr(ws), wsb,
+                                     _stream(dev))
+    if st != WTC_OK:
+        raise WTCError(st, "wtconv_base_correlation")
+    return out
+
+
+def wtconv_base_correlation_workspace(B, C, H, W, k, dtype="fp32", impl=CORR_VALU):
+    d = make_desc(B, C, H, W, 0, k, dtype, 0)
+    return int(load_library().wtconv_base_correlation_workspace(ctypes.byref(d), int(impl)))
 
 
 def _ws_query(name, B, C, H, W, L, k, dtype, layout=0):

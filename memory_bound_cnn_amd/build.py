@@ -28,7 +28,7 @@ SOURCES = ["wtconv_fused.hip", "wtconv_fused_k1.hip", "wtconv_fused_k3.hip", "wt
            "wtconv_fused_k7.hip", "wtconv_fused_s_p64.hip", "wtconv_fused_s_p32.hip",
            "wtconv_fused_s_p128a.hip", "wtconv_fused_s_p128b.hip", "wtconv_fused_s_small.hip", "wtconv_fused_s_p112.hip",
            "wtconv_fused_s_dw.hip",
-           "wtconv_tiny.hip", "wtconv_lane.hip", "wtconv_unfused.hip", "wtconv_top.hip", "wtconv_layout.hip", "wtconv_noalloc.hip", "wtconv_api.cpp", "wtconv_plan.cpp"]
+           "wtconv_tiny.hip", "wtconv_lane.hip", "wtconv_unfused.hip", "wtconv_top.hip", "wtconv_layout.hip", "wtconv_noalloc.hip", "wtconv_corr.hip", "wtconv_api.cpp", "wtconv_plan.cpp"]
 
 
 def _compile(src):

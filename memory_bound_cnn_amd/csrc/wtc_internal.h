@@ -304,6 +304,15 @@ int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, con
                      float* dw0, float* ds0, float* db0, float* dwl, float* dsl, char* ws,
                      void* stream, int stage = 0, const float* zext = nullptr);
 int launch_fill_zero(float* p, int n, void* stream);
+// The base level's weight-gradient correlation partials alone, by the
+// level-by-level baseline's tile kernels: part[blk][c][k^2 + 1] (slot k^2 =
+// sum of g), *nblk blocks; part holds unfused_corr_blocks(B, C, H, W) blocks.
+int base_corr_partials(const wtc_desc* d, const void* x, const void* g, float* part, int* nblk, void* stream);
+// The same correlation of bf16 planes (k <= 7, H, W <= 64) on the matrix
+// cores: part[chunk][c][k^2 + 1] over nchunk batch chunks (slot k^2 unused).
+int launch_corr0_mfma(const wtc_desc* d, const void* x, const void* g, float* part, int nchunk, void* stream);
+// out[c][t] = sum over nblk blocks of part[blk][c][t] (t < kk; record length kk1), fixed order
+int launch_corr_sum(const float* part, int C, int nblk, int kk1, int kk, float* out, void* stream);
 // Argument checks of the backward entry points (descriptor, then pointers):
 // WTC_OK or the status the entry point returns, before any HIP call.
 int backward_check(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,

@@ -629,6 +629,30 @@ double io_fused(const wtc_desc* d, int dir, int depth) {
     return t + 3.0 * N * e + 2.0 * recs + 2.0 * params;
 }
 
+// Base-level correlation on its own: the batch chunks of the matrix-core
+// kernel (one-wave workgroups, about four per SIMD in all) and the limits of
+// each path.
+int corr_chunks(const wtc_desc* d) {
+    const int want = std::max(1, cdiv(16 * kComputeUnits, d->C));
+    const int ppc = cdiv(d->B, std::min(want, d->B));
+    return cdiv(d->B, ppc);
+}
+int base_corr_check(const wtc_desc* d, int impl) {
+    int st = check_desc(d);
+    if (st != WTC_OK) return st;
+    if (d->layout != 0) return WTC_EDTYPE;
+    if (impl != 0 && impl != 1) return WTC_EINVAL;
+    if ((long)d->B * d->C * d->H * d->W >= (1L << 31)) return WTC_ESHAPE;   // 32-bit element indices
+    if (impl == 0) return d->k <= kMaxKAny ? WTC_OK : WTC_ESHAPE;
+    if (d->dtype != WTC_BF16) return WTC_EDTYPE;
+    if (d->k > kMaxK || d->H > 64 || d->W > 64) return WTC_ESHAPE;
+    return WTC_OK;
+}
+size_t base_corr_floats(const wtc_desc* d, int impl) {
+    const size_t rec = (size_t)d->C * (d->k * d->k + 1);
+    return impl == 0 ? (size_t)unfused_corr_blocks(d->B, d->C, d->H, d->W) * rec : (size_t)corr_chunks(d) * rec;
+}
+
 }  // namespace
 
 int backward_check(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0,
@@ -754,6 +778,34 @@ int wtconv_backward_unfused(const wtc_desc* d, const void* x, const void* g, con
                              static_cast<char*>(workspace), workspace_bytes, stream);
     return unf_bwd_run(d, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, static_cast<char*>(workspace),
                        workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Base-level correlation (VALU tiles or matrix cores)
+// ---------------------------------------------------------------------------
+size_t wtconv_base_correlation_workspace(const wtc_desc* d, int impl) {
+    if (base_corr_check(d, impl) != WTC_OK) return 0;
+    return base_corr_floats(d, impl) * sizeof(float);
+}
+
+int wtconv_base_correlation(const wtc_desc* d, const void* x, const void* g, float* c0, int impl, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    int st = base_corr_check(d, impl);
+    if (st != WTC_OK) return st;
+    if (!x || !g || !c0) return WTC_EINVAL;
+    const size_t need = base_corr_floats(d, impl) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return WTC_EWORKSPACE;
+    float* part = static_cast<float*>(workspace);
+    const int kk = d->k * d->k;
+    int nblk = 0;
+    if (impl == 0) {
+        st = base_corr_partials(d, x, g, part, &nblk, stream);
+    } else {
+        nblk = corr_chunks(d);
+        st = launch_corr0_mfma(d, x, g, part, nblk, stream);
+    }
+    if (st != WTC_OK) return st;
+    return launch_corr_sum(part, d->C, nblk, kk + 1, kk, c0, stream);
 }
 
 // ---------------------------------------------------------------------------

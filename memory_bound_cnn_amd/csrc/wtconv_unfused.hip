@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "wtc_internal.h"
 #include "wtc_numeric.h"
@@ -735,10 +736,11 @@ int launch_corr_finalize(const float* part, int nch, int nblk, int k, const floa
 
 namespace {
 
-// correlation + finalize of one level (nch channels, nb planes per channel)
+// correlation partials of one level (nch channels, nb planes per channel):
+// part[blk][ch][K*K + 1]; returns the number of blocks
 template <int K, typename TA, typename TX>
-void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const float* wt, const float* scale,
-                 float* dw, float* ds, float* db, float* part, hipStream_t st, int k_rt = K) {
+int launch_corr_parts(const TA* A, const TX* X, int nb, int nch, int h, int w, float* part, hipStream_t st,
+                      int k_rt = K) {
     const int nblk = unfused_corr_blocks(nb, nch, h, w);
     if constexpr (K == 0) {
         // runtime kernel size: small tiles for every plane size (blocks beyond
@@ -747,9 +749,7 @@ void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const 
         const size_t lds = tile_lds_floats(t, k_rt, true) * sizeof(float);
         hipLaunchKernelGGL((k_tcorr_rk<TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, k_rt,
                            nblk, part);
-        hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, k_rt, wt, scale, dw, ds, db);
-    } else {
-    if (big_planes(h, w)) {
+    } else if (big_planes(h, w)) {
         const int ntx = (w + kBigTile - 1) / kBigTile, nty = (h + kBigTile - 1) / kBigTile;
         hipLaunchKernelGGL((k_tcorr_big<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), 0, st, A, X, nb, nch, h, w,
                            ntx, nty, nblk, part);
@@ -759,9 +759,15 @@ void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const 
         hipLaunchKernelGGL((k_tcorr<K, TA, TX>), dim3(nch, nblk), dim3(kThreads), lds, st, A, X, nb, nch, t, nblk,
                            part);
     }
-    hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, K, wt, scale, dw,
-                       ds, db);
-    }
+    return nblk;
+}
+
+// correlation + finalize of one level (nch channels, nb planes per channel)
+template <int K, typename TA, typename TX>
+void launch_corr(const TA* A, const TX* X, int nb, int nch, int h, int w, const float* wt, const float* scale,
+                 float* dw, float* ds, float* db, float* part, hipStream_t st, int k_rt = K) {
+    const int nblk = launch_corr_parts<K, TA, TX>(A, X, nb, nch, h, w, part, st, k_rt);
+    hipLaunchKernelGGL(k_corr_finalize, dim3(nch), dim3(64), 0, st, part, nch, nblk, k_rt, wt, scale, dw, ds, db);
 }
 
 template <int K, typename T>
@@ -893,6 +899,25 @@ int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, con
         case 7: return bwd_k<7>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
         default: return bwd_k<0>(d, p, x, g, w0, s0, wl, sl, dx, dw0, ds0, db0, dwl, dsl, ws, st, stage, zext);
     }
+}
+
+int base_corr_partials(const wtc_desc* d, const void* x, const void* g, float* part, int* nblk, void* stream) {
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    auto go = [&](auto kc, auto tag) {
+        using T = decltype(tag);
+        constexpr int K = decltype(kc)::value;
+        *nblk = launch_corr_parts<K, T, T>(static_cast<const T*>(g), static_cast<const T*>(x), d->B, d->C, d->H,
+                                           d->W, part, st, d->k);
+    };
+    const bool bf = d->dtype == WTC_BF16;
+    switch (d->k) {
+        case 1: bf ? go(std::integral_constant<int, 1>{}, uint16_t{}) : go(std::integral_constant<int, 1>{}, float{}); break;
+        case 3: bf ? go(std::integral_constant<int, 3>{}, uint16_t{}) : go(std::integral_constant<int, 3>{}, float{}); break;
+        case 5: bf ? go(std::integral_constant<int, 5>{}, uint16_t{}) : go(std::integral_constant<int, 5>{}, float{}); break;
+        case 7: bf ? go(std::integral_constant<int, 7>{}, uint16_t{}) : go(std::integral_constant<int, 7>{}, float{}); break;
+        default: bf ? go(std::integral_constant<int, 0>{}, uint16_t{}) : go(std::integral_constant<int, 0>{}, float{}); break;
+    }
+    return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
 int launch_fill_zero(float* p, int n, void* stream) {

@@ -200,6 +200,30 @@ int unfused_backward(const wtc_desc* d, const UnfusedPlan& p, const void* x, con
     return WTC_OK;
 }
 
+int base_corr_partials(const wtc_desc* d, const void* x, const void* g, float* part, int* nblk, void*) {
+    const size_t n = (size_t)d->B * d->C * d->H * d->W * (d->dtype == WTC_BF16 ? 2 : 4);
+    rd(x, n);
+    rd(g, n);
+    *nblk = unfused_corr_blocks(d->B, d->C, d->H, d->W);
+    wr(part, sizeof(float) * (size_t)*nblk * d->C * (d->k * d->k + 1));
+    return WTC_OK;
+}
+
+int launch_corr0_mfma(const wtc_desc* d, const void* x, const void* g, float* part, int nchunk, void*) {
+    need(d->dtype == WTC_BF16 && d->k <= kMaxK && d->H <= 64 && d->W <= 64 && nchunk >= 1, "matrix-core correlation");
+    const size_t n = (size_t)d->B * d->C * d->H * d->W * 2;
+    rd(x, n);
+    rd(g, n);
+    wr(part, sizeof(float) * (size_t)nchunk * d->C * (d->k * d->k + 1));
+    return WTC_OK;
+}
+
+int launch_corr_sum(const float* part, int C, int nblk, int kk1, int kk, float* out, void*) {
+    rd(part, sizeof(float) * (size_t)nblk * C * kk1);
+    wr(out, sizeof(float) * (size_t)C * kk);
+    return WTC_OK;
+}
+
 int launch_fill_zero(float* p, int n, void*) {
     wr(p, sizeof(float) * (size_t)(n > 0 ? n : 0));
     return 0;

@@ -80,6 +80,18 @@ int one(const wtc_desc& d) {
         }
     }
     expect(wtconv_flops(&d, 0) > 0 && wtconv_flops(&d, 1) > wtconv_flops(&d, 0), "flops", d);
+    // the base-level correlation alone, both implementations where they apply
+    for (int impl = 0; impl < 2; ++impl) {
+        const size_t wc = wtconv_base_correlation_workspace(&d, impl);
+        Buf wsc(wc), c0(sizeof(float) * d.C * KK);
+        const int st = wtconv_base_correlation(&d, x.p, g.p, c0.f(), impl, wsc.p, wc, nullptr);
+        expect(st == WTC_OK || st == WTC_ESHAPE || st == WTC_EDTYPE, "base correlation status", d);
+        if (st == WTC_OK) {
+            ++ran;
+            expect(wtconv_base_correlation(&d, x.p, g.p, c0.f(), impl, wsc.p, wc - 1, nullptr) == WTC_EWORKSPACE,
+                   "base correlation short workspace", d);
+        }
+    }
     return ran;
 }
 

@@ -222,3 +222,31 @@ def test_channels_last_workspace_and_model():
         assert binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16", layout=lay) == \
             3 * (t // 2) + binding.wtconv_backward_unfused_workspace(B, C, H, W, L, k, "bf16")
     assert binding.wtconv_forward_workspace(B, C, H, W, L, k, layout=3) == 0
+
+
+def test_base_correlation_limits_checked_before_any_hip_call():
+    lib = binding.load_library()
+    bf = dict(dtype=binding.WTC_BF16, L=0, H=32, W=32)
+    for impl in (binding.CORR_VALU, binding.CORR_MFMA):
+        d = _desc(**bf)
+        need = lib.wtconv_base_correlation_workspace(ctypes.byref(d), impl)
+        assert need >= 4 * d.C * (d.k * d.k + 1)
+        assert lib.wtconv_base_correlation(ctypes.byref(d), FAKE, FAKE, FAKE, impl, FAKE, need - 1,
+                                           None) == binding.WTC_EWORKSPACE
+        assert lib.wtconv_base_correlation(ctypes.byref(d), FAKE, None, FAKE, impl, FAKE, need,
+                                           None) == binding.WTC_EINVAL
+    cases = [
+        (dict(dtype=0), binding.CORR_MFMA, binding.WTC_EDTYPE),        # matrix cores: bf16 only
+        (dict(k=9), binding.CORR_MFMA, binding.WTC_ESHAPE),            # k <= 7
+        (dict(H=65), binding.CORR_MFMA, binding.WTC_ESHAPE),           # planes up to 64 x 64
+        (dict(layout=1), binding.CORR_VALU, binding.WTC_EDTYPE),       # NCHW only
+        (dict(k=33), binding.CORR_VALU, binding.WTC_ESHAPE),
+        (dict(), 2, binding.WTC_EINVAL),
+    ]
+    for kw, impl, status in cases:
+        a = dict(bf)
+        a.update(kw)
+        d = _desc(**a)
+        assert lib.wtconv_base_correlation_workspace(ctypes.byref(d), impl) == 0
+        assert lib.wtconv_base_correlation(ctypes.byref(d), FAKE, FAKE, FAKE, impl, FAKE, 1 << 30,
+                                           None) == status, (kw, impl)
