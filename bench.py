@@ -685,7 +685,7 @@ def main():
                         binding.wtconv_io_model_bytes(*sh, impl=1, direction=1)
                 summary.append(row)
         line["per_workload"] = summary
-        line["dwconv_comparison"] = dwconv_comparison(wl, torch, binding, a.torch_dwconv)
+        line["dwconv_comparison"] = dwconv_comparison(wl.at_level(L), torch, binding, a.torch_dwconv)
         line["channels_last_comparison"] = channels_last_comparison(torch, binding)
         line["base_correlation_comparison"] = base_correlation_comparison(torch, binding)
         line["training_step_memory"] = memory_comparison(wl, L, torch, binding)

@@ -130,7 +130,7 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         if (lds > kLdsLimit || NP * per_units >= 65536) return;   // fast in-kernel division range
         // plain depthwise conv (no levels) on a plane class with fixed-geometry
         // direct-load instances: those are compiled for more waves per SIMD
-        const bool nolev = d->L == 0 && lay.dl && a.Hq == 64 && (k == 5 || k == 7);
+        const bool nolev = d->L == 0 && d->dtype == WTC_FP32 && lay.dl && a.Hq == 64 && (k == 5 || k == 7);
         const int wpe = fused_waves_per_simd(bwd, bpq, nolev);
         const int lds_wgs = (int)(kLdsLimit / lds);
         const int reg_wgs = std::max(1, 4 * wpe / (nthr / 64));

@@ -480,7 +480,7 @@ __device__ __forceinline__ void quad_rows(const float (&xk)[4][4], float (&r0)[2
 // per CU) needs 4; otherwise the register budget of fused_waves_per_simd.
 template <class G, bool BWD, int BPQ>
 constexpr int kernel_waves() {
-    return G::kMaxThreads > 512 ? 4 : fused_waves_per_simd(BWD, BPQ, G::kNoLevels);
+    return G::kMaxThreads > 512 ? 4 : fused_waves_per_simd(BWD, BPQ, G::kNoLevels && BPQ == 1);
 }
 
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>

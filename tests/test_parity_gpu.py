@@ -44,6 +44,8 @@ REDUCED = [
     (2, 2, 112, 112, 2, 5, 33, "fp32"),    # the LL band of the 224x224 planes (peeled path)
     (5, 8, 14, 14, 2, 5, 40, "fp32"),      # odd 14x14
     (9, 8, 7, 7, 1, 5, 41, "fp32"),        # odd 7x7
+    (1, 3, 128, 128, 0, 5, 34, "fp32"),    # the depthwise convs WTConv is compared with, on sweep planes
+    (1, 3, 128, 128, 0, 7, 35, "fp32"),
 ]
 
 
