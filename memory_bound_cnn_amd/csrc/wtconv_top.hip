@@ -150,18 +150,31 @@ struct TopGeom {
     static constexpr int XN = XR * XS > 4 * YSZ ? XR * XS : 4 * YSZ;
 };
 
+// Tile units (plane-major, tiles in row order) dealt to the XCDs in
+// contiguous ranges: workgroup i runs on XCD i % 8 (workgroups are dealt to
+// the XCDs in turn) and takes unit (i % 8) ceil(n / 8) + i / 8, so the tiles
+// of one plane -- whose halos share rows and cache lines -- pass through one
+// L2 one after another.  The grid is 8 ceil(n / 8) workgroups.
+__device__ __forceinline__ uint32_t top_unit(uint32_t n) {
+    const uint32_t per = (n + 7) >> 3;
+    return (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+}
+
 template <int K, typename T>
 __global__ void __launch_bounds__(kTopThreads) k_top_fwd(const T* __restrict__ x, int C, int H, int W, int ntx,
                                                          int nty, const float* __restrict__ w0,
                                                          const float* __restrict__ s0, const float* __restrict__ b0,
                                                          const float* __restrict__ wl, const float* __restrict__ sl,
-                                                         const float* __restrict__ zext, T* __restrict__ out) {
+                                                         const float* __restrict__ zext, T* __restrict__ out,
+                                                         uint32_t nunit) {
     using G = TopGeom<K>;
     constexpr int R = G::R, KK = K * K;
     __shared__ __align__(16) float xs[G::XN];   // x tile; later the level-1 results
     __shared__ __align__(16) float bs[4 * G::BSZ];      // the four level-1 bands of the tile
     const int ntile = ntx * nty;
-    const int p = blockIdx.x / ntile, tile = blockIdx.x - p * ntile;
+    const uint32_t unit = top_unit(nunit);
+    if (unit >= nunit) return;   // whole workgroup, before any barrier
+    const int p = (int)(unit / ntile), tile = (int)(unit - (uint32_t)p * ntile);
     const int ty0 = (tile / ntx) * kTop, tx0 = (tile % ntx) * kTop;
     const int c = p % C;
     const int h1 = (H + 1) >> 1, w1 = (W + 1) >> 1;
@@ -308,14 +321,16 @@ __global__ void __launch_bounds__(kTopThreads) __attribute__((amdgpu_waves_per_e
                                                          const float* __restrict__ s0, const float* __restrict__ wl,
                                                          const float* __restrict__ sl, const float* __restrict__ dll,
                                                          T* __restrict__ dx, float* __restrict__ part0,
-                                                         float* __restrict__ part1) {
+                                                         float* __restrict__ part1, uint32_t nunit) {
     using G = TopGeom<K>;
     constexpr int R = G::R, KK = K * K;
     __shared__ __align__(16) float gs[G::XN];       // g tile; then X1; then the level-1 results
     __shared__ __align__(16) float bs[4 * G::BSZ];  // the four level-1 bands of g; then level-1 partials
     __shared__ float r0[16][KK + 1];                 // base correlation partials, one per 16-lane row
     const int ntile = ntx * nty;
-    const int p = blockIdx.x / ntile, tile = blockIdx.x - p * ntile;
+    const uint32_t unit = top_unit(nunit);
+    if (unit >= nunit) return;   // whole workgroup, before any barrier
+    const int p = (int)(unit / ntile), tile = (int)(unit - (uint32_t)p * ntile);
     const int ty0 = (tile / ntx) * kTop, tx0 = (tile % ntx) * kTop;
     const int c = p % C, bb = p / C;
     const int h1 = (H + 1) >> 1, w1 = (W + 1) >> 1;
@@ -566,9 +581,9 @@ template <int K, typename T>
 int top_fwd_k(const wtc_desc* d, const void* x, const float* w0, const float* s0, const float* b0, const float* wl,
               const float* sl, const float* zext, void* out, hipStream_t st) {
     const int ntx = (d->W + kTop - 1) / kTop, nty = (d->H + kTop - 1) / kTop;
-    const uint32_t grid = (uint32_t)d->B * d->C * ntx * nty;
+    const uint32_t nunit = (uint32_t)d->B * d->C * ntx * nty, grid = 8 * ((nunit + 7) / 8);
     hipLaunchKernelGGL((k_top_fwd<K, T>), dim3(grid), dim3(kTopThreads), 0, st, reinterpret_cast<const T*>(x), d->C,
-                       d->H, d->W, ntx, nty, w0, s0, b0, wl, sl, zext, reinterpret_cast<T*>(out));
+                       d->H, d->W, ntx, nty, w0, s0, b0, wl, sl, zext, reinterpret_cast<T*>(out), nunit);
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
@@ -588,10 +603,10 @@ template <int K, typename T>
 int top_bwd_k(const wtc_desc* d, const void* x, const void* g, const float* w0, const float* s0, const float* wl,
               const float* sl, const float* dll, void* dx, float* part0, float* part1, hipStream_t st) {
     const int ntx = (d->W + kTop - 1) / kTop, nty = (d->H + kTop - 1) / kTop;
-    const uint32_t grid = (uint32_t)d->B * d->C * ntx * nty;
+    const uint32_t nunit = (uint32_t)d->B * d->C * ntx * nty, grid = 8 * ((nunit + 7) / 8);
     hipLaunchKernelGGL((k_top_bwd<K, T>), dim3(grid), dim3(kTopThreads), 0, st, reinterpret_cast<const T*>(x),
                        reinterpret_cast<const T*>(g), d->C, d->H, d->W, ntx, nty, w0, s0, wl, sl, dll,
-                       reinterpret_cast<T*>(dx), part0, part1);
+                       reinterpret_cast<T*>(dx), part0, part1, nunit);
     return hipGetLastError() == hipSuccess ? WTC_OK : WTC_EHIP;
 }
 
