@@ -109,9 +109,9 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
     // overlap (one barrier less per plane), then overlap from level 2, then
     // the smaller workgroup.  Overlapping bands must have their zero rings
     // rewritten for every plane; in the forward pass, with half the arithmetic
-    // per pixel of the backward, that costs more than the occupancy it buys
-    // (measured on 32x32 planes: 53 us without, 67 us with overlap), so the
-    // forward pass overlaps only when nothing else fits.
+    // per pixel of the backward, that mostly costs more than the occupancy it
+    // buys, so the forward pass overlaps only when nothing else fits, or for
+    // bf16 32x32 planes (below).
     // folded level weights (one 16-byte aligned set of round_up(k^2, 4) floats
     // per level and band), base weights, bias and scale
     const int wts_n = round_up(round_up(KK, 4) * 4 * d->L + KK + 4, 4);
@@ -167,7 +167,11 @@ int plan_fused(const wtc_desc* d, bool bwd, FusedPlan* p) {
         Layout lay = make_layout(k, a.Hq, a.Wq, a.Lm, 3, bwd, bovl, mode, esz);
         if ((size_t)(lay.slot + wts_n) * 4 > kLdsLimit) lay = make_layout(k, a.Hq, a.Wq, a.Lm, 1, bwd, bovl, mode, esz);
         if (variant == -2 && lay.mode != 2) continue;   // same layout as mode 0
-        if (bovl > 0 && !bwd && best.score >= 0) continue;
+        // (forward overlap: only bf16 32x32 planes from level 1, whose fixed-geometry
+        // instance it takes to three waves per SIMD: 58.7 -> 54.8 us on 64x192 planes;
+        // 16x16 fp32 planes with overlap measured 60 -> 75 us)
+        const bool fwd_ovl = d->dtype == WTC_BF16 && a.Hq == 32 && a.Wq == 32 && bovl == 1;
+        if (bovl > 0 && !bwd && best.score >= 0 && !fwd_ovl) continue;
         if (a.qpp <= 64) {
             // several planes per workgroup when planes are small
             for (int np = 1; np <= (dl ? 1 : 64 / a.qpp); ++np) consider(lay, np, round_up(4 * a.qpp * np, 64), 1);

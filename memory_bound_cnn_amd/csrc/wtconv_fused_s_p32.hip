@@ -20,7 +20,7 @@ bool launch_fused_static_p32(const FusedArgs& a, int dtype, int bwd, int bpq, in
     if (!hit && dtype == WTC_FP32 && bwd == 1)
         hit = try_static<5, float, 1, 1, true, 32, 32, 3, 3, 1, 64, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_BF16 && bwd == 0)
-        hit = try_static<5, bf16_t, 0, 1, true, 32, 32, 3, 3, 1, 64, 0, 2>(a, bpq, nthr, lds, grid, st, &e);
+        hit = try_static<5, bf16_t, 0, 1, true, 32, 32, 3, 3, 1, 64, 1, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_BF16 && bwd == 1)
         hit = try_static<5, bf16_t, 1, 1, true, 32, 32, 3, 3, 1, 64, 0, 1>(a, bpq, nthr, lds, grid, st, &e);
     *err = (int)e;
