@@ -334,6 +334,7 @@ CHANNELS_LAST = [
     (2, 4, 64, 64, 2, 5, 99, "bf16"),      # bf16 64 x 64
     (4, 3, 24, 24, 0, 7, 100, "fp32"),     # L = 0, k = 7
     (35, 17, 8, 8, 2, 5, 101, "fp32"),     # many units, odd channel count
+    (2, 8, 32, 32, 3, 5, 102, "bf16"),     # 16-byte transposes of bf16 (channels a multiple of 8)
 ]
 
 
