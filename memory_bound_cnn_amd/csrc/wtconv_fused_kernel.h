@@ -476,6 +476,16 @@ __device__ __forceinline__ void quad_rows(const float (&xk)[4][4], float (&r0)[2
     }
 }
 
+// Level count of a fixed geometry (compile time); -1 for the runtime one.
+template <class G>
+constexpr int fixed_lm() {
+    if constexpr (G::kFixed) {
+        return G::Lm();
+    } else {
+        return -1;
+    }
+}
+
 // Waves per SIMD a kernel is compiled for: a workgroup of 1024 threads (one
 // per CU) needs 4; otherwise the register budget of fused_waves_per_simd.
 template <class G, bool BWD, int BPQ>
@@ -887,6 +897,39 @@ wtc_fused_kernel(const FusedArgs a) {
         // ---------------- phase 1: stage the planes in LDS ----------------
         if (pf_on) {
             pf_commit(bb);
+        } else if constexpr (VEC && BWD && BPQ > 1 && (fixed_lm<G>() == 1 || fixed_lm<G>() == 3)) {
+            // the units' loads are issued in batches of SB before their stores:
+            // one memory latency per batch instead of one per unit.  The
+            // two-blocks-per-quad backward has no registers for a prefetch that
+            // lives through a plane; a batch of four fits beside its
+            // accumulators with one or three levels (128x128 planes, L = 3:
+            // 642 -> 585 us), while with two, four or five levels even a batch of
+            // two spills 24-48 VGPRs and measured slower.
+            constexpr int SU = (G::NP() * G::Hq() * (G::Wq() / UW) + G::nthr() - 1) / G::nthr();
+            constexpr int SB = 4;
+#pragma unroll
+            for (int k0 = 0; k0 < SU; k0 += SB) {
+                float sv[SB][4];
+#pragma unroll
+                for (int k = 0; k < SB && k0 + k < SU; ++k) {
+                    const int e = tid + (k0 + k) * nthr;
+                    const int s2 = fdiv(e, dper), m = e - s2 * per;
+                    const int y = fdiv(m, dwv), xq = m - y * wv;
+                    if (e < g.NP() * per && bb + s2 < b_end)
+                        gload4<NHWC>(plane_at(srcp, bb + s2, c) + ((size_t)y * a.W + xq * UW) * ps, ps, sv[k]);
+                }
+#pragma unroll
+                for (int k = 0; k < SB && k0 + k < SU; ++k) {
+                    const int e = tid + (k0 + k) * nthr;
+                    const int s2 = fdiv(e, dper), m = e - s2 * per;
+                    const int y = fdiv(m, dwv), xq = m - y * wv;
+                    if (e < g.NP() * per && bb + s2 < b_end) {
+                        float* d = lds + s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) d[i] = sv[k][i];
+                    }
+                }
+            }
         } else {
             for (int e = tid; e < g.NP() * per; e += nthr) {
                 const int s2 = fdiv(e, dper), m = e - s2 * per;
