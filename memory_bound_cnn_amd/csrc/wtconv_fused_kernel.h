@@ -627,10 +627,17 @@ wtc_fused_kernel(const FusedArgs a) {
     // issue the global loads of the NP planes starting at batch index bbn
     auto pf_issue = [&](int bbn) {
         if constexpr (VEC) {
+            // Every unit's load is issued, a missing unit reading the plane's
+            // first pixels (the caller issues only for planes that exist), and
+            // the commit waits for every unit: no load of these registers is
+            // then left in flight on any path, so the compiler needs no
+            // wait-for-everything before this plane's loads.
             const ST* base = plane_at(srcp, bbn, c);
 #pragma unroll
-            for (int k = 0; k < PFU; ++k)
-                if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) gload4<NHWC>(base + pf_goff[k], ps, pf[k]);
+            for (int k = 0; k < PFU; ++k) {
+                const bool ok = pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end;
+                gload4<NHWC>(base + (ok ? pf_goff[k] : 0), ps, pf[k]);
+            }
         } else if constexpr (G::kFixed) {
             // unit k: plane k % NP, in-plane pixel tid + (k / NP) * nthr, so one
             // row/column decode serves the NP planes (NP is a constant here; the
@@ -672,6 +679,11 @@ wtc_fused_kernel(const FusedArgs a) {
     };
     auto pf_commit = [&](int bbn) {
         if constexpr (VEC) {
+#pragma unroll
+            for (int k = 0; k < PFU; ++k) {
+#pragma unroll
+                for (int i = 0; i < UW; ++i) asm volatile("" : "+v"(pf[k][i]));   // waited for on every path
+            }
 #pragma unroll
             for (int k = 0; k < PFU; ++k)
                 if (pf_lds[k] >= 0 && bbn + (pf_lds[k] >> 16) < b_end) {
@@ -1156,6 +1168,7 @@ wtc_fused_kernel(const FusedArgs a) {
             if constexpr (BWD) {
                 // x over the quad's 8x8 block -> band t (and LL) at levels 1, 2, 3
                 float ll1[4][4];
+                float xr0[2][2][4], xr1[2][2][4];
                 const ST* xp = auxp + poff + (size_t)opaque(8 * qy * a.W + 8 * qx) * ps;
 #pragma unroll
                 for (int jy = 0; jy < 4; ++jy) {
@@ -1173,11 +1186,25 @@ wtc_fused_kernel(const FusedArgs a) {
                         if (jy == 2) quad_rows<2>(xkeep, r0, r1);
                         if (jy == 3) quad_rows<3>(xkeep, r0, r1);
                     } else {
-                    const ST* p0r = xp + (size_t)(2 * jy) * a.W * ps;
-                    ld_row4<VEC, NHWC>(p0r, y0 < a.H, 8 * qx, a.W, r0[0], ps);
-                    ld_row4<VEC, NHWC>(p0r + 4 * ps, y0 < a.H, 8 * qx + 4, a.W, r0[1], ps);
-                    ld_row4<VEC, NHWC>(p0r + (size_t)a.W * ps, y0 + 1 < a.H, 8 * qx, a.W, r1[0], ps);
-                    ld_row4<VEC, NHWC>(p0r + (size_t)(a.W + 4) * ps, y0 + 1 < a.H, 8 * qx + 4, a.W, r1[1], ps);
+                    // row pairs loaded two at a time: one memory round trip per two pairs
+                    if ((jy & 1) == 0) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const ST* p0r = xp + (size_t)(2 * (jy + h)) * a.W * ps;
+                            const int yh = y0 + 2 * h;
+                            ld_row4<VEC, NHWC>(p0r, yh < a.H, 8 * qx, a.W, xr0[h][0], ps);
+                            ld_row4<VEC, NHWC>(p0r + 4 * ps, yh < a.H, 8 * qx + 4, a.W, xr0[h][1], ps);
+                            ld_row4<VEC, NHWC>(p0r + (size_t)a.W * ps, yh + 1 < a.H, 8 * qx, a.W, xr1[h][0], ps);
+                            ld_row4<VEC, NHWC>(p0r + (size_t)(a.W + 4) * ps, yh + 1 < a.H, 8 * qx + 4, a.W, xr1[h][1], ps);
+                        }
+                    }
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            r0[q][i] = xr0[jy & 1][q][i];
+                            r1[q][i] = xr1[jy & 1][q][i];
+                        }
                     }
 #pragma unroll
                     for (int jx = 0; jx < 4; ++jx) {
