@@ -189,10 +189,12 @@ __device__ __forceinline__ void zero_rings(float* lds, const G& g, int off, int 
 //   acc[oy][ox]   += w[ky][kx] * win[oy+ky][ox+kx]
 //   corr[ky][kx]  += xv[oy][ox] * win[oy+ky][ox+kx]     (CORR only)
 // ---------------------------------------------------------------------------
-template <int K, int OH, int OW, int AL, bool CORR>
+// CTR: also hand back the window's centre, ctr[oy][ox] = win[oy+K/2][ox+K/2]
+// (the block itself), taken from the rows as they pass instead of read again.
+template <int K, int OH, int OW, int AL, bool CORR, bool CTR = false>
 __device__ __forceinline__ void stencil(const float* win, int S, const float (&w)[K * K],
                                         float (&acc)[OH][OW], const float (&xv)[OH][OW],
-                                        float (&corr)[K * K]) {
+                                        float (&corr)[K * K], float (*ctr)[OW] = nullptr) {
     constexpr int WH = OH + K - 1, WW = OW + K - 1;
     // Two window rows live: row wy+1 is read while row wy is consumed.  The
     // scheduling barrier keeps the compiler from hoisting every row's LDS
@@ -203,6 +205,12 @@ __device__ __forceinline__ void stencil(const float* win, int S, const float (&w
     for (int wy = 0; wy < WH; ++wy) {
         float (&row)[WW] = rows[wy & 1];
         if (wy + 1 < WH) lds_row<WW, AL>(win + (wy + 1) * S, rows[(wy + 1) & 1]);
+        if constexpr (CTR) {
+            if (wy >= K / 2 && wy < K / 2 + OH) {
+#pragma unroll
+                for (int ox = 0; ox < OW; ++ox) ctr[wy - K / 2][ox] = row[K / 2 + ox];
+            }
+        }
 #pragma unroll
         for (int oy = 0; oy < OH; ++oy) {
             const int ky = wy - oy;
@@ -1031,16 +1039,24 @@ wtc_fused_kernel(const FusedArgs a) {
                 }
             }
             const float* win = S + g.a0_off() + py0 * g.a0_S() + px0;
-            // (the LL problem of a peeled plane has no base conv: scale and bias 0)
-            if (!(G::kSub && a.nobase)) stencil<K, 4, 4, 4, BWD>(win, g.a0_S(), w, acc[s], xo, corr0);
-            // the block itself (window centre): raw analysis cascade in registers
+            // the block itself (window centre), for the raw analysis cascade in
+            // registers: handed back by the stencil as its rows pass (except in
+            // the two-blocks-per-quad backward, where keeping it live through
+            // the stencil spills: read again there)
+            constexpr bool CTRS = !(BWD && BPQ > 1);
             float ctr[4][4];
+            if (CTRS && !(G::kSub && a.nobase)) {
+                stencil<K, 4, 4, 4, BWD, CTRS>(win, g.a0_S(), w, acc[s], xo, corr0, ctr);
+            } else {
+                if (!(G::kSub && a.nobase)) stencil<K, 4, 4, 4, BWD>(win, g.a0_S(), w, acc[s], xo, corr0);
+                // (the LL problem of a peeled plane has no base conv: scale and bias 0)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float rowv[4];
-                lds_row<4, (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1)>(win + (i + R) * g.a0_S() + R, rowv);
+                for (int i = 0; i < 4; ++i) {
+                    float rowv[4];
+                    lds_row<4, (R % 4 == 0) ? 4 : ((R % 2 == 0) ? 2 : 1)>(win + (i + R) * g.a0_S() + R, rowv);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) ctr[i][j] = rowv[j];
+                    for (int j = 0; j < 4; ++j) ctr[i][j] = rowv[j];
+                }
             }
             if constexpr (BWD) {
 #pragma unroll
