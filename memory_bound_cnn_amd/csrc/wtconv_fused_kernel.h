@@ -1126,6 +1126,29 @@ wtc_fused_kernel(const FusedArgs a) {
         // the level-0 plane is dead: the next planes' copies land during the rest
         if (DL && !SDL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP(), c, b_end);
 
+        // Two-blocks-per-quad backward: the first block's first two x row pairs
+        // for the level-1 analysis below are loaded now, so their round trip
+        // passes during phase 3 and the deep levels (fixed geometry: every
+        // thread owns both its blocks).  With one or three levels (128x128
+        // planes: L = 1 511 -> 484 us, L = 3 -1 %); with two levels it spills
+        // and measured 2 % slower, with four or five no change.
+        constexpr bool XPRE = BWD && !XDL && !XQB && BPQ > 1 && VEC && !NHWC &&
+                              (fixed_lm<G>() == 1 || fixed_lm<G>() == 3);
+        float xpre0[XPRE ? 2 : 1][2][4], xpre1[XPRE ? 2 : 1][2][4];
+        if constexpr (XPRE) {
+            const int qy = qyv[0], qx = qxv[0];
+            const ST* xp = auxp + poff + (size_t)opaque(8 * qy * a.W + 8 * qx);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const ST* p0r = xp + (size_t)(2 * h) * a.W;
+                const int yh = 8 * qy + 2 * h;
+                ld_row4<VEC, NHWC>(p0r, yh < a.H, 8 * qx, a.W, xpre0[h][0]);
+                ld_row4<VEC, NHWC>(p0r + 4, yh < a.H, 8 * qx + 4, a.W, xpre0[h][1]);
+                ld_row4<VEC, NHWC>(p0r + (size_t)a.W, yh + 1 < a.H, 8 * qx, a.W, xpre1[h][0]);
+                ld_row4<VEC, NHWC>(p0r + (size_t)(a.W + 4), yh + 1 < a.H, 8 * qx + 4, a.W, xpre1[h][1]);
+            }
+        }
+
         // ---------------- phase 3: analysis of levels early_lv+1..Lm ----------------
         for (int i = g.early() + 1; i <= Lm; ++i) {
             const int hi = g.Hq() >> i, wi = g.Wq() >> i, Si = g.b_S(i), bs = g.b_bs(i);
@@ -1203,7 +1226,17 @@ wtc_fused_kernel(const FusedArgs a) {
                         if (jy == 3) quad_rows<3>(xkeep, r0, r1);
                     } else {
                     // row pairs loaded two at a time: one memory round trip per two pairs
-                    if ((jy & 1) == 0) {
+                    if (XPRE && s == 0 && jy == 0) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) {
+                                    xr0[h][q][i] = xpre0[XPRE ? h : 0][q][i];
+                                    xr1[h][q][i] = xpre1[XPRE ? h : 0][q][i];
+                                }
+                    } else if ((jy & 1) == 0) {
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
                             const ST* p0r = xp + (size_t)(2 * (jy + h)) * a.W * ps;
