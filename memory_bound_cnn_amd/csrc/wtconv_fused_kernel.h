@@ -81,21 +81,15 @@ __device__ __forceinline__ void store2(float* p, float v0, float v1) {
     *reinterpret_cast<float2*>(p) = make_float2(v0, v1);
 }
 __device__ __forceinline__ void store2(bf16_t* p, float v0, float v1) {
-    bf16_t b0, b1;
-    from_f32(b0, v0);
-    from_f32(b1, v1);
-    *reinterpret_cast<uint32_t*>(p) = (uint32_t)b0.bits | ((uint32_t)b1.bits << 16);
+    *reinterpret_cast<uint32_t*>(p) = bf16x2_rne(v0, v1);
 }
 __device__ __forceinline__ void store4(float* p, const float (&v)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ void store4(bf16_t* p, const float (&v)[4]) {
-    bf16_t b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) from_f32(b[i], v[i]);
     uint2 q;
-    q.x = (uint32_t)b[0].bits | ((uint32_t)b[1].bits << 16);
-    q.y = (uint32_t)b[2].bits | ((uint32_t)b[3].bits << 16);
+    q.x = bf16x2_rne(v[0], v[1]);
+    q.y = bf16x2_rne(v[2], v[3]);
     *reinterpret_cast<uint2*>(p) = q;
 }
 
