@@ -342,6 +342,7 @@ struct RtGeom {
     static constexpr int kDeep = LMX > 3 ? LMX - 2 : 1;
     static constexpr bool kSub = true;   // may run the LL problem of a peeled plane
     static constexpr int kMaxThreads = 512;
+    static constexpr int kHq = 0, kWq = 0, kNP = 0, kNthr = 0;   // known at run time only
     const FusedArgs& a;
     __device__ RtGeom(const FusedArgs& args) : a(args) {}
     __device__ int Lm() const { return a.Lm; }
@@ -391,6 +392,7 @@ struct CtGeom {
     // not fit the pipeline): the smaller classes never check for it
     static constexpr bool kSub = HQ > 64;
     static constexpr int kMaxThreads = NTHR > 512 ? NTHR : 512;
+    static constexpr int kHq = HQ, kWq = WQ, kNP = NPV, kNthr = NTHR;
     const FusedArgs& a;
     __device__ CtGeom(const FusedArgs& args) : a(args) {}
     __device__ static constexpr int Lm() { return LM; }
@@ -493,6 +495,18 @@ constexpr int fixed_lm() {
 template <class G, bool BWD, int BPQ>
 constexpr int kernel_waves() {
     return G::kMaxThreads > 512 ? 4 : fused_waves_per_simd(BWD, BPQ, G::kNoLevels && BPQ == 1);
+}
+
+// Units of four pixels per thread of the next plane that the two-blocks-per-
+// quad backward prefetches (fixed geometry, one plane per workgroup, the plane
+// an exact number of unit steps); 0: no prefetch.
+template <class G, bool BWD, int BPQ, bool VEC>
+constexpr int next_plane_units() {
+    if constexpr (G::kFixed && !G::kNHWC && VEC && BWD && BPQ > 1) {
+        constexpr int wv = G::kWq / 4;
+        if (G::kNP == 1 && G::kNthr % wv == 0 && (G::kHq * wv) % G::kNthr == 0) return G::kHq * wv / G::kNthr;
+    }
+    return 0;
 }
 
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
@@ -872,6 +886,25 @@ wtc_fused_kernel(const FusedArgs a) {
     const bool dactive = BWD && drole < droles;
     const int du = drole & 3, dky = (drole >> 2) % K, dsb = (drole >> 2) / K;
 
+    // Two-blocks-per-quad backward with one or three levels, on a plane that
+    // fills its zero-extended size: the next plane's loads are issued when the
+    // synthesis phase starts and stored at the top of the next iteration, so
+    // their round trip passes during the synthesis and the stores of this
+    // plane (the registers are free there; a prefetch that lived through the
+    // whole plane would spill).  Unit k of a thread is pixel 4 (tid + k nthr).
+    constexpr int XPU0 = next_plane_units<G, BWD, BPQ, VEC>();
+    constexpr bool XPF = XPU0 > 0;
+    constexpr int XPU = XPF ? XPU0 : 1;
+    constexpr int XWV = XPF ? G::kWq / 4 : 1;   // 4-pixel units per plane row
+    constexpr int XRPK = XPF ? G::kNthr / XWV : 1;   // plane rows per unit step
+    const bool xwhole = XPF && a.H == g.Hq() && a.W == g.Wq();
+    float xpf[XPU][4];
+#pragma unroll
+    for (int k = 0; k < XPU; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xpf[k][i] = 0.f;
+    bool xpf_ok = false;   // this plane was prefetched by the previous iteration
+
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
         const int b = bb + slot;
@@ -909,8 +942,24 @@ wtc_fused_kernel(const FusedArgs a) {
         lds_barrier();  // the previous plane is fully consumed
 
         // ---------------- phase 1: stage the planes in LDS ----------------
+        if constexpr (XPF) {
+            // the prefetch registers are consumed on every path, so no load
+            // into them is left in flight when the next ones are issued
+#pragma unroll
+            for (int k = 0; k < XPU; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(xpf[k][i]));
+        }
         if (pf_on) {
             pf_commit(bb);
+        } else if (XPF && xpf_ok) {
+            // this plane, loaded by the previous iteration
+            const int t1 = opaque(tid);
+            float* dst0 = lds + g.a0_off() + ((t1 / XWV) + R) * g.a0_S() + R + (t1 % XWV) * 4;
+#pragma unroll
+            for (int k = 0; k < XPU; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst0[k * XRPK * g.a0_S() + i] = xpf[k][i];
         } else if constexpr (VEC && BWD && BPQ > 1 && (fixed_lm<G>() == 1 || fixed_lm<G>() == 3)) {
             // the units' loads are issued in batches of SB before their stores:
             // one memory latency per batch instead of one per unit.  The
@@ -1307,6 +1356,23 @@ wtc_fused_kernel(const FusedArgs a) {
         }
 
         if (SDL && BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP(), c, b_end);
+
+        if constexpr (XPF) {
+            xpf_ok = xwhole && bb + 1 < b_end;
+            if (xpf_ok) {
+                const ST* src0 = plane_at(srcp, bb + 1, c) + (size_t)opaque(tid) * 4;
+#pragma unroll
+                for (int k = 0; k < XPU; ++k) load4(src0 + (size_t)k * XWV * XRPK * 4, xpf[k]);
+            } else {
+                // (defined on every path: no value of these registers lives
+                // through the next plane)
+#pragma unroll
+                for (int k = 0; k < XPU; ++k)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) xpf[k][i] = 0.f;
+            }
+        }
+
 
         // ---------------- phase 4b: x bands of levels >= 4 (backward) ----------------
         if constexpr (BWD) {
