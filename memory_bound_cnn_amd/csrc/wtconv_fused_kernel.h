@@ -275,6 +275,21 @@ __device__ __forceinline__ void gstore4(ST* p, size_t ps, const float (&v)[4]) {
     }
 }
 
+// Raw buffer resource over `bytes` bytes at `base`: the hardware range check
+// drops stores at offsets past the range, so out-of-plane lanes need no branch.
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr uint32_t kRsrcWord3 = 0x00020000;   // raw 32-bit data format
+constexpr int kOutOfRange = 0x7FFFFFF0;       // past every range used here (< 2^31 bytes)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
+}
+// four floats at byte offset `off` of the resource, one 16-byte store
+__device__ __forceinline__ void bstore4(rsrc_t r, int off, const float (&v)[4]) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const u4 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+}
+
 // Pixel (y, x) of a plane, zero outside [0,H) x [0,W).
 template <typename ST>
 __device__ __forceinline__ float ld_px(const ST* plane, int y, int x, int H, int W) {
@@ -509,6 +524,20 @@ constexpr int next_plane_units() {
     return 0;
 }
 
+// Fixed-geometry forward whose register prefetch holds every 4-pixel unit of
+// its plane group: the prefetch is on for every plane (the last plane of a
+// segment loads its own group again, which is in L2) and the output stores go
+// through a buffer resource whose range check drops the lanes outside the
+// plane, so no memory instruction of the plane loop sits under a branch.
+// The compiler then counts the stores issued after a prefetch load and waits
+// for that load alone, instead of for every store of the previous plane.
+template <class G, bool BWD, bool VEC, int PFU>
+constexpr bool static_prefetch() {
+    if constexpr (G::kFixed && !G::kDL && !BWD && VEC)
+        return PFU * G::kNthr >= G::kNP * G::kHq * (G::kWq / 4);
+    return false;
+}
+
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 __global__ void __launch_bounds__(G::kMaxThreads) __attribute__((amdgpu_waves_per_eu(kernel_waves<G, BWD, BPQ>())))
 wtc_fused_kernel(const FusedArgs a) {
@@ -615,7 +644,10 @@ wtc_fused_kernel(const FusedArgs a) {
     // runtime-geometry backward stages synchronously: with a plane held in
     // registers beside its correlation accumulators it spills, measured 5-13 %
     // slower on 14x14 to 30x30 planes)
-    const bool pf_on = !DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0;
+    constexpr bool PFS = static_prefetch<G, BWD, VEC, PFU>();
+    // buffer-resource output stores (fp32 NCHW planes, byte offsets < 2^31)
+    constexpr bool BST = PFS && !G::kNHWC && sizeof(ST) == 4;
+    const bool pf_on = PFS || (!DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0);
     float pf[PFU][UW];
     // With 4-pixel units the decode of each unit is done once per segment: its
     // offset within a plane group in device memory, and (packed) its plane
@@ -905,6 +937,10 @@ wtc_fused_kernel(const FusedArgs a) {
         for (int i = 0; i < 4; ++i) xpf[k][i] = 0.f;
     bool xpf_ok = false;   // this plane was prefetched by the previous iteration
 
+    // the segment's first prefetch has landed: no load is pending on entry to
+    // the plane loop, so the loop-top wait counts only the previous
+    // iteration's prefetch loads and the stores issued after them
+    if constexpr (PFS) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
         const int b = bb + slot;
@@ -1018,7 +1054,8 @@ wtc_fused_kernel(const FusedArgs a) {
         }
         lds_barrier();
         // the next planes' loads fly while this plane is computed
-        if (pf_on && bb + g.NP() < b_end) pf_issue(bb + g.NP());
+        if constexpr (PFS) pf_issue(bb + g.NP() < b_end ? bb + g.NP() : bb);
+        else if (pf_on && bb + g.NP() < b_end) pf_issue(bb + g.NP());
         }
 
         // ---------------- phase 2: base conv; analysis of levels 1..3 ----------------
@@ -1476,87 +1513,103 @@ wtc_fused_kernel(const FusedArgs a) {
         // level-(i-1) coordinate; level 1 adds one 2x2 butterfly per position.
 #pragma unroll
         for (int s = 0; s < BPQ; ++s) {
-            if (!(pok && qok[s])) continue;
+            const bool sok = pok && qok[s];
+            if (!BST && !sok) continue;
             const int qy = qyv[s], qx = qxv[s];
             const int py0 = 8 * qy + 4 * sy, px0 = 8 * qx + 4 * sx;
-            const float bias = wbase[KK];
-            float z[4][4];
-            if (Lm >= 1) {
-                // levels Lm..3: v = Z_3 at this lane's level-2 position
-                float v = 0.f;
-                for (int i = Lm; i >= 3; --i) {
-                    const int wi = g.Wq() >> i, pi = (g.Hq() >> i) * wi;
-                    const int jy = py0 >> i, jx = px0 >> i;
-                    const int by = (py0 >> (i - 1)) & 1, bx = (px0 >> (i - 1)) & 1;
-                    const float* Y = S + g.yd_off(i) + jy * wi + jx;
-                    float T0 = Y[0] + v;
-                    if (i == Lm && tail && jy == 0 && jx == 0) T0 += S[g.tail_off()];
-                    const float sxb = bx ? -1.f : 1.f, syb = by ? -1.f : 1.f;
-                    v = T0 + sxb * Y[pi] + syb * Y[2 * pi] + (sxb * syb) * Y[3 * pi];
-                }
-                float z2[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-                if (Lm >= 2) {
-                    const float* B2 = S + g.b_off(2) + (py0 / 4 + R) * g.b_S(2) + px0 / 4 + R;
-                    const int bs2 = g.b_bs(2);
-                    float T0 = B2[0] + v;
-                    if (Lm == 2 && tail && py0 == 0 && px0 == 0) T0 += S[g.tail_off()];
-                    float r[4];
-                    haar4(T0, B2[bs2], B2[2 * bs2], B2[3 * bs2], r);
-                    z2[0][0] = r[0]; z2[0][1] = r[1]; z2[1][0] = r[2]; z2[1][1] = r[3];
-                }
-                const float* B1 = S + g.b_off(1);
-                const int S1 = g.b_S(1), bs1 = g.b_bs(1);
-#pragma unroll
-                for (int dy = 0; dy < 2; ++dy)
-#pragma unroll
-                    for (int dx = 0; dx < 2; ++dx) {
-                        const int jy = py0 / 2 + dy, jx = px0 / 2 + dx;
-                        const int o = (jy + R) * S1 + jx + R;
-                        float T0 = B1[o] + bias + z2[dy][dx];
-                        if (Lm == 1 && tail && jy == 0 && jx == 0) T0 += S[g.tail_off()];
-                        float r[4];
-                        haar4(T0, B1[bs1 + o], B1[2 * bs1 + o], B1[3 * bs1 + o], r);
-                        z[2 * dy][2 * dx] = r[0];
-                        z[2 * dy][2 * dx + 1] = r[1];
-                        z[2 * dy + 1][2 * dx] = r[2];
-                        z[2 * dy + 1][2 * dx + 1] = r[3];
+            if (sok) {
+                const float bias = wbase[KK];
+                float z[4][4];
+                if (Lm >= 1) {
+                    // levels Lm..3: v = Z_3 at this lane's level-2 position
+                    float v = 0.f;
+                    for (int i = Lm; i >= 3; --i) {
+                        const int wi = g.Wq() >> i, pi = (g.Hq() >> i) * wi;
+                        const int jy = py0 >> i, jx = px0 >> i;
+                        const int by = (py0 >> (i - 1)) & 1, bx = (px0 >> (i - 1)) & 1;
+                        const float* Y = S + g.yd_off(i) + jy * wi + jx;
+                        float T0 = Y[0] + v;
+                        if (i == Lm && tail && jy == 0 && jx == 0) T0 += S[g.tail_off()];
+                        const float sxb = bx ? -1.f : 1.f, syb = by ? -1.f : 1.f;
+                        v = T0 + sxb * Y[pi] + syb * Y[2 * pi] + (sxb * syb) * Y[3 * pi];
                     }
-            } else {
+                    float z2[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+                    if (Lm >= 2) {
+                        const float* B2 = S + g.b_off(2) + (py0 / 4 + R) * g.b_S(2) + px0 / 4 + R;
+                        const int bs2 = g.b_bs(2);
+                        float T0 = B2[0] + v;
+                        if (Lm == 2 && tail && py0 == 0 && px0 == 0) T0 += S[g.tail_off()];
+                        float r[4];
+                        haar4(T0, B2[bs2], B2[2 * bs2], B2[3 * bs2], r);
+                        z2[0][0] = r[0]; z2[0][1] = r[1]; z2[1][0] = r[2]; z2[1][1] = r[3];
+                    }
+                    const float* B1 = S + g.b_off(1);
+                    const int S1 = g.b_S(1), bs1 = g.b_bs(1);
+#pragma unroll
+                    for (int dy = 0; dy < 2; ++dy)
+#pragma unroll
+                        for (int dx = 0; dx < 2; ++dx) {
+                            const int jy = py0 / 2 + dy, jx = px0 / 2 + dx;
+                            const int o = (jy + R) * S1 + jx + R;
+                            float T0 = B1[o] + bias + z2[dy][dx];
+                            if (Lm == 1 && tail && jy == 0 && jx == 0) T0 += S[g.tail_off()];
+                            float r[4];
+                            haar4(T0, B1[bs1 + o], B1[2 * bs1 + o], B1[3 * bs1 + o], r);
+                            z[2 * dy][2 * dx] = r[0];
+                            z[2 * dy][2 * dx + 1] = r[1];
+                            z[2 * dy + 1][2 * dx] = r[2];
+                            z[2 * dy + 1][2 * dx + 1] = r[3];
+                        }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) z[i][j] = bias;
+                    if (tail && py0 == 0 && px0 == 0) z[0][0] += S[g.tail_off()];
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) z[i][j] = bias;
-                if (tail && py0 == 0 && px0 == 0) z[0][0] += S[g.tail_off()];
+                    for (int j = 0; j < 4; ++j) acc[s][i][j] = fmaf(wbase[KK + 1], acc[s][i][j], z[i][j]);
             }
+            if constexpr (BST) {
+                // rows outside the plane, and blocks or planes that do not
+                // exist, get an offset past the resource's range: dropped
+                const rsrc_t ro = make_rsrc(dstp + (pok ? poff : 0), (uint32_t)(a.H * a.W) * 4u);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[s][i][j] = fmaf(wbase[KK + 1], acc[s][i][j], z[i][j]);
-            ST* op = dstp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
-            if constexpr (VEC) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (py0 + i < a.H && px0 < a.W) gstore4<NHWC>(op + (size_t)i * a.W * ps, ps, acc[s][i]);
-            } else if (NHWC) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (py0 + i < a.H && px0 + j < a.W) from_f32(op[((size_t)i * a.W + j) * ps], acc[s][i][j]);
-            } else if ((a.W & 1) == 0) {
-                // even width: pixel pairs
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p)
-                        if (py0 + i < a.H && px0 + 2 * p < a.W)
-                            store2(op + i * a.W + 2 * p, acc[s][i][2 * p], acc[s][i][2 * p + 1]);
+                for (int i = 0; i < 4; ++i) {
+                    const bool rok = sok && py0 + i < a.H && px0 < a.W;
+                    // (opaque: one store per row, not a branch per side of the select)
+                    const int off = opaque(rok ? ((py0 + i) * a.W + px0) * 4 : kOutOfRange);
+                    bstore4(ro, off, acc[s][i]);
+                }
             } else {
+                ST* op = dstp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
+                if constexpr (VEC) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < 4; ++i)
+                        if (py0 + i < a.H && px0 < a.W) gstore4<NHWC>(op + (size_t)i * a.W * ps, ps, acc[s][i]);
+                } else if (NHWC) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (py0 + i < a.H && px0 + j < a.W) from_f32(op[i * a.W + j], acc[s][i][j]);
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (py0 + i < a.H && px0 + j < a.W) from_f32(op[((size_t)i * a.W + j) * ps], acc[s][i][j]);
+                } else if ((a.W & 1) == 0) {
+                    // even width: pixel pairs
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p)
+                            if (py0 + i < a.H && px0 + 2 * p < a.W)
+                                store2(op + i * a.W + 2 * p, acc[s][i][2 * p], acc[s][i][2 * p + 1]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (py0 + i < a.H && px0 + j < a.W) from_f32(op[i * a.W + j], acc[s][i][j]);
+                }
             }
         }
     }
