@@ -646,7 +646,10 @@ wtc_fused_kernel(const FusedArgs a) {
     // slower on 14x14 to 30x30 planes)
     constexpr bool PFS = static_prefetch<G, BWD, VEC, PFU>();
     // buffer-resource output stores (fp32 NCHW planes, byte offsets < 2^31)
-    constexpr bool BST = PFS && !G::kNHWC && sizeof(ST) == 4;
+    // (also the two-blocks-per-quad backward whose next plane is loaded
+    // during the current one: the loop-top wait for those loads then leaves
+    // this plane's dx stores outstanding)
+    constexpr bool BST = (PFS || next_plane_units<G, BWD, BPQ, VEC>() > 0) && !G::kNHWC && sizeof(ST) == 4;
     const bool pf_on = PFS || (!DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0);
     float pf[PFU][UW];
     // With 4-pixel units the decode of each unit is done once per segment: its
@@ -940,7 +943,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // the segment's first prefetch has landed: no load is pending on entry to
     // the plane loop, so the loop-top wait counts only the previous
     // iteration's prefetch loads and the stores issued after them
-    if constexpr (PFS) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    if constexpr (PFS || XPF) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
         const int b = bb + slot;
@@ -1450,16 +1453,20 @@ wtc_fused_kernel(const FusedArgs a) {
                 // C_i^du[ky][kx] = sum_m X[m] G[m - (ky - R, kx - R)] (G with its zero
                 // halo): this role takes kernel row dky and its band rows; a chunk of
                 // 4 X values and 4 + 2R values of one G row serve all K columns.
-                if (dactive) {
+                // (the role is decoded here from an opaque copy of tid, so none
+                // of it is held in registers through the rest of the plane)
+                const int drl = opaque(tid);
+                const int du4 = drl & 3, dky4 = (drl >> 2) % K, dsb4 = (drl >> 2) / K;
+                if (drl < droles) {
                     float cv[K];
 #pragma unroll
                     for (int kx = 0; kx < K; ++kx) cv[kx] = 0.f;
                     for (int s2 = 0; s2 < g.NP(); ++s2) {
                         if (bb + s2 >= b_end) break;
                         const float* Sl = lds + s2 * g.slot();
-                        for (int my = dsb; my < hi; my += g.dsub()) {
-                            const float* XR = Sl + g.xb_off(i) + du * hi * wi + my * wi;
-                            const float* GR = Sl + g.b_off(i) + du * bs + (my - dky + 2 * R) * Si;
+                        for (int my = dsb4; my < hi; my += g.dsub()) {
+                            const float* XR = Sl + g.xb_off(i) + du4 * hi * wi + my * wi;
+                            const float* GR = Sl + g.b_off(i) + du4 * bs + (my - dky4 + 2 * R) * Si;
 #pragma unroll
                             for (int mx0 = 0; mx0 < wi; mx0 += 4) {
                                 float xv[4], gv[4 + 2 * R];
