@@ -649,7 +649,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // (also the two-blocks-per-quad backward whose next plane is loaded
     // during the current one: the loop-top wait for those loads then leaves
     // this plane's dx stores outstanding)
-    constexpr bool BST = (PFS || next_plane_units<G, BWD, BPQ, VEC>() > 0) && !G::kNHWC && sizeof(ST) == 4;
+    constexpr bool BST = (PFS || next_plane_units<G, BWD, BPQ, VEC>() > 0) && VEC && !G::kNHWC && sizeof(ST) == 4;
     const bool pf_on = PFS || (!DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0);
     float pf[PFU][UW];
     // With 4-pixel units the decode of each unit is done once per segment: its
@@ -1580,14 +1580,19 @@ wtc_fused_kernel(const FusedArgs a) {
                     for (int j = 0; j < 4; ++j) acc[s][i][j] = fmaf(wbase[KK + 1], acc[s][i][j], z[i][j]);
             }
             if constexpr (BST) {
-                // rows outside the plane, and blocks or planes that do not
-                // exist, get an offset past the resource's range: dropped
-                const rsrc_t ro = make_rsrc(dstp + (pok ? poff : 0), (uint32_t)(a.H * a.W) * 4u);
+                // One resource over the workgroup's NP planes of channel c
+                // (uniform, so no loop over distinct descriptors); a lane's
+                // plane starts slot * C planes in.  Rows outside the plane, and
+                // blocks or planes that do not exist, get an offset past the
+                // range: dropped.
+                const rsrc_t ro = make_rsrc(dstp + (size_t)bb * cplane + (size_t)c * plane_sz,
+                                            (uint32_t)((g.NP() - 1) * cplane + a.H * a.W) * 4u);
+                const int soff = (g.NP() == 1 ? 0 : slot * cplane) * 4;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool rok = sok && py0 + i < a.H && px0 < a.W;
                     // (opaque: one store per row, not a branch per side of the select)
-                    const int off = opaque(rok ? ((py0 + i) * a.W + px0) * 4 : kOutOfRange);
+                    const int off = opaque(rok ? soff + ((py0 + i) * a.W + px0) * 4 : kOutOfRange);
                     bstore4(ro, off, acc[s][i]);
                 }
             } else {
