@@ -538,6 +538,18 @@ constexpr bool static_prefetch() {
     return false;
 }
 
+// With a static prefetch and a layout in which no other array overlaps the
+// level-0 plane, that plane is dead once phase 2 ends: the next plane is
+// committed there and then (and the one after it issued), so the plane loop
+// needs no barrier and no staging at its top.  (Measured on 128x128 planes:
+// one level 249.6 -> 241.2 us; without levels 169.4 -> 180.0 us, so the plain
+// depthwise convolution keeps the staging at the loop top.)
+template <class G, bool PFS>
+constexpr bool early_commit() {
+    if constexpr (PFS && G::kFixed) return !G::ovl() && G::bovl() == 0 && G::Lm() >= 1;
+    return false;
+}
+
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, class G>
 __global__ void __launch_bounds__(G::kMaxThreads) __attribute__((amdgpu_waves_per_eu(kernel_waves<G, BWD, BPQ>())))
 wtc_fused_kernel(const FusedArgs a) {
@@ -650,6 +662,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // during the current one: the loop-top wait for those loads then leaves
     // this plane's dx stores outstanding)
     constexpr bool BST = (PFS || next_plane_units<G, BWD, BPQ, VEC>() > 0) && VEC && !G::kNHWC && sizeof(ST) == 4;
+    constexpr bool EC = early_commit<G, PFS>();
     const bool pf_on = PFS || (!DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0);
     float pf[PFU][UW];
     // With 4-pixel units the decode of each unit is done once per segment: its
@@ -944,6 +957,12 @@ wtc_fused_kernel(const FusedArgs a) {
     // the plane loop, so the loop-top wait counts only the previous
     // iteration's prefetch loads and the stores issued after them
     if constexpr (PFS || XPF) __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    if constexpr (EC) {
+        // the segment's first planes go in here; the loop commits the others
+        pf_commit(b_begin);
+        lds_barrier();
+        pf_issue(b_begin + g.NP() < b_end ? b_begin + g.NP() : b_begin);
+    }
     for (int bb = b_begin; bb < b_end; bb += g.NP()) {
         roles(opaque(tid0));
         const int b = bb + slot;
@@ -977,7 +996,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 // otherwise also wait for the copy, vector-memory counts being in order)
                 if (!BWD && bb + g.NP() < b_end) stage_issue(bb + g.NP(), c, b_end);
             }
-        } else {
+        } else if constexpr (!EC) {
         lds_barrier();  // the previous plane is fully consumed
 
         // ---------------- phase 1: stage the planes in LDS ----------------
@@ -1208,6 +1227,15 @@ wtc_fused_kernel(const FusedArgs a) {
         lds_barrier();
         // the level-0 plane is dead: the next planes' copies land during the rest
         if (DL && !SDL && bb + g.NP() < b_end) dl_issue(srcp, g.a0_off(), g.a0_S(), R, R, bb + g.NP(), c, b_end);
+        if constexpr (EC) {
+            // the next planes (prefetched during this plane's phase 2) go in
+            // now -- phases 3..6 never read the level-0 plane, and their
+            // barriers order these writes before the next phase 2 -- and the
+            // planes after them are issued (a segment's last planes reload
+            // the current group, which exists)
+            pf_commit(bb + g.NP());
+            pf_issue(bb + 2 * g.NP() < b_end ? bb + 2 * g.NP() : bb);
+        }
 
         // Two-blocks-per-quad backward: the first block's first two x row pairs
         // for the level-1 analysis below are loaded now, so their round trip
