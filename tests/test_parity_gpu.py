@@ -117,6 +117,25 @@ def test_runtime_geometry_direct_loads(B, C, H, W, L, k, seed, dtype):
     _case(B, C, H, W, L, k, seed, dtype)
 
 
+# Planes smaller than the fixed-geometry instance they run on (zero-extended
+# to its size): the prefetch covers fewer units, rows past the plane are
+# dropped by the output resource's range check, and the backward stages its
+# planes without the next-plane loads.
+PARTIAL_FIXED = [
+    (2, 3, 124, 124, 1, 5, 90, "fp32"),    # 128x128 instance, one level (early commit)
+    (1, 3, 124, 124, 3, 5, 91, "fp32"),    # 128x128 instance, three levels
+    (1, 2, 124, 120, 5, 5, 92, "fp32"),    # 128x128 instance, five levels, unequal sides
+    (2, 2, 108, 108, 2, 5, 93, "fp32"),    # 112x112 instance
+    (3, 4, 28, 28, 3, 5, 94, "bf16"),      # bf16 32x32 instance
+    (2, 3, 124, 124, 0, 5, 95, "fp32"),    # depthwise conv on the 128x128 instance
+]
+
+
+@pytest.mark.parametrize("B,C,H,W,L,k,seed,dtype", PARTIAL_FIXED)
+def test_partial_fixed_geometry(B, C, H, W, L, k, seed, dtype):
+    _case(B, C, H, W, L, k, seed, dtype)
+
+
 def test_bf16_odd_plane():
     _case(3, 4, 14, 14, 2, 5, 60, "bf16")
 
