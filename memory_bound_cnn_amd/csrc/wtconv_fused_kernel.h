@@ -283,11 +283,17 @@ constexpr int kOutOfRange = 0x7FFFFFF0;       // past every range used here (< 2
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
-// four floats at byte offset `off` of the resource, one 16-byte store
-__device__ __forceinline__ void bstore4(rsrc_t r, int off, const float (&v)[4]) {
+// four pixels at byte offset `off` of the resource: one 16-byte store of
+// floats, or one 8-byte store of bfloat16 (rounded to nearest even)
+__device__ __forceinline__ void bstore4(rsrc_t r, int off, const float (&v)[4], float*) {
     typedef unsigned int u4 __attribute__((ext_vector_type(4)));
     const u4 d = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
     __builtin_amdgcn_raw_buffer_store_b128(d, r, off, 0, 0);
+}
+__device__ __forceinline__ void bstore4(rsrc_t r, int off, const float (&v)[4], bf16_t*) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    const u2 d = {bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
 }
 
 // Pixel (y, x) of a plane, zero outside [0,H) x [0,W).
@@ -657,11 +663,11 @@ wtc_fused_kernel(const FusedArgs a) {
     // registers beside its correlation accumulators it spills, measured 5-13 %
     // slower on 14x14 to 30x30 planes)
     constexpr bool PFS = static_prefetch<G, BWD, VEC, PFU>();
-    // buffer-resource output stores (fp32 NCHW planes, byte offsets < 2^31)
+    // buffer-resource output stores (NCHW planes, byte offsets < 2^31)
     // (also the two-blocks-per-quad backward whose next plane is loaded
     // during the current one: the loop-top wait for those loads then leaves
     // this plane's dx stores outstanding)
-    constexpr bool BST = (PFS || next_plane_units<G, BWD, BPQ, VEC>() > 0) && VEC && !G::kNHWC && sizeof(ST) == 4;
+    constexpr bool BST = (PFS || next_plane_units<G, BWD, BPQ, VEC>() > 0) && VEC && !G::kNHWC;
     constexpr bool EC = early_commit<G, PFS>();
     const bool pf_on = PFS || (!DL && !(BWD && BPQ > 1) && !(BWD && !G::kFixed) && a.pf_on != 0);
     float pf[PFU][UW];
@@ -1232,9 +1238,10 @@ wtc_fused_kernel(const FusedArgs a) {
             // now -- phases 3..6 never read the level-0 plane, and their
             // barriers order these writes before the next phase 2 -- and the
             // planes after them are issued (a segment's last planes reload
-            // the current group, which exists)
+            // the group loaded most recently, which exists and is in L2)
             pf_commit(bb + g.NP());
-            pf_issue(bb + 2 * g.NP() < b_end ? bb + 2 * g.NP() : bb);
+            const int nb2 = bb + 2 * g.NP();
+            pf_issue(nb2 < b_end ? nb2 : (bb + g.NP() < b_end ? bb + g.NP() : bb));
         }
 
         // Two-blocks-per-quad backward: the first block's first two x row pairs
@@ -1613,15 +1620,16 @@ wtc_fused_kernel(const FusedArgs a) {
                 // plane starts slot * C planes in.  Rows outside the plane, and
                 // blocks or planes that do not exist, get an offset past the
                 // range: dropped.
+                constexpr int EB = (int)sizeof(ST);
                 const rsrc_t ro = make_rsrc(dstp + (size_t)bb * cplane + (size_t)c * plane_sz,
-                                            (uint32_t)((g.NP() - 1) * cplane + a.H * a.W) * 4u);
-                const int soff = (g.NP() == 1 ? 0 : slot * cplane) * 4;
+                                            (uint32_t)((g.NP() - 1) * cplane + a.H * a.W) * (uint32_t)EB);
+                const int soff = (g.NP() == 1 ? 0 : slot * cplane) * EB;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const bool rok = sok && py0 + i < a.H && px0 < a.W;
                     // (opaque: one store per row, not a branch per side of the select)
-                    const int off = opaque(rok ? soff + ((py0 + i) * a.W + px0) * 4 : kOutOfRange);
-                    bstore4(ro, off, acc[s][i]);
+                    const int off = opaque(rok ? soff + ((py0 + i) * a.W + px0) * EB : kOutOfRange);
+                    bstore4(ro, off, acc[s][i], (ST*)nullptr);
                 }
             } else {
                 ST* op = dstp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
