@@ -530,6 +530,15 @@ constexpr int next_plane_units() {
     return 0;
 }
 
+template <class G>
+constexpr bool tail_possible() {
+    if constexpr (G::kFixed) {
+        constexpr int T = G::Lm() >= 3 ? (1 << G::Lm()) : 8;
+        return G::kHq == T && G::kWq == T;
+    }
+    return true;
+}
+
 // Fixed-geometry forward whose register prefetch holds every 4-pixel unit of
 // its plane group: the prefetch is on for every plane (the last plane of a
 // segment loads its own group again, which is in L2) and the output stores go
@@ -600,7 +609,12 @@ wtc_fused_kernel(const FusedArgs a) {
     }
     const int c_first = (int)(q0 / a.B);
     const int Lm = g.Lm();
-    const bool tail = a.L > Lm;
+    // Levels past the last one with a grid above 1 x 1 (the tail) exist only
+    // when the whole plane fits one level-Lm cell, i.e. when the plane is
+    // zero-extended to max(8, 2^Lm) on both sides: a fixed geometry of any
+    // other size never has a tail, and its kernel carries no tail term.
+    constexpr bool TAILS = !G::kFixed || tail_possible<G>();
+    const bool tail = TAILS && a.L > Lm;
     const size_t plane_sz = (size_t)a.H * a.W;
     // global addressing: plane (b, c) starts at b C H W + c (channels-last) or
     // (b C + c) H W (NCHW); pixel (y, x) of a plane is (y W + x) ps further
