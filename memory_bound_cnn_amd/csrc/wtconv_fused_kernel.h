@@ -359,6 +359,7 @@ struct RtGeom {
     static constexpr bool kNHWC = NHWC;  // activations channels-last: pixel stride C
     static constexpr bool kXSeg = false;
     static constexpr bool kFixed = false;
+    static constexpr bool kWhole = false;
     static constexpr bool kNoLevels = false;
     static constexpr int kDeep = LMX > 3 ? LMX - 2 : 1;
     static constexpr bool kSub = true;   // may run the LL problem of a peeled plane
@@ -397,7 +398,7 @@ struct RtGeom {
 };
 
 template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, int MODE, int ESZ,
-          bool NHWC = false>
+          bool NHWC = false, bool WHOLE = false>
 struct CtGeom {
     static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, MODE, ESZ);
     static constexpr bool kDL = MODE == 1;
@@ -407,6 +408,7 @@ struct CtGeom {
     static constexpr bool kXSeg =
         MODE == 1 && (!BWDL || red_len(NTHR, K, LM, NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1) <= lay.a0_off);
     static constexpr bool kFixed = true;
+    static constexpr bool kWhole = WHOLE;   // the plane is exactly HQ x WQ
     static constexpr bool kNoLevels = LM == 0;
     static constexpr int kDeep = kMaxLm - 2;
     // the LL problem of a peeled plane is over 64 pixels wide (its parent did
@@ -530,6 +532,20 @@ constexpr int next_plane_units() {
     return 0;
 }
 
+// The plane's height and width: fixed at compile time in the instances for
+// planes that fill their zero-extended size exactly ("whole" planes), so that
+// their bounds tests fold away and their row strides are shifts.
+template <class G>
+__device__ __forceinline__ int plane_h(const FusedArgs& a) {
+    if constexpr (G::kWhole) return G::kHq;
+    else return a.H;
+}
+template <class G>
+__device__ __forceinline__ int plane_w(const FusedArgs& a) {
+    if constexpr (G::kWhole) return G::kWq;
+    else return a.W;
+}
+
 template <class G>
 constexpr bool tail_possible() {
     if constexpr (G::kFixed) {
@@ -585,6 +601,8 @@ wtc_fused_kernel(const FusedArgs a) {
     extern __shared__ __align__(16) float lds[];
 
     const G g(a);
+    // plane size: a compile-time constant in whole-plane instances
+    const int aH = plane_h<G>(a), aW = plane_w<G>(a);
     const int tid0 = threadIdx.x;
     const int nthr = g.nthr(), nquads = nthr >> 2;
     // This workgroup's planes: [q0, q1) in channel-major order (q = c*B + b),
@@ -615,7 +633,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // other size never has a tail, and its kernel carries no tail term.
     constexpr bool TAILS = !G::kFixed || tail_possible<G>();
     const bool tail = TAILS && a.L > Lm;
-    const size_t plane_sz = (size_t)a.H * a.W;
+    const size_t plane_sz = (size_t)aH * aW;
     // global addressing: plane (b, c) starts at b C H W + c (channels-last) or
     // (b C + c) H W (NCHW); pixel (y, x) of a plane is (y W + x) ps further
     constexpr bool NHWC = G::kNHWC;
@@ -669,8 +687,8 @@ wtc_fused_kernel(const FusedArgs a) {
     ST* dstp = reinterpret_cast<ST*>(a.dst);
 
     // ---- plane staging: units of UW pixels, unit e -> (slot, row, column) ----
-    const int wv = VEC ? (a.W >> 2) : a.W;
-    const int per = a.H * wv;
+    const int wv = VEC ? (aW >> 2) : aW;
+    const int per = aH * wv;
     const FastDiv dper = make_div(per), dwv = make_div(wv);
     // (the backward kernel with two blocks per quad never has the capacity; the
     // runtime-geometry backward stages synchronously: with a plane held in
@@ -703,7 +721,7 @@ wtc_fused_kernel(const FusedArgs a) {
             if (e < g.NP() * per) {
                 const int s2 = fdiv(e, dper), m = e - s2 * per;
                 const int y = fdiv(m, dwv), xq = m - y * wv;
-                pf_goff[k] = s2 * cplane + (y * a.W + xq * UW) * (NHWC ? a.C : 1);
+                pf_goff[k] = s2 * cplane + (y * aW + xq * UW) * (NHWC ? a.C : 1);
                 pf_lds[k] = (s2 << 16) | (s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW);
             }
         }
@@ -802,16 +820,16 @@ wtc_fused_kernel(const FusedArgs a) {
                     const int s2 = NPc == 1 ? 0 : j / G::Hq();
                     const int r = j - s2 * G::Hq();
                     if (JT % NW != 0 && j >= JT) continue;
-                    if (!decltype(full)::value && r >= a.H) continue;
+                    if (!decltype(full)::value && r >= aH) continue;
                     if (NPc > 1 && bbn + s2 >= bend) continue;
                     __builtin_amdgcn_global_load_lds(
-                        (const void*)(plane_at(base, bbn + s2, ch) + ((size_t)r * a.W + lane) * ps),
+                        (const void*)(plane_at(base, bbn + s2, ch) + ((size_t)r * aW + lane) * ps),
                         (__attribute__((address_space(3))) void*)(lds + s2 * g.slot() + roff + (r + rr) * rS + rc),
                         4, 0, 0);
                 }
             };
-            if (lane < a.W) {
-                if (a.H == G::Hq()) rows(std::true_type{});
+            if (lane < aW) {
+                if (aH == G::Hq()) rows(std::true_type{});
                 else rows(std::false_type{});
             }
         } else if constexpr (DL && !SDL) {
@@ -824,11 +842,11 @@ wtc_fused_kernel(const FusedArgs a) {
             const int nw = nthr >> 6;
             const ST* pb = plane_at(base, bbn, ch);
             float* lb = lds + roff + rr * rS + rc;
-            for (int c0 = 0; c0 < a.W; c0 += 64) {
-                if (c0 + lane >= a.W) break;
-                const ST* src = pb + ((size_t)wave * a.W + c0 + lane) * ps;
+            for (int c0 = 0; c0 < aW; c0 += 64) {
+                if (c0 + lane >= aW) break;
+                const ST* src = pb + ((size_t)wave * aW + c0 + lane) * ps;
                 float* dst = lb + wave * rS + c0;
-                for (int r = wave; r < a.H; r += nw, src += (size_t)nw * a.W * ps, dst += nw * rS)
+                for (int r = wave; r < aH; r += nw, src += (size_t)nw * aW * ps, dst += nw * rS)
                     __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)dst,
                                                      4, 0, 0);
             }
@@ -843,7 +861,7 @@ wtc_fused_kernel(const FusedArgs a) {
             constexpr int CH = (G::Hq() * G::Wq() / 2 + 63) / 64, JT = NPc * CH;
             constexpr int NJ = (JT + NW - 1) / NW;
             const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = tid0 & 63;
-            const int words = (a.H * a.W) >> 1;
+            const int words = (aH * aW) >> 1;
             auto chunks = [&](auto full) {
 #pragma unroll
                 for (int jj = 0; jj < NJ; ++jj) {
@@ -866,7 +884,7 @@ wtc_fused_kernel(const FusedArgs a) {
             if (bbn >= bend) return;
             const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6), lane = opaque(tid0) & 63;
             const int nw = nthr >> 6;
-            const int words = (a.H * a.W) >> 1;
+            const int words = (aH * aW) >> 1;
             const uint32_t* src = reinterpret_cast<const uint32_t*>(srcp + ((size_t)bbn * a.C + ch) * plane_sz);
             float* dst = lds + g.st_off();
             for (int k = wave * 64; k < words; k += nw * 64)
@@ -884,7 +902,7 @@ wtc_fused_kernel(const FusedArgs a) {
     if (pf_on) pf_issue(b_begin);
     if constexpr (XDL) {
         for (int s2 = 0; s2 < g.NP(); ++s2)
-            zero_ring(lds + s2 * g.slot() + g.xp_off(), g.Hq(), g.xp_S(), 0, a.H, 0, a.W, tid, nthr);
+            zero_ring(lds + s2 * g.slot() + g.xp_off(), g.Hq(), g.xp_S(), 0, aH, 0, aW, tid, nthr);
         if (!pre) dl_issue(auxp, g.xp_off(), g.xp_S(), 0, 0, b_begin, c, b_end);
     }
     if constexpr (DL && !SDL) {
@@ -898,7 +916,7 @@ wtc_fused_kernel(const FusedArgs a) {
     // slots), and per plane where regions overlap ----
     for (int s2 = 0; s2 < g.NP(); ++s2) {
         float* S = lds + s2 * g.slot();
-        zero_ring(S + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
+        zero_ring(S + g.a0_off(), g.a0_rows(), g.a0_S(), R, aH, R, aW, tid, nthr);
         for (int i = 1; i <= Lm; ++i)
             for (int u = 0; u < 4; ++u)
                 zero_ring(S + g.b_off(i) + u * g.b_bs(i), g.b_rows(i), g.b_S(i), R, g.Hq() >> i, R,
@@ -965,7 +983,7 @@ wtc_fused_kernel(const FusedArgs a) {
     constexpr int XPU = XPF ? XPU0 : 1;
     constexpr int XWV = XPF ? G::kWq / 4 : 1;   // 4-pixel units per plane row
     constexpr int XRPK = XPF ? G::kNthr / XWV : 1;   // plane rows per unit step
-    const bool xwhole = XPF && a.H == g.Hq() && a.W == g.Wq();
+    const bool xwhole = XPF && aH == g.Hq() && aW == g.Wq();
     float xpf[XPU][4];
 #pragma unroll
     for (int k = 0; k < XPU; ++k)
@@ -998,7 +1016,7 @@ wtc_fused_kernel(const FusedArgs a) {
             if constexpr (SDL) {
                 // widen the staged 16-bit pixels into the level-0 plane (4 per unit)
                 typedef uint32_t lds_u2 __attribute__((ext_vector_type(2)));
-                const int wq = a.W >> 2, per_plane = a.H * wq;
+                const int wq = aW >> 2, per_plane = aH * wq;
                 for (int e = tid; e < g.NP() * per_plane; e += nthr) {
                     const int s2 = g.NP() == 1 ? 0 : e / per_plane, m = e - s2 * per_plane;
                     if (bb + s2 >= b_end) continue;
@@ -1057,7 +1075,7 @@ wtc_fused_kernel(const FusedArgs a) {
                     const int s2 = fdiv(e, dper), m = e - s2 * per;
                     const int y = fdiv(m, dwv), xq = m - y * wv;
                     if (e < g.NP() * per && bb + s2 < b_end)
-                        gload4<NHWC>(plane_at(srcp, bb + s2, c) + ((size_t)y * a.W + xq * UW) * ps, ps, sv[k]);
+                        gload4<NHWC>(plane_at(srcp, bb + s2, c) + ((size_t)y * aW + xq * UW) * ps, ps, sv[k]);
                 }
 #pragma unroll
                 for (int k = 0; k < SB && k0 + k < SU; ++k) {
@@ -1076,7 +1094,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 const int s2 = fdiv(e, dper), m = e - s2 * per;
                 if (bb + s2 >= b_end) continue;
                 const int y = fdiv(m, dwv), xq = m - y * wv;
-                const ST* pl = plane_at(srcp, bb + s2, c) + ((size_t)y * a.W + xq * UW) * ps;
+                const ST* pl = plane_at(srcp, bb + s2, c) + ((size_t)y * aW + xq * UW) * ps;
                 float* d = lds + s2 * g.slot() + g.a0_off() + (y + R) * g.a0_S() + R + xq * UW;
                 if constexpr (VEC) {
                     float v[4];
@@ -1089,10 +1107,10 @@ wtc_fused_kernel(const FusedArgs a) {
             }
         }
         if (g.bovl() > 0) {
-            zero_rings<R>(lds, g, g.a0_off(), 0, 1, g.a0_rows(), g.a0_S(), a.H, a.W, tid, nthr);
+            zero_rings<R>(lds, g, g.a0_off(), 0, 1, g.a0_rows(), g.a0_S(), aH, aW, tid, nthr);
         } else if (g.ovl()) {
             for (int s2 = 0; s2 < g.NP(); ++s2)
-                zero_ring(lds + s2 * g.slot() + g.a0_off(), g.a0_rows(), g.a0_S(), R, a.H, R, a.W, tid, nthr);
+                zero_ring(lds + s2 * g.slot() + g.a0_off(), g.a0_rows(), g.a0_S(), R, aH, R, aW, tid, nthr);
         }
         lds_barrier();
         // the next planes' loads fly while this plane is computed
@@ -1149,10 +1167,10 @@ wtc_fused_kernel(const FusedArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lds_row<4, 4>(xr + i * g.xp_S(), xo[i]);
             } else if constexpr (BWD) {
-                const ST* xp = auxp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
+                const ST* xp = auxp + poff + (size_t)opaque(py0 * aW + px0) * ps;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    ld_row4<VEC, NHWC>(xp + (size_t)i * a.W * ps, py0 + i < a.H, px0, a.W, xo[i], ps);
+                    ld_row4<VEC, NHWC>(xp + (size_t)i * aW * ps, py0 + i < aH, px0, aW, xo[i], ps);
                 if constexpr (XQB) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -1269,15 +1287,15 @@ wtc_fused_kernel(const FusedArgs a) {
         float xpre0[XPRE ? 2 : 1][2][4], xpre1[XPRE ? 2 : 1][2][4];
         if constexpr (XPRE) {
             const int qy = qyv[0], qx = qxv[0];
-            const ST* xp = auxp + poff + (size_t)opaque(8 * qy * a.W + 8 * qx);
+            const ST* xp = auxp + poff + (size_t)opaque(8 * qy * aW + 8 * qx);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const ST* p0r = xp + (size_t)(2 * h) * a.W;
+                const ST* p0r = xp + (size_t)(2 * h) * aW;
                 const int yh = 8 * qy + 2 * h;
-                ld_row4<VEC, NHWC>(p0r, yh < a.H, 8 * qx, a.W, xpre0[h][0]);
-                ld_row4<VEC, NHWC>(p0r + 4, yh < a.H, 8 * qx + 4, a.W, xpre0[h][1]);
-                ld_row4<VEC, NHWC>(p0r + (size_t)a.W, yh + 1 < a.H, 8 * qx, a.W, xpre1[h][0]);
-                ld_row4<VEC, NHWC>(p0r + (size_t)(a.W + 4), yh + 1 < a.H, 8 * qx + 4, a.W, xpre1[h][1]);
+                ld_row4<VEC, NHWC>(p0r, yh < aH, 8 * qx, aW, xpre0[h][0]);
+                ld_row4<VEC, NHWC>(p0r + 4, yh < aH, 8 * qx + 4, aW, xpre0[h][1]);
+                ld_row4<VEC, NHWC>(p0r + (size_t)aW, yh + 1 < aH, 8 * qx, aW, xpre1[h][0]);
+                ld_row4<VEC, NHWC>(p0r + (size_t)(aW + 4), yh + 1 < aH, 8 * qx + 4, aW, xpre1[h][1]);
             }
         }
 
@@ -1340,7 +1358,7 @@ wtc_fused_kernel(const FusedArgs a) {
                 // x over the quad's 8x8 block -> band t (and LL) at levels 1, 2, 3
                 float ll1[4][4];
                 float xr0[2][2][4], xr1[2][2][4];
-                const ST* xp = auxp + poff + (size_t)opaque(8 * qy * a.W + 8 * qx) * ps;
+                const ST* xp = auxp + poff + (size_t)opaque(8 * qy * aW + 8 * qx) * ps;
 #pragma unroll
                 for (int jy = 0; jy < 4; ++jy) {
                     float r0[2][4], r1[2][4];
@@ -1371,12 +1389,12 @@ wtc_fused_kernel(const FusedArgs a) {
                     } else if ((jy & 1) == 0) {
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            const ST* p0r = xp + (size_t)(2 * (jy + h)) * a.W * ps;
+                            const ST* p0r = xp + (size_t)(2 * (jy + h)) * aW * ps;
                             const int yh = y0 + 2 * h;
-                            ld_row4<VEC, NHWC>(p0r, yh < a.H, 8 * qx, a.W, xr0[h][0], ps);
-                            ld_row4<VEC, NHWC>(p0r + 4 * ps, yh < a.H, 8 * qx + 4, a.W, xr0[h][1], ps);
-                            ld_row4<VEC, NHWC>(p0r + (size_t)a.W * ps, yh + 1 < a.H, 8 * qx, a.W, xr1[h][0], ps);
-                            ld_row4<VEC, NHWC>(p0r + (size_t)(a.W + 4) * ps, yh + 1 < a.H, 8 * qx + 4, a.W, xr1[h][1], ps);
+                            ld_row4<VEC, NHWC>(p0r, yh < aH, 8 * qx, aW, xr0[h][0], ps);
+                            ld_row4<VEC, NHWC>(p0r + 4 * ps, yh < aH, 8 * qx + 4, aW, xr0[h][1], ps);
+                            ld_row4<VEC, NHWC>(p0r + (size_t)aW * ps, yh + 1 < aH, 8 * qx, aW, xr1[h][0], ps);
+                            ld_row4<VEC, NHWC>(p0r + (size_t)(aW + 4) * ps, yh + 1 < aH, 8 * qx + 4, aW, xr1[h][1], ps);
                         }
                     }
 #pragma unroll
@@ -1636,41 +1654,41 @@ wtc_fused_kernel(const FusedArgs a) {
                 // range: dropped.
                 constexpr int EB = (int)sizeof(ST);
                 const rsrc_t ro = make_rsrc(dstp + (size_t)bb * cplane + (size_t)c * plane_sz,
-                                            (uint32_t)((g.NP() - 1) * cplane + a.H * a.W) * (uint32_t)EB);
+                                            (uint32_t)((g.NP() - 1) * cplane + aH * aW) * (uint32_t)EB);
                 const int soff = (g.NP() == 1 ? 0 : slot * cplane) * EB;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bool rok = sok && py0 + i < a.H && px0 < a.W;
+                    const bool rok = sok && py0 + i < aH && px0 < aW;
                     // (opaque: one store per row, not a branch per side of the select)
-                    const int off = opaque(rok ? soff + ((py0 + i) * a.W + px0) * EB : kOutOfRange);
+                    const int off = opaque(rok ? soff + ((py0 + i) * aW + px0) * EB : kOutOfRange);
                     bstore4(ro, off, acc[s][i], (ST*)nullptr);
                 }
             } else {
-                ST* op = dstp + poff + (size_t)opaque(py0 * a.W + px0) * ps;
+                ST* op = dstp + poff + (size_t)opaque(py0 * aW + px0) * ps;
                 if constexpr (VEC) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        if (py0 + i < a.H && px0 < a.W) gstore4<NHWC>(op + (size_t)i * a.W * ps, ps, acc[s][i]);
+                        if (py0 + i < aH && px0 < aW) gstore4<NHWC>(op + (size_t)i * aW * ps, ps, acc[s][i]);
                 } else if (NHWC) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            if (py0 + i < a.H && px0 + j < a.W) from_f32(op[((size_t)i * a.W + j) * ps], acc[s][i][j]);
-                } else if ((a.W & 1) == 0) {
+                            if (py0 + i < aH && px0 + j < aW) from_f32(op[((size_t)i * aW + j) * ps], acc[s][i][j]);
+                } else if ((aW & 1) == 0) {
                     // even width: pixel pairs
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int p = 0; p < 2; ++p)
-                            if (py0 + i < a.H && px0 + 2 * p < a.W)
-                                store2(op + i * a.W + 2 * p, acc[s][i][2 * p], acc[s][i][2 * p + 1]);
+                            if (py0 + i < aH && px0 + 2 * p < aW)
+                                store2(op + i * aW + 2 * p, acc[s][i][2 * p], acc[s][i][2 * p + 1]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            if (py0 + i < a.H && px0 + j < a.W) from_f32(op[i * a.W + j], acc[s][i][j]);
+                            if (py0 + i < aH && px0 + j < aW) from_f32(op[i * aW + j], acc[s][i][j]);
                 }
             }
         }
@@ -1832,17 +1850,18 @@ namespace wtc {
 namespace fused_detail {
 
 // Launch the fixed-geometry instantiation if the plan matches it exactly.
+// A whole-plane instance (WH) matches only planes of exactly HQ x WQ pixels.
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
-          int NTHR, int BOVL, int MODE = 0, bool NH = false>
+          int NTHR, int BOVL, int MODE = 0, bool NH = false, bool WH = false>
 bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
                 hipError_t* err) {
     if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
         nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || a.lay.mode != MODE ||
-        (a.nhwc != 0) != NH)
+        (a.nhwc != 0) != NH || (WH && (a.H != HQ || a.W != WQ)))
         return false;
     *err = launch_t<K, ST, BWD, BPQ, VEC,
-                    CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST), NH>>(a, nthr, lds, grid,
-                                                                                                 st);
+                    CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST), NH, WH>>(a, nthr, lds,
+                                                                                                     grid, st);
     return true;
 }
 

@@ -11,6 +11,16 @@ bool launch_fused_static_p128a(const FusedArgs& a, int dtype, int bwd, int bpq, 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     bool hit = false;
+    // planes of exactly 128 x 128 pixels: whole-plane instances
+    if (!hit && dtype == WTC_FP32 && bwd == 0)
+        hit = try_static<5, float, 0, 2, true, 128, 128, 1, 1, 1, 512, 0, 0, false, true>(a, bpq, nthr, lds, grid, st, &e);
+    if (!hit && dtype == WTC_FP32 && bwd == 1)
+        hit = try_static<5, float, 1, 2, true, 128, 128, 1, 1, 1, 512, 0, 0, false, true>(a, bpq, nthr, lds, grid, st, &e);
+    if (!hit && dtype == WTC_FP32 && bwd == 0)
+        hit = try_static<5, float, 0, 2, true, 128, 128, 2, 1, 1, 512, 0, 0, false, true>(a, bpq, nthr, lds, grid, st, &e);
+    if (!hit && dtype == WTC_FP32 && bwd == 1)
+        hit = try_static<5, float, 1, 2, true, 128, 128, 2, 1, 1, 512, 0, 0, false, true>(a, bpq, nthr, lds, grid, st, &e);
+    // other planes zero-extended to 128 x 128
     if (!hit && dtype == WTC_FP32 && bwd == 0)
         hit = try_static<5, float, 0, 2, true, 128, 128, 1, 1, 1, 512, 0>(a, bpq, nthr, lds, grid, st, &e);
     if (!hit && dtype == WTC_FP32 && bwd == 1)
