@@ -360,6 +360,7 @@ struct RtGeom {
     static constexpr bool kXSeg = false;
     static constexpr bool kFixed = false;
     static constexpr bool kWhole = false;
+    static constexpr int kPH = 0, kPW = 0;
     static constexpr bool kNoLevels = false;
     static constexpr int kDeep = LMX > 3 ? LMX - 2 : 1;
     static constexpr bool kSub = true;   // may run the LL problem of a peeled plane
@@ -398,7 +399,7 @@ struct RtGeom {
 };
 
 template <int K, int HQ, int WQ, int LM, int EARLY, int NPV, int NTHR, bool BWDL, int BOVL, int MODE, int ESZ,
-          bool NHWC = false, bool WHOLE = false>
+          bool NHWC = false, bool WHOLE = false, int PH = 0, int PW = 0>
 struct CtGeom {
     static constexpr Layout lay = make_layout(K, HQ, WQ, LM, EARLY, BWDL, BOVL, MODE, ESZ);
     static constexpr bool kDL = MODE == 1;
@@ -409,6 +410,7 @@ struct CtGeom {
         MODE == 1 && (!BWDL || red_len(NTHR, K, LM, NTHR / (4 * K) > 0 ? NTHR / (4 * K) : 1) <= lay.a0_off);
     static constexpr bool kFixed = true;
     static constexpr bool kWhole = WHOLE;   // the plane is exactly HQ x WQ
+    static constexpr int kPH = WHOLE ? HQ : PH, kPW = WHOLE ? WQ : PW;   // plane size, if fixed (else 0)
     static constexpr bool kNoLevels = LM == 0;
     static constexpr int kDeep = kMaxLm - 2;
     // the LL problem of a peeled plane is over 64 pixels wide (its parent did
@@ -533,16 +535,17 @@ constexpr int next_plane_units() {
 }
 
 // The plane's height and width: fixed at compile time in the instances for
-// planes that fill their zero-extended size exactly ("whole" planes), so that
-// their bounds tests fold away and their row strides are shifts.
+// planes that fill their zero-extended size exactly ("whole" planes) or for
+// one benchmark plane size, so that their bounds tests fold away and their
+// row strides are shifts.
 template <class G>
 __device__ __forceinline__ int plane_h(const FusedArgs& a) {
-    if constexpr (G::kWhole) return G::kHq;
+    if constexpr (G::kPH > 0) return G::kPH;
     else return a.H;
 }
 template <class G>
 __device__ __forceinline__ int plane_w(const FusedArgs& a) {
-    if constexpr (G::kWhole) return G::kWq;
+    if constexpr (G::kPW > 0) return G::kPW;
     else return a.W;
 }
 
@@ -1850,18 +1853,19 @@ namespace wtc {
 namespace fused_detail {
 
 // Launch the fixed-geometry instantiation if the plan matches it exactly.
-// A whole-plane instance (WH) matches only planes of exactly HQ x WQ pixels.
+// A whole-plane instance (WH) matches only planes of exactly HQ x WQ pixels,
+// one with a plane size (PH x PW > 0) only planes of that size.
 template <int K, typename ST, bool BWD, int BPQ, bool VEC, int HQ, int WQ, int LM, int EARLY, int NPV,
-          int NTHR, int BOVL, int MODE = 0, bool NH = false, bool WH = false>
+          int NTHR, int BOVL, int MODE = 0, bool NH = false, bool WH = false, int PH = 0, int PW = 0>
 bool try_static(const FusedArgs& a, int bpq, int nthr, size_t lds, int grid, hipStream_t st,
                 hipError_t* err) {
     if (a.Hq != HQ || a.Wq != WQ || a.Lm != LM || a.lay.early_lv != EARLY || a.NP != NPV ||
         nthr != NTHR || bpq != BPQ || (a.vec != 0) != VEC || a.lay.bovl != BOVL || a.lay.mode != MODE ||
-        (a.nhwc != 0) != NH || (WH && (a.H != HQ || a.W != WQ)))
+        (a.nhwc != 0) != NH || (WH && (a.H != HQ || a.W != WQ)) || (PH > 0 && (a.H != PH || a.W != PW)))
         return false;
     *err = launch_t<K, ST, BWD, BPQ, VEC,
-                    CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST), NH, WH>>(a, nthr, lds,
-                                                                                                     grid, st);
+                    CtGeom<K, HQ, WQ, LM, EARLY, NPV, NTHR, BWD, BOVL, MODE, (int)sizeof(ST), NH, WH, PH, PW>>(
+        a, nthr, lds, grid, st);
     return true;
 }
 
